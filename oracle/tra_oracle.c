@@ -1,0 +1,355 @@
+/*
+ * tra_oracle.c -- plain, slow, fp64 CPU oracle for entropy-radius block-sparse
+ * spatiotemporal self-attention over a (T, H, W) video token grid.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link,
+ * load or execute this file or the library built from it; only the test
+ * suite, the smoke check and the benchmark's CPU-baseline leg use it.  It
+ * shares no code, header, table or constant generator with the HIP path.
+ *
+ * What it computes (per head, batch 1, all arithmetic in IEEE fp64):
+ *
+ *   tokens      q, k, v are [heads][T][H][W][d] bfloat16 bit patterns, widened
+ *               exactly to fp64.  Token (t, y, x) belongs to block
+ *               (t, y / s, x / s) with s = sqrt(block): an s x s spatial tile
+ *               inside one frame.  Tiles are counted ceil(H/s) x ceil(W/s)
+ *               per frame; cells past the grid edge are not tokens.
+ *               (Token Radius Attention for Efficient Video Generation,
+ *               "The TRA Pipeline": tile-major layout so that spatial
+ *               neighbours share a block.)
+ *   probe       pooled means Qbar_b, Kbar_b over the real tokens of each
+ *               block; logits s_bc = Qbar_b . Kbar_c / sqrt(d) over all nb
+ *               blocks; p_b = softmax(s_b); H_b = -sum_c p_bc ln p_bc;
+ *               Hn_b = H_b / ln(nb) (0 when nb = 1).
+ *               (Same page, "Insight I" and "The TRA Pipeline:
+ *               Entropy-to-Budget": attention entropy decides how much a query
+ *               needs; here measured on block-pooled queries and keys.)
+ *   radius      r_b = min(r_min + floor(Hn_b * (r_max - r_min + 1)), r_max):
+ *               a linear quantiser of normalised entropy onto the integer
+ *               radii r_min..r_max.  (Same page, "Budget-to-Radius": entropy
+ *               becomes a per-query radius.)
+ *   mask        M[i][j] = 1 iff max(|t_i - t_j|, |y_i/s - y_j/s|,
+ *               |x_i/s - x_j/s|) <= r_blk(i): Chebyshev distance on block
+ *               coordinates (frame, tile row, tile column) against the
+ *               query's own block radius, built per query row from token
+ *               coordinates.  (Same page, "Insight II": a query-centred
+ *               neighbourhood in space, limited in time; Radial Attention to
+ *               Accelerate Video Generation, "The idea behind Radial
+ *               Attention": attention decays with spatiotemporal distance.)
+ *   attention   o_i = sum_j w_ij v_j with w_ij = exp(s_ij - m_i) / sum_j
+ *               exp(s_ij - m_i) over the keys with M[i][j] = 1,
+ *               s_ij = q_i . k_j / sqrt(d), m_i = max_j s_ij: exact softmax
+ *               attention restricted to the kept key blocks.
+ *               (AB-Attention speeds up video diffusion transformers up to
+ *               2.23x, first paragraph: dynamic block-sparse attention
+ *               computes exact attention only on the chosen key/value
+ *               blocks.)
+ *   block lists L(qb) = ascending list of key blocks kb whose Chebyshev
+ *               block distance from qb is <= r_qb -- exactly the blocks that
+ *               hold a key of some query row of qb under M.
+ *
+ * A radius of ORC_RADIUS_INF (INT32_MAX) is the dense case: every key kept.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <omp.h>
+
+#define ORC_RADIUS_INF 2147483647
+#define ORC_OK 0
+#define ORC_EINVAL (-1)
+#define ORC_ENOMEM (-4)
+
+typedef struct {
+    int T, H, W, s, nby, nbx;
+    long nb, N;
+} orc_grid;
+
+static double orc_lut[65536];
+static int orc_lut_ready = 0;
+
+/* bfloat16 bit pattern -> fp64, exact: a bf16 is the upper half of a binary32. */
+static void orc_init_lut(void)
+{
+    if (orc_lut_ready) return;
+    for (uint32_t h = 0; h < 65536u; ++h) {
+        uint32_t u = h << 16;
+        float f;
+        memcpy(&f, &u, sizeof f);
+        orc_lut[h] = (double)f;
+    }
+    orc_lut_ready = 1;
+}
+
+static int orc_grid_make(orc_grid *g, int T, int H, int W, int block)
+{
+    if (T < 1 || H < 1 || W < 1 || block < 1) return ORC_EINVAL;
+    int s = 0;
+    while ((s + 1) * (s + 1) <= block) ++s;
+    if (s * s != block) return ORC_EINVAL;
+    g->T = T; g->H = H; g->W = W; g->s = s;
+    g->nby = (H + s - 1) / s;
+    g->nbx = (W + s - 1) / s;
+    g->nb = (long)T * g->nby * g->nbx;
+    g->N = (long)T * H * W;
+    return ORC_OK;
+}
+
+static long orc_labs(long a) { return a < 0 ? -a : a; }
+
+/* Chebyshev distance between the blocks of tokens (ti,yi,xi) and (tj,yj,xj). */
+static long orc_block_cheb(const orc_grid *g, int ti, int yi, int xi, int tj, int yj, int xj)
+{
+    long dt = orc_labs((long)ti - tj);
+    long dy = orc_labs((long)(yi / g->s) - (yj / g->s));
+    long dx = orc_labs((long)(xi / g->s) - (xj / g->s));
+    long m = dt > dy ? dt : dy;
+    return m > dx ? m : dx;
+}
+
+/* Linear quantiser of normalised entropy onto r_min..r_max. */
+int orc_radius(double h_norm, int r_min, int r_max)
+{
+    if (r_min == ORC_RADIUS_INF && r_max == ORC_RADIUS_INF) return ORC_RADIUS_INF;
+    long R = (long)r_max - (long)r_min + 1;
+    long r = (long)r_min + (long)floor(h_norm * (double)R);
+    if (r > r_max) r = r_max;
+    return (int)r;
+}
+
+/* Mean of x over the real tokens of each block: out[heads][nb][d]. */
+int orc_pool(const uint16_t *x, int T, int H, int W, int heads, int d, int block, double *out)
+{
+    orc_grid g;
+    if (!x || !out || heads < 1 || d < 1 || orc_grid_make(&g, T, H, W, block)) return ORC_EINVAL;
+    orc_init_lut();
+    long *count = (long *)calloc((size_t)g.nb, sizeof(long));
+    if (!count) return ORC_ENOMEM;
+    for (int t = 0; t < T; ++t)
+        for (int y = 0; y < H; ++y)
+            for (int xx = 0; xx < W; ++xx)
+                count[((long)t * g.nby + y / g.s) * g.nbx + xx / g.s] += 1;
+#pragma omp parallel for schedule(static)
+    for (int h = 0; h < heads; ++h) {
+        double *o = out + (size_t)h * g.nb * d;
+        memset(o, 0, sizeof(double) * (size_t)g.nb * d);
+        const uint16_t *xh = x + (size_t)h * g.N * d;
+        long n = 0;
+        for (int t = 0; t < T; ++t)
+            for (int y = 0; y < H; ++y)
+                for (int xx = 0; xx < W; ++xx, ++n) {
+                    long b = ((long)t * g.nby + y / g.s) * g.nbx + xx / g.s;
+                    for (int c = 0; c < d; ++c) o[b * d + c] += orc_lut[xh[n * d + c]];
+                }
+        for (long b = 0; b < g.nb; ++b)
+            for (int c = 0; c < d; ++c) o[b * d + c] /= (double)count[b];
+    }
+    free(count);
+    return ORC_OK;
+}
+
+/*
+ * Pooled-entropy probe and radius per (head, block).
+ * h_norm[heads][nb] (fp64) and radius[heads][nb] (int32).
+ * r_min == r_max == ORC_RADIUS_INF is the dense case: every radius infinite,
+ * h_norm left at 0.
+ */
+int orc_probe(const uint16_t *q, const uint16_t *k, int T, int H, int W, int heads, int d,
+              int block, int r_min, int r_max, double *h_norm, int32_t *radius)
+{
+    orc_grid g;
+    if (!q || !k || !h_norm || !radius || heads < 1 || d < 1) return ORC_EINVAL;
+    if (orc_grid_make(&g, T, H, W, block)) return ORC_EINVAL;
+    int dense = (r_min == ORC_RADIUS_INF && r_max == ORC_RADIUS_INF);
+    if (!dense && (r_min < 0 || r_max < r_min)) return ORC_EINVAL;
+    if (dense) {
+        for (long i = 0; i < (long)heads * g.nb; ++i) { h_norm[i] = 0.0; radius[i] = ORC_RADIUS_INF; }
+        return ORC_OK;
+    }
+    size_t pooled = (size_t)heads * g.nb * d;
+    double *qb = (double *)malloc(sizeof(double) * pooled);
+    double *kb = (double *)malloc(sizeof(double) * pooled);
+    if (!qb || !kb) { free(qb); free(kb); return ORC_ENOMEM; }
+    int rc = orc_pool(q, T, H, W, heads, d, block, qb);
+    if (!rc) rc = orc_pool(k, T, H, W, heads, d, block, kb);
+    if (rc) { free(qb); free(kb); return rc; }
+    const double inv_sqrt_d = 1.0 / sqrt((double)d);
+    const double log_nb = log((double)g.nb);
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)g.nb);
+        if (!s) {
+#pragma omp atomic write
+            fail = 1;
+        }
+#pragma omp for collapse(2) schedule(dynamic, 8)
+        for (int h = 0; h < heads; ++h)
+            for (long b = 0; b < g.nb; ++b) {
+                if (!s) continue;
+                const double *qv = qb + ((size_t)h * g.nb + b) * d;
+                double m = -INFINITY;
+                for (long c = 0; c < g.nb; ++c) {
+                    const double *kv = kb + ((size_t)h * g.nb + c) * d;
+                    double acc = 0.0;
+                    for (int i = 0; i < d; ++i) acc += qv[i] * kv[i];
+                    s[c] = acc * inv_sqrt_d;
+                    if (s[c] > m) m = s[c];
+                }
+                double Z = 0.0;
+                for (long c = 0; c < g.nb; ++c) Z += exp(s[c] - m);
+                double Hb = 0.0;
+                for (long c = 0; c < g.nb; ++c) {
+                    double p = exp(s[c] - m) / Z;
+                    if (p > 0.0) Hb -= p * log(p);
+                }
+                double hn = g.nb > 1 ? Hb / log_nb : 0.0;
+                h_norm[(size_t)h * g.nb + b] = hn;
+                radius[(size_t)h * g.nb + b] = orc_radius(hn, r_min, r_max);
+            }
+        free(s);
+    }
+    free(qb);
+    free(kb);
+    return fail ? ORC_ENOMEM : ORC_OK;
+}
+
+/*
+ * Key-block lists: for every (head, query block) the ascending key blocks
+ * within the query block's Chebyshev radius.  idx[heads][nb][maxcnt] (only the
+ * first cnt entries of a row are written), cnt[heads][nb].
+ */
+int orc_block_lists(const int32_t *radius, int T, int H, int W, int heads, int block,
+                    long maxcnt, int32_t *idx, int32_t *cnt)
+{
+    orc_grid g;
+    if (!radius || !idx || !cnt || heads < 1 || maxcnt < 1) return ORC_EINVAL;
+    if (orc_grid_make(&g, T, H, W, block)) return ORC_EINVAL;
+    int bad = 0;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int h = 0; h < heads; ++h)
+        for (long qb = 0; qb < g.nb; ++qb) {
+            long r = radius[(size_t)h * g.nb + qb];
+            int tq = (int)(qb / ((long)g.nby * g.nbx));
+            int byq = (int)((qb / g.nbx) % g.nby);
+            int bxq = (int)(qb % g.nbx);
+            long c = 0;
+            int32_t *row = idx + ((size_t)h * g.nb + qb) * maxcnt;
+            if (r < 0) {
+#pragma omp atomic write
+                bad = 1;
+                cnt[(size_t)h * g.nb + qb] = 0;
+                continue;
+            }
+            for (long kb = 0; kb < g.nb; ++kb) {
+                int tk = (int)(kb / ((long)g.nby * g.nbx));
+                int byk = (int)((kb / g.nbx) % g.nby);
+                int bxk = (int)(kb % g.nbx);
+                long dt = orc_labs((long)tq - tk), dy = orc_labs((long)byq - byk), dx = orc_labs((long)bxq - bxk);
+                long m = dt > dy ? dt : dy;
+                m = m > dx ? m : dx;
+                if (m <= r) {
+                    if (c >= maxcnt) {
+#pragma omp atomic write
+                        bad = 1;
+                        break;
+                    }
+                    row[c++] = (int32_t)kb;
+                }
+            }
+            cnt[(size_t)h * g.nb + qb] = (int32_t)c;
+        }
+    return bad ? ORC_EINVAL : ORC_OK;
+}
+
+/*
+ * Masked softmax attention for selected query rows.
+ * rows[n] = head * N + token (token = (t*H + y)*W + x); out[n][d] fp64.
+ * radius[heads][nb] gives each query block's radius (ORC_RADIUS_INF = dense).
+ */
+int orc_attention_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                       int T, int H, int W, int heads, int d, int block,
+                       const int32_t *radius, long nrows, const int64_t *rows, double *out)
+{
+    orc_grid g;
+    if (!q || !k || !v || !radius || !rows || !out || heads < 1 || d < 1 || nrows < 0) return ORC_EINVAL;
+    if (orc_grid_make(&g, T, H, W, block)) return ORC_EINVAL;
+    for (long n = 0; n < nrows; ++n)
+        if (rows[n] < 0 || rows[n] >= (int64_t)heads * g.N) return ORC_EINVAL;
+    orc_init_lut();
+    const double inv_sqrt_d = 1.0 / sqrt((double)d);
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)g.N);
+        long *js = (long *)malloc(sizeof(long) * (size_t)g.N);
+        double *qi = (double *)malloc(sizeof(double) * (size_t)d);
+        double *acc = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!s || !js || !qi || !acc) {
+#pragma omp atomic write
+            fail = 1;
+        }
+#pragma omp for schedule(dynamic, 4)
+        for (long n = 0; n < nrows; ++n) {
+            if (!s || !js || !qi || !acc) continue;
+            int h = (int)(rows[n] / g.N);
+            long i = rows[n] % g.N;
+            int ti = (int)(i / ((long)H * W)), yi = (int)((i / W) % H), xi = (int)(i % W);
+            long bi = ((long)ti * g.nby + yi / g.s) * g.nbx + xi / g.s;
+            long r = radius[(size_t)h * g.nb + bi];
+            const uint16_t *qh = q + (size_t)h * g.N * d;
+            const uint16_t *kh = k + (size_t)h * g.N * d;
+            const uint16_t *vh = v + (size_t)h * g.N * d;
+            for (int c = 0; c < d; ++c) qi[c] = orc_lut[qh[i * d + c]];
+            /* explicit token mask row, then the logits of the kept keys */
+            long cnt = 0;
+            double m = -INFINITY;
+            for (int tj = 0; tj < T; ++tj) {
+                if (orc_labs((long)ti - tj) > r) continue; /* no key of this frame passes */
+                for (int yj = 0; yj < H; ++yj)
+                    for (int xj = 0; xj < W; ++xj) {
+                        if (orc_block_cheb(&g, ti, yi, xi, tj, yj, xj) > r) continue;
+                        long j = ((long)tj * H + yj) * W + xj;
+                        const uint16_t *kj = kh + (size_t)j * d;
+                        double dot = 0.0;
+                        for (int c = 0; c < d; ++c) dot += qi[c] * orc_lut[kj[c]];
+                        s[cnt] = dot * inv_sqrt_d;
+                        js[cnt] = j;
+                        if (s[cnt] > m) m = s[cnt];
+                        ++cnt;
+                    }
+            }
+            double Z = 0.0;
+            for (int c = 0; c < d; ++c) acc[c] = 0.0;
+            for (long e = 0; e < cnt; ++e) {
+                double w = exp(s[e] - m);
+                Z += w;
+                const uint16_t *vj = vh + (size_t)js[e] * d;
+                for (int c = 0; c < d; ++c) acc[c] += w * orc_lut[vj[c]];
+            }
+            double *o = out + (size_t)n * d;
+            for (int c = 0; c < d; ++c) o[c] = acc[c] / Z;
+        }
+        free(s); free(js); free(qi); free(acc);
+    }
+    return fail ? ORC_ENOMEM : ORC_OK;
+}
+
+/* Masked softmax attention for every token: out[heads][T][H][W][d] fp64. */
+int orc_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                  int T, int H, int W, int heads, int d, int block,
+                  const int32_t *radius, double *out)
+{
+    orc_grid g;
+    if (heads < 1 || orc_grid_make(&g, T, H, W, block)) return ORC_EINVAL;
+    long nrows = (long)heads * g.N;
+    int64_t *rows = (int64_t *)malloc(sizeof(int64_t) * (size_t)nrows);
+    if (!rows) return ORC_ENOMEM;
+    for (long n = 0; n < nrows; ++n) rows[n] = n;
+    int rc = orc_attention_rows(q, k, v, T, H, W, heads, d, block, radius, nrows, rows, out);
+    free(rows);
+    return rc;
+}
+
+int orc_num_threads(void) { return omp_get_max_threads(); }

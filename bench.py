@@ -1,0 +1,264 @@
+"""Benchmark of the entropy-radius block-sparse attention layer on one MI355X.
+
+One step = one whole layer, ``tra_attention`` (probe -> radii -> key-block
+lists -> block-sparse attention) over all heads, inputs resident in HBM.
+Default workload: the Wan2.1-1.3B 480x832 81-frame layer (T=21, H=30, W=52,
+12 heads, head_dim 128, bf16, 64-token 8x8 tiles, radii 1..8).
+
+Prints one JSON line (last line of stdout) with ms/layer, the attention
+kernel's achieved TFLOP/s on computed blocks against the dense bf16/fp16
+matrix-core peak, the dense-mode time, an injected-radius density sweep and
+the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ms/layer + effective TFLOP/s (fraction of bf16 MFMA peak) vs dense, Wan-1.3B shape"
+PEAK_TFLOPS = 2500.0        # MI355X dense bf16 / fp16 matrix-core peak
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+INF = 2147483647
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tra_attn_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "content_adaptive_sparse_amd", "csrc", "tra_attn.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attn_source_hash():
+    with open(ATTN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload_key):
+    """HBM bytes per attention launch from rocprofv3 counters, if they were
+    taken on the current kernel source for this workload; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("attn_source_sha") != attn_source_hash() or rec.get("workload") != workload_key:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(q, k, v, c, budget_s):
+    """fp64 oracle on a bounded sample: full probe and block lists, then
+    attention rows until about budget_s seconds; extrapolated to one layer."""
+    import oracle
+    t0 = time.perf_counter()
+    hn, r = oracle.probe(q, k, c.r_min, c.r_max)
+    oracle.block_lists(r, c.T, c.H, c.W, maxcnt=oracle.grid_blocks(c.T, c.H, c.W)[2])
+    t_fixed = time.perf_counter() - t0
+    total_rows = c.heads * c.N
+    rng = np.random.default_rng(0)
+    rows_done, t_rows, batch = 0, 0.0, 256
+    while t_rows < budget_s and rows_done < total_rows:
+        rows = rng.choice(total_rows, size=min(batch, total_rows), replace=False)
+        t1 = time.perf_counter()
+        oracle.attention_rows(q, k, v, r, rows)
+        dt = time.perf_counter() - t1
+        t_rows += dt
+        rows_done += rows.size
+        batch = int(min(max(batch, rows.size * max(budget_s - t_rows, 0.0) / max(dt, 1e-3)), 65536)) or 256
+    ms_layer = 1e3 * (t_fixed + t_rows * total_rows / rows_done)
+    return {
+        "value": round(ms_layer, 1),
+        "unit": "ms/layer",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"full fp64 probe + block lists ({t_fixed:.1f} s), then {rows_done} of "
+                   f"{total_rows} query rows of masked attention on the same radii "
+                   f"({t_rows:.1f} s), attention time extrapolated linearly to all rows"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=1, help="workload id (tra_inputs.CONFIGS)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU oracle sample budget (0 skips it)")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--only-layer", action="store_true",
+                    help="time the layer only (for profiler runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer shards "
+              "by head with no communication, so there is no multi-GPU path to time.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import content_adaptive_sparse_amd as tra
+    import tra_inputs as ti
+
+    c = ti.CONFIGS[args.config]
+    T, H, W, heads, d = c.T, c.H, c.W, c.heads, c.d
+    nby, nbx, nb = tra.tra_grid(T, H, W)
+    log(f"[bench] workload {c.name}; generating inputs", )
+    q, k, v = ti.make_config_inputs(args.config)
+
+    def dev(x):
+        return torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    out = torch.empty(heads, T, H, W, d, dtype=torch.float32, device="cuda")
+    flops_pair = 4 * 64 * 64 * d
+
+    def layer(r_min, r_max):
+        tra.tra_attention(qd, kd, vd, T, H, W, heads, d, 64, r_min, r_max, out)
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / steps
+        return e0.elapsed_time(e1) / steps, wall
+
+    def profiled(fn, steps):
+        torch.cuda.synchronize()
+        tra.tra_profile_begin()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        res = tra.tra_profile_end()
+        return {kk: (ms / n if n else 0.0) for kk, (ms, n) in res.items()}
+
+    # ---- the layer (timed region: exactly --steps calls) ----
+    ms_layer, ms_wall = timed(lambda: layer(c.r_min, c.r_max), args.steps, args.warmup)
+    log(f"[bench] layer {ms_layer:.3f} ms (wall {ms_wall:.3f})")
+    if args.only_layer:
+        ms_dense, _ = timed(lambda: layer(INF, INF), args.steps, args.warmup)
+        log(f"[bench] dense layer {ms_dense:.3f} ms")
+        return
+
+    # realised radii / lists of the probe (same kernels as inside the layer)
+    radius = torch.empty(heads, nb, dtype=torch.int32, device="cuda")
+    tra.tra_probe(qd, kd, T, H, W, heads, d, 64, c.r_min, c.r_max, radius)
+    maxcnt = tra.tra_maxcnt(T, H, W, 64, c.r_max)
+    idx = torch.empty(heads, nb, maxcnt, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(heads, nb, dtype=torch.int32, device="cuda")
+    tra.tra_mask(radius, T, H, W, heads, 64, c.r_max, idx, cnt)
+    torch.cuda.synchronize()
+    pairs = int(cnt.sum().item())
+    density = pairs / (heads * nb * nb)
+    rhist = np.bincount(radius.cpu().numpy().ravel(), minlength=c.r_max + 1).tolist()
+    del idx
+
+    kern = profiled(lambda: layer(c.r_min, c.r_max), max(5, args.steps // 2))
+    t_attn = kern["attn"]
+    achieved = flops_pair * pairs / (t_attn * 1e-3) / 1e12
+    log(f"[bench] kernels (ms): {kern}; density {density:.4f}; attn {achieved:.1f} TFLOP/s")
+
+    # ---- dense mode of the same kernel ----
+    ms_dense, _ = timed(lambda: layer(INF, INF), max(3, args.steps // 2), 2)
+    kd_ = profiled(lambda: layer(INF, INF), 3)
+    dense_tflops = flops_pair * heads * nb * nb / (kd_["attn"] * 1e-3) / 1e12
+    log(f"[bench] dense layer {ms_dense:.3f} ms, attn {kd_['attn']:.3f} ms = {dense_tflops:.1f} TFLOP/s")
+
+    # ---- injected-radius density sweep (attention kernel only) ----
+    sweep = []
+    if not args.no_sweep:
+        rng = np.random.default_rng(0)
+        cases = [("r=1", np.ones((heads, nb))), ("r=2", np.full((heads, nb), 2)),
+                 ("r in {1,2}", rng.integers(1, 3, size=(heads, nb))),
+                 ("r in {2,3}", rng.integers(2, 4, size=(heads, nb)))]
+        for name, rr in cases:
+            rmax = int(rr.max())
+            rd = torch.from_numpy(rr.astype(np.int32)).cuda()
+            mc = tra.tra_maxcnt(T, H, W, 64, rmax)
+            ix = torch.empty(heads, nb, mc, dtype=torch.int32, device="cuda")
+            cn = torch.empty(heads, nb, dtype=torch.int32, device="cuda")
+            tra.tra_mask(rd, T, H, W, heads, 64, rmax, ix, cn)
+            torch.cuda.synchronize()
+            p = int(cn.sum().item())
+            kk = profiled(lambda: tra.tra_attn(qd, kd, vd, T, H, W, heads, d, 64, ix, cn, mc, out), 5)
+            sweep.append({"radii": name, "density": round(p / (heads * nb * nb), 4),
+                          "attn_ms": round(kk["attn"], 4),
+                          "tflops": round(flops_pair * p / (kk["attn"] * 1e-3) / 1e12, 1),
+                          "speedup_vs_dense_attn": round(kd_["attn"] / kk["attn"], 2)})
+            log(f"[bench] sweep {sweep[-1]}")
+            del ix, cn
+
+    # HBM bandwidth of the probe/pack kernel (algorithmic bytes: read q, k, v,
+    # write the packed k and v^T tiles and the pooled means)
+    pack_bytes = 3 * heads * c.N * d * 2 + 2 * heads * nb * 64 * d * 2 + 2 * heads * nb * d * 4
+    pack_gbs = pack_bytes / (kern["pack_pool"] * 1e-3) / 1e9
+    mask_bytes = 4 * (heads * nb + pairs)
+    mask_gbs = mask_bytes / (kern["mask"] * 1e-3) / 1e9 if kern["mask"] > 0 else None
+
+    workload_key = f"config{args.config}"
+    traffic = measured_traffic(workload_key)
+    res = {
+        "metric": METRIC,
+        "value": round(ms_layer, 4),
+        "unit": "ms/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_layer, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": c.name,
+            "T": T, "H": H, "W": W, "heads": heads, "head_dim": d, "block": 64,
+            "r_min": c.r_min, "r_max": c.r_max, "batch": 1,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "details": {
+            "effective_tflops_attn": round(achieved, 1),
+            "frac_of_bf16_peak": round(achieved / PEAK_TFLOPS, 4),
+            "effective_tflops_layer": round(flops_pair * pairs / (ms_layer * 1e-3) / 1e12, 1),
+            "block_density": round(density, 4),
+            "computed_block_pairs": pairs,
+            "radius_histogram": rhist,
+            "kernel_ms": {kk: round(vv, 4) for kk, vv in kern.items() if vv},
+            "dense_ms_per_layer": round(ms_dense, 4),
+            "dense_attn_ms": round(kd_["attn"], 4),
+            "dense_attn_tflops": round(dense_tflops, 1),
+            "speedup_vs_dense_layer": round(ms_dense / ms_layer, 3),
+            "pack_pool_gbs": round(pack_gbs, 1),
+            "mask_gbs": None if mask_gbs is None else round(mask_gbs, 2),
+            "density_sweep": sweep,
+            "wall_ms_per_step": round(ms_wall, 4),
+            "pv_dtype": "fp16",
+        },
+    }
+    if args.cpu_seconds > 0:
+        log("[bench] CPU oracle baseline")
+        res["cpu_baseline"] = cpu_baseline(q, k, v, c, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,174 @@
+"""Python binding of the entropy-radius block-sparse attention library (gfx950).
+
+Argument marshalling only: every function forwards to the C ABI of
+``libtra_attention.so`` (declared in ``include/tra_attention.h``) with the
+same name and argument order.  Tensors are torch tensors on the GPU
+(bf16 q/k/v, fp32 out, int32 radius/idx/cnt); torch provides device memory
+and the stream, nothing else.  Integers are accepted in place of tensors as raw
+device pointers.  There is no fallback: if the HIP library is not built,
+every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from .build import LIB_PATH
+
+__all__ = [
+    "TRA_RADIUS_INF", "TraError", "library", "tra_attention", "tra_probe", "tra_mask",
+    "tra_attn", "tra_grid", "tra_maxcnt", "tra_status_string", "tra_version",
+    "tra_profile_begin", "tra_profile_end", "KERNEL_KINDS",
+]
+
+TRA_RADIUS_INF = 2147483647
+KERNEL_KINDS = ("pack_pool", "entropy", "mask", "attn", "fill")
+
+_lib = None
+
+
+class TraError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what} failed: {tra_status_string(status)} ({status})")
+        self.status = status
+
+
+def library() -> ctypes.CDLL:
+    """Load ``libtra_attention.so``; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"HIP library not built: {LIB_PATH} is missing "
+                "(run `python -m content_adaptive_sparse_amd.build` or __graft_entry__.build())")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I, L = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+        lib.tra_status_string.argtypes = [I]
+        lib.tra_status_string.restype = ctypes.c_char_p
+        lib.tra_version.argtypes = []
+        lib.tra_version.restype = I
+        lib.tra_grid.argtypes = [I, I, I, I, P, P, P]
+        lib.tra_grid.restype = I
+        lib.tra_maxcnt.argtypes = [I, I, I, I, I]
+        lib.tra_maxcnt.restype = L
+        lib.tra_attention.argtypes = [P, P, P, I, I, I, I, I, I, I, I, P, P]
+        lib.tra_attention.restype = I
+        lib.tra_probe.argtypes = [P, P, I, I, I, I, I, I, I, I, P, P, P]
+        lib.tra_probe.restype = I
+        lib.tra_mask.argtypes = [P, I, I, I, I, I, I, P, P, P]
+        lib.tra_mask.restype = I
+        lib.tra_attn.argtypes = [P, P, P, I, I, I, I, I, I, P, P, L, P, P]
+        lib.tra_attn.restype = I
+        lib.tra_profile_begin.argtypes = []
+        lib.tra_profile_begin.restype = I
+        lib.tra_profile_end.argtypes = [P, P, I]
+        lib.tra_profile_end.restype = I
+        _lib = lib
+    return _lib
+
+
+def _ptr(x, dtype=None, what="tensor"):
+    """Device pointer of a contiguous GPU tensor (or a raw int / None)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if not x.is_cuda:
+        raise ValueError(f"{what} must be a GPU tensor")
+    if not x.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if dtype is not None and x.dtype not in dtype:
+        raise ValueError(f"{what} has dtype {x.dtype}, expected one of {dtype}")
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _bf16():
+    import torch
+    return (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _f32():
+    import torch
+    return (torch.float32,)
+
+
+def _i32():
+    import torch
+    return (torch.int32,)
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise TraError(status, what)
+
+
+def tra_status_string(status: int) -> str:
+    return library().tra_status_string(int(status)).decode()
+
+
+def tra_version() -> int:
+    return library().tra_version()
+
+
+def tra_grid(T: int, H: int, W: int, block: int = 64):
+    """(nby, nbx, nb) of the tile grid."""
+    a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(library().tra_grid(T, H, W, block, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)),
+           "tra_grid")
+    return a.value, b.value, c.value
+
+
+def tra_maxcnt(T: int, H: int, W: int, block: int, r_max: int) -> int:
+    n = library().tra_maxcnt(T, H, W, block, r_max)
+    if n < 0:
+        raise TraError(int(n), "tra_maxcnt")
+    return n
+
+
+def tra_attention(q, k, v, T, H, W, heads, head_dim, block, r_min, r_max, out, stream=None):
+    _check(library().tra_attention(
+        _ptr(q, _bf16(), "q"), _ptr(k, _bf16(), "k"), _ptr(v, _bf16(), "v"), T, H, W, heads,
+        head_dim, block, r_min, r_max, _ptr(out, _f32(), "out"), _stream(stream)), "tra_attention")
+
+
+def tra_probe(q, k, T, H, W, heads, head_dim, block, r_min, r_max, radius, h_norm=None,
+              stream=None):
+    _check(library().tra_probe(
+        _ptr(q, _bf16(), "q"), _ptr(k, _bf16(), "k"), T, H, W, heads, head_dim, block, r_min,
+        r_max, _ptr(radius, _i32(), "radius"), _ptr(h_norm, _f32(), "h_norm"), _stream(stream)),
+        "tra_probe")
+
+
+def tra_mask(radius, T, H, W, heads, block, r_max, idx, cnt, stream=None):
+    _check(library().tra_mask(
+        _ptr(radius, _i32(), "radius"), T, H, W, heads, block, r_max, _ptr(idx, _i32(), "idx"),
+        _ptr(cnt, _i32(), "cnt"), _stream(stream)), "tra_mask")
+
+
+def tra_attn(q, k, v, T, H, W, heads, head_dim, block, idx, cnt, maxcnt, out, stream=None):
+    _check(library().tra_attn(
+        _ptr(q, _bf16(), "q"), _ptr(k, _bf16(), "k"), _ptr(v, _bf16(), "v"), T, H, W, heads,
+        head_dim, block, _ptr(idx, _i32(), "idx"), _ptr(cnt, _i32(), "cnt"), int(maxcnt),
+        _ptr(out, _f32(), "out"), _stream(stream)), "tra_attn")
+
+
+def tra_profile_begin():
+    _check(library().tra_profile_begin(), "tra_profile_begin")
+
+
+def tra_profile_end():
+    """Per-kernel-kind (milliseconds, launches) recorded since tra_profile_begin."""
+    n = len(KERNEL_KINDS)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int * n)()
+    _check(library().tra_profile_end(ms, cnt, n), "tra_profile_end")
+    return {name: (ms[i], cnt[i]) for i, name in enumerate(KERNEL_KINDS)}

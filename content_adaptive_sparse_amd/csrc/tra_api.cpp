@@ -1,0 +1,378 @@
+// C ABI of the entropy-radius block-sparse attention library: argument
+// validation, tile-grid arithmetic, stream-ordered scratch memory and the
+// launch sequence probe -> mask -> attention.  Declarations and the contract
+// of every entry point are in include/tra_attention.h.
+#include "tra_attention.h"
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include <mutex>
+#include <vector>
+
+#include "tra_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+bool is_dense(int r_min, int r_max) { return r_min == TRA_RADIUS_INF && r_max == TRA_RADIUS_INF; }
+
+int make_grid(int T, int H, int W, int block, tra::Grid *g) {
+    if (T < 1 || H < 1 || W < 1) return TRA_ERR_INVALID_ARG;
+    if (block != tra::kBlockTokens) return TRA_ERR_UNSUPPORTED;
+    const int64_t nby = (H + tra::kTileSide - 1) / tra::kTileSide;
+    const int64_t nbx = (W + tra::kTileSide - 1) / tra::kTileSide;
+    const int64_t nb = (int64_t)T * nby * nbx;
+    if (nb > INT32_MAX || (int64_t)T * H * W > INT32_MAX) return TRA_ERR_UNSUPPORTED;
+    g->T = T; g->H = H; g->W = W;
+    g->nby = (int)nby; g->nbx = (int)nbx; g->nb = (int)nb;
+    return TRA_OK;
+}
+
+int check_radii(int r_min, int r_max) {
+    if (is_dense(r_min, r_max)) return TRA_OK;
+    if (r_min < 0 || r_max < r_min) return TRA_ERR_INVALID_ARG;
+    return TRA_OK;
+}
+
+int check_dims(int heads, int head_dim, const tra::Grid &g) {
+    if (heads < 1 || head_dim < 1) return TRA_ERR_INVALID_ARG;
+    if (head_dim != 64 && head_dim != 128) return TRA_ERR_UNSUPPORTED;
+    if (heads > 65535) return TRA_ERR_UNSUPPORTED;
+    // packed tiles and tokens, per tensor
+    if ((int64_t)heads * g.nb * tra::kBlockTokens * head_dim > kMaxElems) return TRA_ERR_UNSUPPORTED;
+    if ((int64_t)heads * g.nb > INT32_MAX) return TRA_ERR_UNSUPPORTED;
+    return TRA_OK;
+}
+
+int64_t maxcnt_of(const tra::Grid &g, int r_max) {
+    if (r_max == TRA_RADIUS_INF) return g.nb;
+    const int64_t w = 2 * (int64_t)r_max + 1;
+    const int64_t a = w < g.T ? w : g.T;
+    const int64_t b = w < g.nby ? w : g.nby;
+    const int64_t c = w < g.nbx ? w : g.nbx;
+    return a * b * c;
+}
+
+// Library-owned stream-ordered memory pool per device.  Freed scratch stays in
+// the pool (release threshold = max) so repeated calls do not reach the driver.
+std::mutex g_pool_mu;
+hipMemPool_t g_pool[kMaxDevices] = {};
+
+hipError_t pool_for_current_device(hipMemPool_t *out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_pool_mu);
+    if (!g_pool[dev]) {
+        hipMemPoolProps props = {};
+        props.allocType = hipMemAllocationTypePinned;
+        props.handleTypes = hipMemHandleTypeNone;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t p = nullptr;
+        e = hipMemPoolCreate(&p, &props);
+        if (e != hipSuccess) return e;
+        uint64_t threshold = UINT64_MAX;
+        e = hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &threshold);
+        if (e != hipSuccess) {
+            (void)hipMemPoolDestroy(p);
+            return e;
+        }
+        g_pool[dev] = p;
+    }
+    *out = g_pool[dev];
+    return hipSuccess;
+}
+
+// Scratch carved from one stream-ordered allocation; freed on the stream when
+// the scope ends (after every kernel that uses it has been enqueued).
+class Scratch {
+  public:
+    explicit Scratch(hipStream_t s) : s_(s) {}
+    ~Scratch() {
+        if (base_) (void)hipFreeAsync(base_, s_);
+    }
+    // Reserve `bytes` (256-byte aligned); returns the offset.
+    size_t reserve(size_t bytes) {
+        const size_t off = size_;
+        size_ += (bytes + 255) & ~size_t(255);
+        return off;
+    }
+    int allocate() {
+        if (size_ == 0) return TRA_OK;
+        hipMemPool_t pool = nullptr;
+        if (pool_for_current_device(&pool) != hipSuccess) return TRA_ERR_HIP;
+        const hipError_t e = hipMallocFromPoolAsync(&base_, size_, pool, s_);
+        if (e == hipErrorOutOfMemory) return TRA_ERR_NOMEM;
+        if (e != hipSuccess) {
+            base_ = nullptr;
+            return TRA_ERR_HIP;
+        }
+        return TRA_OK;
+    }
+    template <typename T>
+    T *at(size_t off) const {
+        return reinterpret_cast<T *>(static_cast<char *>(base_) + off);
+    }
+
+  private:
+    hipStream_t s_;
+    void *base_ = nullptr;
+    size_t size_ = 0;
+};
+
+int hip_status(hipError_t e) { return e == hipSuccess ? TRA_OK : TRA_ERR_HIP; }
+
+// ---- optional per-kernel event timing ----
+struct ProfRecord {
+    int kind;
+    hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRecord> g_prof;
+
+// Brackets one kernel launch with events on its stream when profiling is on.
+class ProfScope {
+  public:
+    ProfScope(int kind, hipStream_t s) : s_(s) {
+        std::lock_guard<std::mutex> lock(g_prof_mu);
+        if (!g_prof_on) return;
+        rec_.kind = kind;
+        if (hipEventCreate(&rec_.start) != hipSuccess) return;
+        if (hipEventCreate(&rec_.stop) != hipSuccess) {
+            (void)hipEventDestroy(rec_.start);
+            return;
+        }
+        active_ = hipEventRecord(rec_.start, s_) == hipSuccess;
+        if (!active_) {
+            (void)hipEventDestroy(rec_.start);
+            (void)hipEventDestroy(rec_.stop);
+        }
+    }
+    ~ProfScope() {
+        if (!active_) return;
+        (void)hipEventRecord(rec_.stop, s_);
+        std::lock_guard<std::mutex> lock(g_prof_mu);
+        g_prof.push_back(rec_);
+    }
+
+  private:
+    hipStream_t s_;
+    ProfRecord rec_{};
+    bool active_ = false;
+};
+
+}  // namespace
+
+extern "C" {
+
+const char *tra_status_string(int status) {
+    switch (status) {
+        case TRA_OK: return "TRA_OK";
+        case TRA_ERR_INVALID_ARG: return "TRA_ERR_INVALID_ARG";
+        case TRA_ERR_UNSUPPORTED: return "TRA_ERR_UNSUPPORTED";
+        case TRA_ERR_HIP: return "TRA_ERR_HIP";
+        case TRA_ERR_NOMEM: return "TRA_ERR_NOMEM";
+        default: return "TRA_ERR_UNKNOWN";
+    }
+}
+
+int tra_version(void) { return 100; }
+
+int tra_grid(int T, int H, int W, int block, int *nby, int *nbx, int *nb) {
+    tra::Grid g;
+    const int rc = make_grid(T, H, W, block, &g);
+    if (rc != TRA_OK) return rc;
+    if (nby) *nby = g.nby;
+    if (nbx) *nbx = g.nbx;
+    if (nb) *nb = g.nb;
+    return TRA_OK;
+}
+
+int64_t tra_maxcnt(int T, int H, int W, int block, int r_max) {
+    tra::Grid g;
+    const int rc = make_grid(T, H, W, block, &g);
+    if (rc != TRA_OK) return rc;
+    if (r_max < 0) return TRA_ERR_INVALID_ARG;
+    return maxcnt_of(g, r_max);
+}
+
+int tra_probe(const void *q, const void *k, int T, int H, int W, int heads, int head_dim,
+              int block, int r_min, int r_max, int32_t *radius, float *h_norm,
+              hipStream_t stream) {
+    tra::Grid g;
+    int rc = make_grid(T, H, W, block, &g);
+    if (rc == TRA_OK) rc = check_dims(heads, head_dim, g);
+    if (rc == TRA_OK) rc = check_radii(r_min, r_max);
+    if (rc != TRA_OK) return rc;
+    if (!q || !k || !radius) return TRA_ERR_INVALID_ARG;
+    hipError_t e;
+    if (is_dense(r_min, r_max)) {
+        ProfScope p(TRA_KERNEL_FILL, stream);
+        e = tra::launch_fill_dense(g, heads, radius, h_norm, stream);
+        return hip_status(e);
+    }
+
+    Scratch ws(stream);
+    const size_t pooled = (size_t)heads * g.nb * head_dim * sizeof(float);
+    const size_t o_qp = ws.reserve(pooled), o_kp = ws.reserve(pooled);
+    if ((rc = ws.allocate()) != TRA_OK) return rc;
+    float *qp = ws.at<float>(o_qp), *kp = ws.at<float>(o_kp);
+    {
+        ProfScope p(TRA_KERNEL_PACK_POOL, stream);
+        e = tra::launch_pack_pool(head_dim, true, false, (const uint16_t *)q, (const uint16_t *)k,
+                                  nullptr, g, heads, qp, kp, nullptr, nullptr, stream);
+    }
+    if (e == hipSuccess) {
+        ProfScope p(TRA_KERNEL_ENTROPY, stream);
+        e = tra::launch_entropy(head_dim, qp, kp, g, heads, r_min, r_max, radius, h_norm, stream);
+    }
+    return hip_status(e);
+}
+
+int tra_mask(const int32_t *radius, int T, int H, int W, int heads, int block, int r_max,
+             int32_t *idx, int32_t *cnt, hipStream_t stream) {
+    tra::Grid g;
+    int rc = make_grid(T, H, W, block, &g);
+    if (rc != TRA_OK) return rc;
+    if (heads < 1 || r_max < 0) return TRA_ERR_INVALID_ARG;
+    if ((int64_t)heads * g.nb > INT32_MAX) return TRA_ERR_UNSUPPORTED;
+    if (!radius || !idx || !cnt) return TRA_ERR_INVALID_ARG;
+    ProfScope p(TRA_KERNEL_MASK, stream);
+    return hip_status(tra::launch_mask(radius, g, heads, r_max, maxcnt_of(g, r_max), idx, cnt, stream));
+}
+
+int tra_attn(const void *q, const void *k, const void *v, int T, int H, int W, int heads,
+             int head_dim, int block, const int32_t *idx, const int32_t *cnt, int64_t maxcnt,
+             void *out, hipStream_t stream) {
+    tra::Grid g;
+    int rc = make_grid(T, H, W, block, &g);
+    if (rc == TRA_OK) rc = check_dims(heads, head_dim, g);
+    if (rc != TRA_OK) return rc;
+    if (!q || !k || !v || !out) return TRA_ERR_INVALID_ARG;
+    if ((idx == nullptr) != (cnt == nullptr)) return TRA_ERR_INVALID_ARG;
+    if (idx && maxcnt < 1) return TRA_ERR_INVALID_ARG;
+
+    Scratch ws(stream);
+    const size_t tiles = (size_t)heads * g.nb * tra::packed_tile_elems(head_dim) * 2;
+    const size_t o_kt = ws.reserve(tiles), o_vt = ws.reserve(tiles);
+    if ((rc = ws.allocate()) != TRA_OK) return rc;
+    uint16_t *kt = ws.at<uint16_t>(o_kt), *vt = ws.at<uint16_t>(o_vt);
+    hipError_t e;
+    {
+        ProfScope p(TRA_KERNEL_PACK_POOL, stream);
+        e = tra::launch_pack_pool(head_dim, false, true, nullptr, (const uint16_t *)k,
+                                  (const uint16_t *)v, g, heads, nullptr, nullptr, kt, vt, stream);
+    }
+    if (e == hipSuccess) {
+        ProfScope p(TRA_KERNEL_ATTN, stream);
+        e = tra::launch_attn(head_dim, (const uint16_t *)q, kt, vt, idx, cnt, idx ? maxcnt : g.nb,
+                             g, heads, (float *)out, stream);
+    }
+    return hip_status(e);
+}
+
+int tra_attention(const void *q, const void *k, const void *v, int T, int H, int W, int heads,
+                  int head_dim, int block, int r_min, int r_max, void *out, hipStream_t stream) {
+    tra::Grid g;
+    int rc = make_grid(T, H, W, block, &g);
+    if (rc == TRA_OK) rc = check_dims(heads, head_dim, g);
+    if (rc == TRA_OK) rc = check_radii(r_min, r_max);
+    if (rc != TRA_OK) return rc;
+    if (!q || !k || !v || !out) return TRA_ERR_INVALID_ARG;
+
+    const bool dense = is_dense(r_min, r_max);
+    const int64_t maxcnt = maxcnt_of(g, r_max);
+    const size_t rows = (size_t)heads * g.nb;
+    const size_t tiles = rows * tra::packed_tile_elems(head_dim) * 2;
+
+    Scratch ws(stream);
+    const size_t o_kt = ws.reserve(tiles), o_vt = ws.reserve(tiles);
+    size_t o_qp = 0, o_kp = 0, o_r = 0, o_idx = 0, o_cnt = 0;
+    if (!dense) {
+        o_qp = ws.reserve(rows * head_dim * sizeof(float));
+        o_kp = ws.reserve(rows * head_dim * sizeof(float));
+        o_r = ws.reserve(rows * sizeof(int32_t));
+        o_cnt = ws.reserve(rows * sizeof(int32_t));
+        o_idx = ws.reserve(rows * (size_t)maxcnt * sizeof(int32_t));
+    }
+    if ((rc = ws.allocate()) != TRA_OK) return rc;
+    uint16_t *kt = ws.at<uint16_t>(o_kt), *vt = ws.at<uint16_t>(o_vt);
+    const uint16_t *q16 = (const uint16_t *)q, *k16 = (const uint16_t *)k, *v16 = (const uint16_t *)v;
+    float *o32 = (float *)out;
+
+    hipError_t e;
+    if (dense) {
+        {
+            ProfScope p(TRA_KERNEL_PACK_POOL, stream);
+            e = tra::launch_pack_pool(head_dim, false, true, nullptr, k16, v16, g, heads, nullptr,
+                                      nullptr, kt, vt, stream);
+        }
+        if (e == hipSuccess) {
+            ProfScope p(TRA_KERNEL_ATTN, stream);
+            e = tra::launch_attn(head_dim, q16, kt, vt, nullptr, nullptr, g.nb, g, heads, o32, stream);
+        }
+        return hip_status(e);
+    }
+    float *qp = ws.at<float>(o_qp), *kp = ws.at<float>(o_kp);
+    int32_t *radius = ws.at<int32_t>(o_r), *cnt = ws.at<int32_t>(o_cnt), *idx = ws.at<int32_t>(o_idx);
+    {
+        ProfScope p(TRA_KERNEL_PACK_POOL, stream);
+        e = tra::launch_pack_pool(head_dim, true, true, q16, k16, v16, g, heads, qp, kp, kt, vt, stream);
+    }
+    if (e == hipSuccess) {
+        ProfScope p(TRA_KERNEL_ENTROPY, stream);
+        e = tra::launch_entropy(head_dim, qp, kp, g, heads, r_min, r_max, radius, nullptr, stream);
+    }
+    if (e == hipSuccess) {
+        ProfScope p(TRA_KERNEL_MASK, stream);
+        e = tra::launch_mask(radius, g, heads, r_max, maxcnt, idx, cnt, stream);
+    }
+    if (e == hipSuccess) {
+        ProfScope p(TRA_KERNEL_ATTN, stream);
+        e = tra::launch_attn(head_dim, q16, kt, vt, idx, cnt, maxcnt, g, heads, o32, stream);
+    }
+    return hip_status(e);
+}
+
+int tra_profile_begin(void) {
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    g_prof_on = true;
+    return TRA_OK;
+}
+
+int tra_profile_end(double *ms, int *launches, int n) {
+    std::vector<ProfRecord> recs;
+    {
+        std::lock_guard<std::mutex> lock(g_prof_mu);
+        g_prof_on = false;
+        recs.swap(g_prof);
+    }
+    for (int i = 0; i < n; ++i) {
+        if (ms) ms[i] = 0.0;
+        if (launches) launches[i] = 0;
+    }
+    int rc = TRA_OK;
+    for (const ProfRecord &r : recs) {
+        float t = 0.f;
+        if (hipEventSynchronize(r.stop) != hipSuccess || hipEventElapsedTime(&t, r.start, r.stop) != hipSuccess)
+            rc = TRA_ERR_HIP;
+        else if (r.kind < n) {
+            if (ms) ms[r.kind] += t;
+            if (launches) launches[r.kind] += 1;
+        }
+        (void)hipEventDestroy(r.start);
+        (void)hipEventDestroy(r.stop);
+    }
+    return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,178 @@
+/*
+ * tra_attention.h -- C ABI of the entropy-radius block-sparse spatiotemporal
+ * attention library for AMD Instinct MI355X (gfx950).
+ *
+ * The method (Token Radius Attention for Efficient Video Generation,
+ * "2. Methodology" and "The TRA Pipeline"): video tokens on a (T, H, W)
+ * latent grid are grouped into blocks of 64 tokens, each an 8 x 8 spatial tile
+ * inside one frame (the page's tile-major layout).  A cheap probe measures,
+ * per query block, the softmax entropy of block-pooled queries against all
+ * block-pooled keys, and maps it to an integer radius (the page's
+ * entropy -> budget -> radius chain, reduced to one linear quantiser at block
+ * granularity).  Exact softmax attention is then computed for the block's
+ * queries over only the key/value blocks whose Chebyshev distance in
+ * (frame, tile row, tile column) is within that radius -- dynamic block-sparse
+ * attention as described in "AB-Attention speeds up video diffusion
+ * transformers up to 2.23x" (first paragraph), with a radius neighbourhood as
+ * in "Radial Attention to Accelerate Video Generation" ("The idea behind
+ * Radial Attention").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors q, k, v: DEVICE pointers, bfloat16, contiguous
+ *   [heads][T][H][W][head_dim] (batch 1; fold a batch B into heads as B*heads).
+ * - out: DEVICE pointer, float32, same layout.  Only real tokens are written.
+ * - block must be 64 (8 x 8 tiles).  head_dim must be 64 or 128.
+ *   Tiles are counted nby = ceil(H/8), nbx = ceil(W/8) per frame, nb = T*nby*nbx,
+ *   block id kb = (t*nby + by)*nbx + bx; tiles on the right/bottom edge may be
+ *   partial and their missing cells are not tokens (never keys, no output).
+ * - Softmax scale is 1/sqrt(head_dim).
+ * - Radii are integers >= 0; TRA_RADIUS_INF passed as both r_min and r_max
+ *   selects the dense mode (every key block kept, probe skipped).
+ * - V is multiplied on fp16 matrix cores: every |v| must be below 65504 (a
+ *   bfloat16 of magnitude 65536 or more overflows).  Inputs must be finite.
+ * - All work is enqueued on `stream`; no entry point synchronises it.  Scratch
+ *   memory comes from a library-owned stream-ordered pool (hipMallocAsync
+ *   semantics) and is returned to it on `stream` before the call returns.
+ * - The caller owns every pointer it passes; the library keeps none after the
+ *   call returns.  Calls on different streams are independent.
+ * - Argument errors are detected on the host before anything is enqueued and
+ *   return a negative status; launch errors return TRA_ERR_HIP.  Faults inside
+ *   kernels surface at the caller's next synchronisation, as usual in HIP.
+ */
+#ifndef TRA_ATTENTION_H
+#define TRA_ATTENTION_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TRA_RADIUS_INF 2147483647
+
+enum tra_status {
+    TRA_OK = 0,
+    TRA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, r_min > r_max, negative radius */
+    TRA_ERR_UNSUPPORTED = -2, /* block != 64, head_dim not in {64,128}, sizes beyond int32 indexing */
+    TRA_ERR_HIP = -3,         /* a HIP call or kernel launch failed */
+    TRA_ERR_NOMEM = -4        /* scratch allocation failed */
+};
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *tra_status_string(int status);
+
+/* Library ABI version (major*100 + minor). */
+int tra_version(void);
+
+/*
+ * Tile grid of a (T, H, W) token grid: writes nby, nbx, nb (any may be NULL).
+ * Returns TRA_OK, or TRA_ERR_INVALID_ARG / TRA_ERR_UNSUPPORTED for bad sizes.
+ */
+int tra_grid(int T, int H, int W, int block, int *nby, int *nbx, int *nb);
+
+/*
+ * Row stride of the key-block index lists for radii up to r_max:
+ * min(2 r_max + 1, T) * min(2 r_max + 1, nby) * min(2 r_max + 1, nbx)
+ * (nb for TRA_RADIUS_INF).  Returns a negative status on bad arguments.
+ */
+int64_t tra_maxcnt(int T, int H, int W, int block, int r_max);
+
+/*
+ * The whole layer: probe -> radii -> key-block lists -> block-sparse
+ * attention, enqueued on `stream`.
+ *   q, k, v   device bf16 [heads][T][H][W][head_dim]
+ *   r_min, r_max  0 <= r_min <= r_max, or both TRA_RADIUS_INF (dense mode)
+ *   out       device fp32 [heads][T][H][W][head_dim]
+ * Equivalent to tra_probe, then tra_mask, then tra_attn on one stream (the
+ * fused path reads q, k and v from HBM once for the probe and the key/value
+ * tile packing).
+ */
+int tra_attention(const void *q, const void *k, const void *v,
+                  int T, int H, int W, int heads, int head_dim, int block,
+                  int r_min, int r_max, void *out, hipStream_t stream);
+
+/*
+ * Probe (Token Radius Attention ..., "Insight I" and "The TRA Pipeline:
+ * Entropy-to-Budget / Budget-to-Radius"), per (head, query block b):
+ *   Qbar_b, Kbar_b = means of q and k over the real tokens of block b (fp32);
+ *   s_bc = Qbar_b . Kbar_c / sqrt(head_dim) for all nb key blocks c (fp32);
+ *   H_b = entropy of softmax_c(s_bc) in nats, h_norm_b = H_b / ln(nb)
+ *         (0 when nb = 1);
+ *   radius_b = clamp(r_min + floor(h_norm_b * (r_max - r_min + 1)), r_min, r_max),
+ *         the floor taken on the exact product of the stored fp32 h_norm_b
+ *         and the integer (r_max - r_min + 1).
+ *   q, k      device bf16 [heads][T][H][W][head_dim]
+ *   radius    device int32 [heads][nb]   (written)
+ *   h_norm    device fp32 [heads][nb]    (written; may be NULL)
+ * Dense mode (both radii TRA_RADIUS_INF) fills radius with TRA_RADIUS_INF and
+ * h_norm with 0.
+ */
+int tra_probe(const void *q, const void *k, int T, int H, int W, int heads, int head_dim,
+              int block, int r_min, int r_max, int32_t *radius, float *h_norm,
+              hipStream_t stream);
+
+/*
+ * Key-block lists (Token Radius Attention ..., "The TRA Pipeline: Fused CUDA
+ * Kernels": radius comparison and block pruning into a regular block-sparse
+ * mask), per (head, query block qb) with r = radius[h][qb] clamped to
+ * [0, r_max]:
+ *   list = all key blocks kb with max(|t_q - t_k|, |by_q - by_k|, |bx_q - bx_k|) <= r,
+ *          in ascending kb order (always contains qb itself).
+ *   radius  device int32 [heads][nb]
+ *   idx     device int32 [heads][nb][maxcnt], maxcnt = tra_maxcnt(T,H,W,block,r_max);
+ *           only the first cnt entries of each row are written
+ *   cnt     device int32 [heads][nb]
+ * r_max = TRA_RADIUS_INF gives full lists (maxcnt = nb).
+ */
+int tra_mask(const int32_t *radius, int T, int H, int W, int heads, int block, int r_max,
+             int32_t *idx, int32_t *cnt, hipStream_t stream);
+
+/*
+ * Block-sparse attention (AB-Attention ..., first paragraph: exact attention
+ * on the kept key/value blocks only), per head and real query token i of
+ * block qb:
+ *   out_i = sum_j softmax_j(q_i . k_j / sqrt(head_dim)) v_j over the real key
+ *           tokens j of the blocks idx[h][qb][0 .. cnt[h][qb]).
+ *   q, k, v  device bf16 [heads][T][H][W][head_dim]
+ *   idx, cnt device int32 lists as produced by tra_mask with row stride maxcnt;
+ *           both NULL selects the dense mode (every block, ascending)
+ *   out      device fp32 [heads][T][H][W][head_dim]
+ * List entries outside [0, nb) are skipped and cnt is clamped to [0, maxcnt];
+ * a query block whose list keeps no key gets zeros.
+ * Arithmetic: q.k on bf16 matrix cores with fp32 accumulation; online softmax
+ * in fp32; probabilities rounded to fp16 and multiplied with v (converted
+ * exactly bf16 -> fp16) on fp16 matrix cores with fp32 accumulation.
+ */
+int tra_attn(const void *q, const void *k, const void *v, int T, int H, int W, int heads,
+             int head_dim, int block, const int32_t *idx, const int32_t *cnt, int64_t maxcnt,
+             void *out, hipStream_t stream);
+
+/*
+ * Optional per-kernel timing, for benchmarks.  Between tra_profile_begin and
+ * tra_profile_end every kernel this library enqueues is bracketed by a pair of
+ * hipEvents recorded on its own stream (process-wide switch; do not overlap
+ * with calls from other threads).  tra_profile_end synchronises those events,
+ * writes the summed milliseconds ms[kind] and the launch counts
+ * launches[kind] for kind < n (either pointer may be NULL), releases the
+ * events and stops recording.  Kinds:
+ */
+enum tra_kernel_kind {
+    TRA_KERNEL_PACK_POOL = 0, /* pooling of q/k and tile packing of k/v */
+    TRA_KERNEL_ENTROPY = 1,   /* pooled-logit entropy -> radius */
+    TRA_KERNEL_MASK = 2,      /* radius -> key-block lists */
+    TRA_KERNEL_ATTN = 3,      /* block-sparse attention */
+    TRA_KERNEL_FILL = 4,      /* dense-mode radius fill */
+    TRA_KERNEL_KINDS = 5
+};
+int tra_profile_begin(void);
+int tra_profile_end(double *ms, int *launches, int n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRA_ATTENTION_H */

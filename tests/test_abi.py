@@ -1,0 +1,120 @@
+"""The C-ABI library loads, exports what its header declares, and validates
+arguments on the host (no GPU needed: every call here returns before any HIP
+work is enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import content_adaptive_sparse_amd as tra
+from content_adaptive_sparse_amd import build as tra_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tra_attention.h")
+
+INF = tra.TRA_RADIUS_INF
+OK, EINVAL, EUNSUP = 0, -1, -2
+FAKE = 0x1000  # never dereferenced: validation fails before any launch
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(tra_build.LIB_PATH):
+        tra_build.build()
+    return tra.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tra_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_documented_entry_points():
+    names = declared_functions()
+    for n in ["tra_attention", "tra_probe", "tra_mask", "tra_attn", "tra_maxcnt", "tra_grid",
+              "tra_status_string", "tra_version", "tra_profile_begin", "tra_profile_end"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} declared in the header but not exported"
+
+
+def test_status_strings(lib):
+    assert tra.tra_status_string(0) == "TRA_OK"
+    assert tra.tra_status_string(-1) == "TRA_ERR_INVALID_ARG"
+    assert tra.tra_status_string(-2) == "TRA_ERR_UNSUPPORTED"
+    assert tra.tra_status_string(-3) == "TRA_ERR_HIP"
+    assert tra.tra_status_string(-4) == "TRA_ERR_NOMEM"
+    assert tra.tra_status_string(7) == "TRA_ERR_UNKNOWN"
+    assert tra.tra_version() >= 100
+
+
+def test_grid_and_maxcnt_closed_forms(lib):
+    assert tra.tra_grid(21, 30, 52) == (4, 7, 588)
+    assert tra.tra_grid(8, 8, 8) == (1, 1, 8)
+    assert tra.tra_grid(33, 45, 80) == (6, 10, 1980)
+    assert tra.tra_maxcnt(8, 8, 8, 64, 3) == 7
+    assert tra.tra_maxcnt(21, 30, 52, 64, 8) == 476
+    assert tra.tra_maxcnt(61, 30, 52, 64, 12) == 700
+    assert tra.tra_maxcnt(21, 45, 80, 64, 10) == 1260
+    assert tra.tra_maxcnt(33, 45, 80, 64, 16) == 1980
+    assert tra.tra_maxcnt(21, 30, 52, 64, INF) == 588
+    assert tra.tra_maxcnt(21, 30, 52, 64, 0) == 1
+    with pytest.raises(tra.TraError):
+        tra.tra_maxcnt(21, 30, 52, 64, -1)
+    with pytest.raises(tra.TraError):
+        tra.tra_grid(21, 30, 52, 32)
+
+
+def _attention(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, T=4, H=16, W=16, heads=2, d=128, block=64, r_min=1,
+             r_max=4, out=FAKE)
+    a.update(kw)
+    return lib.tra_attention(a["q"], a["k"], a["v"], a["T"], a["H"], a["W"], a["heads"], a["d"],
+                             a["block"], a["r_min"], a["r_max"], a["out"], None)
+
+
+def test_tra_attention_argument_errors(lib):
+    assert _attention(lib, q=None) == EINVAL
+    assert _attention(lib, out=None) == EINVAL
+    assert _attention(lib, T=0) == EINVAL
+    assert _attention(lib, H=-3) == EINVAL
+    assert _attention(lib, heads=0) == EINVAL
+    assert _attention(lib, r_min=5, r_max=4) == EINVAL
+    assert _attention(lib, r_min=-1) == EINVAL
+    assert _attention(lib, r_min=INF, r_max=4) == EINVAL
+    assert _attention(lib, block=32) == EUNSUP
+    assert _attention(lib, d=96) == EUNSUP
+    assert _attention(lib, d=256) == EUNSUP
+    assert _attention(lib, heads=70000) == EUNSUP
+    assert _attention(lib, T=50000, H=50000, W=50000) == EUNSUP
+
+
+def test_staged_entry_point_argument_errors(lib):
+    assert lib.tra_probe(FAKE, FAKE, 4, 16, 16, 2, 128, 64, 1, 4, None, None, None) == EINVAL
+    assert lib.tra_probe(FAKE, FAKE, 4, 16, 16, 2, 128, 64, 4, 1, FAKE, None, None) == EINVAL
+    assert lib.tra_probe(FAKE, FAKE, 4, 16, 16, 2, 80, 64, 1, 4, FAKE, None, None) == EUNSUP
+    assert lib.tra_mask(FAKE, 4, 16, 16, 2, 64, -1, FAKE, FAKE, None) == EINVAL
+    assert lib.tra_mask(None, 4, 16, 16, 2, 64, 3, FAKE, FAKE, None) == EINVAL
+    assert lib.tra_mask(FAKE, 4, 16, 16, 2, 16, 3, FAKE, FAKE, None) == EUNSUP
+    # idx and cnt must both be given or both be NULL
+    assert lib.tra_attn(FAKE, FAKE, FAKE, 4, 16, 16, 2, 128, 64, FAKE, None, 5, FAKE, None) == EINVAL
+    assert lib.tra_attn(FAKE, FAKE, FAKE, 4, 16, 16, 2, 128, 64, FAKE, FAKE, 0, FAKE, None) == EINVAL
+    assert lib.tra_attn(FAKE, FAKE, FAKE, 4, 16, 16, 2, 64, 64, None, None, 0, None, None) == EINVAL
+
+
+def test_profile_switch_without_launches(lib):
+    tra.tra_profile_begin()
+    res = tra.tra_profile_end()
+    assert all(v == (0.0, 0) for v in res.values())
+
+
+def test_binding_refuses_host_tensors(lib):
+    import torch
+    x = torch.zeros(4, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        tra.tra_attention(x, x, x, 1, 1, 4, 1, 1, 64, 0, 0, torch.zeros(4))

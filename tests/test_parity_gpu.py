@@ -1,0 +1,317 @@
+"""GPU parity: the HIP path, called through the C ABI, against the fp64 oracle.
+
+Bars (the same for every case):
+  * radii: identical, except blocks whose oracle h_norm lies within 1e-4 of a
+    quantisation boundary k/(r_max - r_min + 1); those are reported;
+  * key-block lists: bit-exact (idx[:cnt] and cnt) given the same radii;
+  * outputs: max-abs error <= 1e-2 and L1-relative error sum|o - o_ref| /
+    sum|o_ref| <= 1e-3 over real tokens, against the oracle run on the GPU's
+    own radii.
+Small grids compare every output; the full workload shapes compare sampled
+rows (the oracle computes them one by one).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import tra_inputs as ti
+
+torch = pytest.importorskip("torch")
+import content_adaptive_sparse_amd as tra  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+INF = tra.TRA_RADIUS_INF
+MAX_ABS = 1e-2
+L1_REL = 1e-3
+BAND = 1e-4
+
+
+# ---------------------------------------------------------------- helpers --
+
+def dev16(x):
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def gpu_probe(qd, kd, shape, r_min, r_max):
+    heads, T, H, W, d = shape
+    nb = tra.tra_grid(T, H, W)[2]
+    r = torch.empty(heads, nb, dtype=torch.int32, device="cuda")
+    hn = torch.empty(heads, nb, dtype=torch.float32, device="cuda")
+    tra.tra_probe(qd, kd, T, H, W, heads, d, 64, r_min, r_max, r, hn)
+    torch.cuda.synchronize()
+    return hn.cpu().numpy(), r.cpu().numpy()
+
+
+def gpu_mask(radii, shape, r_max):
+    heads, T, H, W, d = shape
+    nb = tra.tra_grid(T, H, W)[2]
+    maxcnt = tra.tra_maxcnt(T, H, W, 64, r_max)
+    rd = torch.from_numpy(np.ascontiguousarray(radii, dtype=np.int32)).cuda()
+    idx = torch.full((heads, nb, maxcnt), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(heads, nb, dtype=torch.int32, device="cuda")
+    tra.tra_mask(rd, T, H, W, heads, 64, r_max, idx, cnt)
+    torch.cuda.synchronize()
+    return idx, cnt, maxcnt
+
+
+def gpu_attn(qd, kd, vd, shape, idx=None, cnt=None, maxcnt=0):
+    heads, T, H, W, d = shape
+    out = torch.full((heads, T, H, W, d), float("nan"), dtype=torch.float32, device="cuda")
+    tra.tra_attn(qd, kd, vd, T, H, W, heads, d, 64, idx, cnt, maxcnt, out)
+    torch.cuda.synchronize()
+    return out
+
+
+def gpu_attention(qd, kd, vd, shape, r_min, r_max):
+    heads, T, H, W, d = shape
+    out = torch.full((heads, T, H, W, d), float("nan"), dtype=torch.float32, device="cuda")
+    tra.tra_attention(qd, kd, vd, T, H, W, heads, d, 64, r_min, r_max, out)
+    torch.cuda.synchronize()
+    return out
+
+
+def assert_close(got, ref, what):
+    got = np.asarray(got, dtype=np.float64)
+    err = np.abs(got - ref)
+    max_abs = float(err.max())
+    l1 = float(err.sum() / np.abs(ref).sum())
+    print(f"[parity] {what}: max_abs={max_abs:.3e} l1_rel={l1:.3e}", flush=True)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    assert max_abs <= MAX_ABS, f"{what}: max-abs {max_abs}"
+    assert l1 <= L1_REL, f"{what}: L1-relative {l1}"
+
+
+def boundary_blocks(hn_ref, r_min, r_max):
+    R = r_max - r_min + 1
+    ks = np.arange(1, R) / R
+    if ks.size == 0:
+        return np.zeros(hn_ref.shape, dtype=bool)
+    return np.min(np.abs(hn_ref[..., None] - ks), axis=-1) < BAND
+
+
+def check_radii(hn_gpu, r_gpu, hn_ref, r_ref, r_min, r_max, what):
+    R = r_max - r_min + 1
+    # the radius follows the stored fp32 h_norm exactly
+    own = np.clip(r_min + np.floor(hn_gpu.astype(np.float64) * R), r_min, r_max).astype(np.int64)
+    assert np.array_equal(own, r_gpu), f"{what}: radius does not follow its own h_norm"
+    band = boundary_blocks(hn_ref, r_min, r_max)
+    diff = r_gpu != r_ref
+    print(f"[parity] {what}: h_norm max|d|={np.abs(hn_gpu - hn_ref).max():.2e}, "
+          f"boundary blocks={int(band.sum())}, radius mismatches={int(diff.sum())}", flush=True)
+    for h, b in zip(*np.nonzero(band)):
+        print(f"[boundary] {what} head {h} block {b}: h_norm oracle={hn_ref[h, b]:.7f} "
+              f"gpu={hn_gpu[h, b]:.7f} r oracle={r_ref[h, b]} gpu={r_gpu[h, b]}", flush=True)
+    assert not (diff & ~band).any(), f"{what}: radius mismatch outside the boundary band"
+
+
+def check_lists(idx_g, cnt_g, radii, shape, maxcnt, what):
+    heads, T, H, W, d = shape
+    idx_o, cnt_o = oracle.block_lists(radii, T, H, W, maxcnt=maxcnt)
+    cnt_g = cnt_g.cpu().numpy()
+    idx_g = idx_g.cpu().numpy()
+    assert np.array_equal(cnt_g, cnt_o), f"{what}: cnt differs"
+    valid = np.arange(maxcnt)[None, None, :] < cnt_o[..., None]
+    assert np.array_equal(np.where(valid, idx_g, -1), np.where(valid, idx_o, -1)), f"{what}: idx differs"
+
+
+def sample_rows(shape, n, seed=0):
+    """Seeded sample of (head * N + token) rows, always including edge-tile tokens."""
+    heads, T, H, W, d = shape
+    N = T * H * W
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(heads * N, size=min(n, heads * N), replace=False).tolist())
+    for h in (0, heads - 1):
+        for t, y, x in ((0, 0, 0), (T - 1, H - 1, W - 1), (T // 2, H - 1, 0), (0, 0, W - 1)):
+            rows.add(h * N + (t * H + y) * W + x)
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+# ------------------------------------------------------ small full grids --
+
+SMALL = [
+    # (T, H, W, heads, d)
+    (3, 20, 28, 2, 128),   # 3x4 tiles per frame, ragged bottom and right
+    (4, 16, 24, 2, 64),    # exact tiles
+    (2, 13, 9, 3, 128),    # 2x2 tiles, heavily ragged
+    (1, 5, 7, 1, 64),      # one partial tile: nb = 1
+    (1, 1, 1, 2, 128),     # a single token
+    (5, 8, 8, 1, 128),     # one tile per frame
+]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_small_grid_staged_path(shape):
+    heads, T, H, W, d = shape[3], shape[0], shape[1], shape[2], shape[4]
+    shp = (heads, T, H, W, d)
+    print(f"[case] staged {shp}", flush=True)
+    q, k, v = ti.make_inputs(T, H, W, heads, d, seed=1, cfg=21)
+    qd, kd, vd = dev16(q), dev16(k), dev16(v)
+    r_min, r_max = 0, 2
+    hn_g, r_g = gpu_probe(qd, kd, shp, r_min, r_max)
+    hn_o, r_o = oracle.probe(q, k, r_min, r_max)
+    check_radii(hn_g, r_g, hn_o, r_o, r_min, r_max, f"probe {shp}")
+    idx, cnt, maxcnt = gpu_mask(r_g, shp, r_max)
+    check_lists(idx, cnt, r_g, shp, maxcnt, f"mask {shp}")
+    out = gpu_attn(qd, kd, vd, shp, idx, cnt, maxcnt).cpu().numpy()
+    ref = oracle.attention(q, k, v, r_g)
+    assert_close(out, ref, f"attn {shp}")
+    # the fused call gives the same result as the staged calls
+    out2 = gpu_attention(qd, kd, vd, shp, r_min, r_max).cpu().numpy()
+    assert np.array_equal(out, out2)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_random_radii_and_dense(d):
+    T, H, W, heads = 4, 19, 27, 2
+    shp = (heads, T, H, W, d)
+    print(f"[case] random radii {shp}", flush=True)
+    q, k, v = ti.random_qkv(T, H, W, heads, d, seed=5, scale=1.5)
+    qd, kd, vd = dev16(q), dev16(k), dev16(v)
+    nb = tra.tra_grid(T, H, W)[2]
+    rng = np.random.default_rng(3)
+    for radii, r_max in ((rng.integers(0, 4, size=(heads, nb)), 3),
+                         (np.zeros((heads, nb)), 0),
+                         (np.full((heads, nb), 9), 9)):
+        radii = radii.astype(np.int32)
+        idx, cnt, maxcnt = gpu_mask(radii, shp, r_max)
+        check_lists(idx, cnt, radii, shp, maxcnt, f"mask r_max={r_max}")
+        out = gpu_attn(qd, kd, vd, shp, idx, cnt, maxcnt).cpu().numpy()
+        assert_close(out, oracle.attention(q, k, v, radii), f"attn r_max={r_max} d={d}")
+    dense = gpu_attn(qd, kd, vd, shp).cpu().numpy()
+    ref = oracle.attention(q, k, v, oracle.dense_radii(heads, nb))
+    assert_close(dense, ref, f"dense d={d}")
+    dense2 = gpu_attention(qd, kd, vd, shp, INF, INF).cpu().numpy()
+    assert np.array_equal(dense, dense2)
+    # a radius covering the whole grid keeps every block in the same order: same bits
+    idx, cnt, maxcnt = gpu_mask(np.full((heads, nb), 9, dtype=np.int32), shp, 9)
+    wide = gpu_attn(qd, kd, vd, shp, idx, cnt, maxcnt).cpu().numpy()
+    assert np.array_equal(wide, dense)
+
+
+def test_config0_end_to_end():
+    c = ti.CONFIGS[0]
+    shp = (c.heads, c.T, c.H, c.W, c.d)
+    print(f"[case] config0 {shp}", flush=True)
+    q, k, v = ti.make_config_inputs(0)
+    qd, kd, vd = dev16(q), dev16(k), dev16(v)
+    hn_g, r_g = gpu_probe(qd, kd, shp, c.r_min, c.r_max)
+    hn_o, r_o = oracle.probe(q, k, c.r_min, c.r_max)
+    check_radii(hn_g, r_g, hn_o, r_o, c.r_min, c.r_max, "config0 probe")
+    out = gpu_attention(qd, kd, vd, shp, c.r_min, c.r_max).cpu().numpy()
+    assert_close(out, oracle.attention(q, k, v, r_g), "config0 attention")
+
+
+# --------------------------------------------------------------- edge cases --
+
+def test_list_edge_cases():
+    T, H, W, heads, d = 2, 16, 16, 1, 128
+    shp = (heads, T, H, W, d)
+    print(f"[case] list edge cases {shp}", flush=True)
+    q, k, v = ti.random_qkv(T, H, W, heads, d, seed=9)
+    qd, kd, vd = dev16(q), dev16(k), dev16(v)
+    nb = tra.tra_grid(T, H, W)[2]
+    maxcnt = 4
+    idx = np.full((heads, nb, maxcnt), -1, dtype=np.int32)
+    cnt = np.zeros((heads, nb), dtype=np.int32)
+    # block 0: empty list -> zeros; block 1: {1, 5}; block 2: invalid entries
+    # are skipped; block 3: cnt beyond maxcnt is clamped; others: own block
+    idx[0, 1, :2] = [1, 5]
+    cnt[0, 1] = 2
+    idx[0, 2, :4] = [2, -3, 99, 6]
+    cnt[0, 2] = 4
+    idx[0, 3, :4] = [0, 1, 2, 3]
+    cnt[0, 3] = 100
+    for b in range(4, nb):
+        idx[0, b, 0] = b
+        cnt[0, b] = 1
+    out = gpu_attn(qd, kd, vd, shp, torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(),
+                   maxcnt).cpu().numpy().reshape(heads, -1, d)
+    tok = np.arange(T * H * W).reshape(T, H, W)
+    blocks = [tok[t, 8 * by:8 * by + 8, 8 * bx:8 * bx + 8].ravel()
+              for t in range(T) for by in range(2) for bx in range(2)]
+    qf, kf, vf = (ti.bf16_to_f32(a).astype(np.float64).reshape(heads, -1, d) for a in (q, k, v))
+
+    def ref_rows(qblock, kblocks):
+        keys = np.concatenate([blocks[b] for b in kblocks])
+        s = qf[0, blocks[qblock]] @ kf[0, keys].T / math.sqrt(d)
+        w = np.exp(s - s.max(axis=1, keepdims=True))
+        return (w / w.sum(axis=1, keepdims=True)) @ vf[0, keys]
+
+    assert (out[0, blocks[0]] == 0).all()
+    assert_close(out[0, blocks[1]], ref_rows(1, [1, 5]), "list {1,5}")
+    assert_close(out[0, blocks[2]], ref_rows(2, [2, 6]), "invalid entries skipped")
+    assert_close(out[0, blocks[3]], ref_rows(3, [0, 1, 2, 3]), "cnt clamped")
+    for b in range(4, nb):
+        assert_close(out[0, blocks[b]], ref_rows(b, [b]), f"own block {b}")
+
+
+def test_mask_clamps_radius_to_r_max():
+    T, H, W, heads = 6, 24, 40, 1
+    shp = (heads, T, H, W, 64)
+    nb = tra.tra_grid(T, H, W)[2]
+    radii = np.array([[7, -2] + [1] * (nb - 2)], dtype=np.int32)
+    idx, cnt, maxcnt = gpu_mask(radii, shp, 2)
+    check_lists(idx, cnt, np.clip(radii, 0, 2), shp, maxcnt, "clamped radii")
+
+
+def test_deterministic():
+    T, H, W, heads, d = 3, 30, 52, 2, 128
+    shp = (heads, T, H, W, d)
+    q, k, v = ti.make_inputs(T, H, W, heads, d, seed=2, cfg=22)
+    qd, kd, vd = dev16(q), dev16(k), dev16(v)
+    a = gpu_attention(qd, kd, vd, shp, 1, 3).cpu().numpy()
+    b = gpu_attention(qd, kd, vd, shp, 1, 3).cpu().numpy()
+    assert np.array_equal(a, b)
+
+
+# ------------------------------------------------- full workload shapes --
+
+_CACHE = {}
+
+
+def config_inputs(cfg):
+    if cfg not in _CACHE:
+        _CACHE.clear()
+        _CACHE[cfg] = ti.make_config_inputs(cfg)
+    return _CACHE[cfg]
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_full_config(cfg):
+    c = ti.CONFIGS[cfg]
+    shp = (c.heads, c.T, c.H, c.W, c.d)
+    print(f"[case] config{cfg} {shp} r=[{c.r_min},{c.r_max}]", flush=True)
+    q, k, v = config_inputs(cfg)
+    qd, kd, vd = dev16(q), dev16(k), dev16(v)
+    hn_g, r_g = gpu_probe(qd, kd, shp, c.r_min, c.r_max)
+    hn_o, r_o = oracle.probe(q, k, c.r_min, c.r_max)
+    check_radii(hn_g, r_g, hn_o, r_o, c.r_min, c.r_max, f"config{cfg} probe")
+    idx, cnt, maxcnt = gpu_mask(r_g, shp, c.r_max)
+    check_lists(idx, cnt, r_g, shp, maxcnt, f"config{cfg} mask")
+    nb = tra.tra_grid(c.T, c.H, c.W)[2]
+    density = cnt.sum().item() / (c.heads * nb * nb)
+    print(f"[parity] config{cfg}: block density {density:.4f}", flush=True)
+    del idx, cnt
+    out = gpu_attention(qd, kd, vd, shp, c.r_min, c.r_max)
+    rows = sample_rows(shp, 96, seed=cfg)
+    got = out.view(-1, c.d)[torch.from_numpy(rows).cuda()].cpu().numpy()
+    del out
+    ref = oracle.attention_rows(q, k, v, r_g, rows)
+    assert_close(got, ref, f"config{cfg} attention (sampled rows)")
+
+
+def test_full_config1_dense_mode():
+    c = ti.CONFIGS[1]
+    shp = (c.heads, c.T, c.H, c.W, c.d)
+    print(f"[case] config1 dense {shp}", flush=True)
+    q, k, v = config_inputs(1)
+    qd, kd, vd = dev16(q), dev16(k), dev16(v)
+    out = gpu_attention(qd, kd, vd, shp, INF, INF)
+    rows = sample_rows(shp, 48, seed=11)
+    got = out.view(-1, c.d)[torch.from_numpy(rows).cuda()].cpu().numpy()
+    nb = tra.tra_grid(c.T, c.H, c.W)[2]
+    ref = oracle.attention_rows(q, k, v, oracle.dense_radii(c.heads, nb), rows)
+    assert_close(got, ref, "config1 dense (sampled rows)")

@@ -26,6 +26,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 template <typename T>
 __device__ __forceinline__ T lds_load16(const uint16_t *p) {
@@ -33,9 +34,14 @@ __device__ __forceinline__ T lds_load16(const uint16_t *p) {
 }
 
 constexpr int kAttnThreads = 128;
+// The running max is only moved (and O, l rescaled) when a tile's max exceeds
+// it by more than this many powers of two; in between, probabilities are
+// taken against the stale max (at most 2^8, exact in fp16) and the final
+// normalisation by l uses the same reference, so the result is unchanged.
+constexpr float kRescaleLog2 = 8.0f;
 
 template <int D>
-__global__ __launch_bounds__(kAttnThreads) void attn_kernel(
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kt,
     const uint16_t *__restrict__ vt, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ cnt, int64_t maxcnt, Grid g, int heads, int per_xcd,
@@ -45,10 +51,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
     constexpr int CH = D / 8;                   // 16-byte chunks per K row
     constexpr int KSW = (CH < 16 ? CH : 16) - 1;
     constexpr int TILE = kBlockTokens * D;      // elements of one K or V^T tile
-    constexpr int CPT = 2 * TILE / 8 / kAttnThreads;  // 16-byte chunks per thread per block
-    static_assert(CPT % 2 == 0, "chunk split");
+    constexpr int CPT = TILE / 8 / kAttnThreads;  // 16-byte chunks per thread per tile
 
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds[TILE];
 
     // Consecutive workgroup ids land on different XCDs; give every XCD a
     // contiguous range of (head, query block) so its L2 sees neighbouring
@@ -83,6 +89,37 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
     const size_t qtok = (size_t)h * g.T * g.H * g.W +
                         ((size_t)t * g.H + min(qy, g.H - 1)) * g.W + min(qx, g.W - 1);
 
+    auto block_at = [&](int j) -> int { return list ? list[j] : j; };
+    auto next_valid = [&](int j) -> int {
+        while (j < n && (unsigned)block_at(j) >= (unsigned)g.nb) ++j;
+        return j;
+    };
+
+    // Register staging of one 16 KB tile: global -> VGPR -> LDS.  (Written as
+    // macros over a fixed-size array so it stays in registers.)
+    u32x4_t stage[CPT];
+    const size_t head_tiles = (size_t)h * g.nb;
+#define TRA_FETCH(base, blk)                                                                 \
+    do {                                                                                     \
+        const u32x4_t *src_ = reinterpret_cast<const u32x4_t *>((base) + (head_tiles + (blk)) * TILE); \
+        _Pragma("unroll") for (int i_ = 0; i_ < CPT; ++i_) stage[i_] = src_[tid + kAttnThreads * i_]; \
+    } while (0)
+#define TRA_PUT(dst)                                                                         \
+    do {                                                                                     \
+        _Pragma("unroll") for (int i_ = 0; i_ < CPT; ++i_)                                   \
+            reinterpret_cast<u32x4_t *>(dst)[tid + kAttnThreads * i_] = stage[i_];            \
+    } while (0)
+
+    int j = next_valid(0);
+    int kb = j < n ? block_at(j) : -1;
+    float *o = out + qtok * D;
+    if (kb < 0) {  // nothing kept: zeros
+        if (qreal)
+            for (int c = 0; c < D / 2; c += 4)
+                *reinterpret_cast<float4 *>(o + c + (D / 2) * hl) = make_float4(0.f, 0.f, 0.f, 0.f);
+        return;
+    }
+
     bf16x8_t qreg[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -93,47 +130,19 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
-    float m_run = -1e30f, l_run = 0.f;
+    float m_ref = -1e30f, l_run = 0.f;
 
-    auto block_at = [&](int j) -> int { return list ? list[j] : j; };
-    auto next_valid = [&](int j) -> int {
-        while (j < n && (unsigned)block_at(j) >= (unsigned)g.nb) ++j;
-        return j;
-    };
+    // prologue: tile 0 into LDS, K of tile 1 in flight
+    TRA_FETCH(kt, kb);
+    TRA_PUT(k_lds);
+    TRA_FETCH(vt, kb);
+    TRA_PUT(v_lds);
+    int jn = next_valid(j + 1);
+    int kbn = jn < n ? block_at(jn) : -1;
+    TRA_FETCH(kt, kbn >= 0 ? kbn : kb);
+    __syncthreads();
 
-    uint4 pre[CPT];
-    auto fetch = [&](int kb) {
-        const uint4 *ks = reinterpret_cast<const uint4 *>(kt + ((size_t)h * g.nb + kb) * TILE);
-        const uint4 *vs = reinterpret_cast<const uint4 *>(vt + ((size_t)h * g.nb + kb) * TILE);
-#pragma unroll
-        for (int i = 0; i < CPT / 2; ++i) {
-            pre[i] = ks[tid + kAttnThreads * i];
-            pre[CPT / 2 + i] = vs[tid + kAttnThreads * i];
-        }
-    };
-
-    int j = next_valid(0);
-    int kb = j < n ? block_at(j) : -1;
-    if (kb >= 0) fetch(kb);
-
-    const uint16_t *Ks = lds;
-    const uint16_t *Vs = lds + TILE;
-
-    while (kb >= 0) {
-        __syncthreads();
-        {
-            uint4 *dst = reinterpret_cast<uint4 *>(lds);
-#pragma unroll
-            for (int i = 0; i < CPT / 2; ++i) {
-                dst[tid + kAttnThreads * i] = pre[i];
-                dst[TILE / 8 + tid + kAttnThreads * i] = pre[CPT / 2 + i];
-            }
-        }
-        __syncthreads();
-        const int jn = next_valid(j + 1);
-        const int kbn = jn < n ? block_at(jn) : -1;
-        if (kbn >= 0) fetch(kbn);
-
+    while (true) {
         // ---- S^T = K Q^T (keys 0..31 and 32..63 of the tile) ----
         f32x16_t s[2];
 #pragma unroll
@@ -144,10 +153,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int cs = (2 * ks + hl) ^ (key & KSW);
-                const bf16x8_t a = lds_load16<bf16x8_t>(Ks + key * D + 8 * cs);
+                const bf16x8_t a = lds_load16<bf16x8_t>(k_lds + key * D + 8 * cs);
                 s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s[mt], 0, 0, 0);
             }
         }
+        __syncthreads();  // every wave is done with k_lds; v_lds holds this tile's V
+        // (past the end of the list this restages the current tile: harmless)
+        TRA_PUT(k_lds);
+        TRA_FETCH(vt, kbn >= 0 ? kbn : kb);
 
         // ---- missing key cells of an edge tile -> -inf ----
         const int kby = (kb / g.nbx) % g.nby, kbx = kb % g.nbx;
@@ -164,33 +177,34 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
                 }
         }
 
-        // ---- online softmax (base 2, scale folded) ----
-        float mx = -1e30f;
+        // ---- online softmax, base 2 with the scale folded into one FMA ----
+        float mx = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                s[mt][r] *= scale_log2;
-                mx = fmaxf(mx, s[mt][r]);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+        const bool grow = mx > m_ref + kRescaleLog2;
+        if (__any(grow)) {
+            const float m_new = grow ? mx : m_ref;
+            const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[mt][r] *= alpha;
+            m_ref = m_new;
+        }
         float psum = 0.f;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(s[mt][r] - m_new);
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][r], scale_log2, -m_ref));
                 s[mt][r] = p;
                 psum += p;
             }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[mt][r] *= alpha;
+        l_run += psum;
 
         // P^T as the B operand: k-step ks2 covers keys 16 ks2 .. 16 ks2 + 15,
         // held in s[ks2 / 2] registers 8 (ks2 % 2) .. + 7.
@@ -207,19 +221,25 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
 #pragma unroll
             for (int ks2 = 0; ks2 < 4; ++ks2) {
                 const int cs = (2 * ks2 + hl) ^ ((d >> 1) & 7);
-                const f16x8_t a = lds_load16<f16x8_t>(Vs + d * 64 + 8 * cs);
+                const f16x8_t a = lds_load16<f16x8_t>(v_lds + d * 64 + 8 * cs);
                 acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pk[ks2], acc[mt], 0, 0, 0);
             }
         }
-
+        if (kbn < 0) break;
+        __syncthreads();  // every wave is done with v_lds; k_lds holds the next K
+        TRA_PUT(v_lds);
         j = jn;
         kb = kbn;
+        jn = next_valid(j + 1);
+        kbn = jn < n ? block_at(jn) : -1;
+        TRA_FETCH(kt, kbn >= 0 ? kbn : kb);
     }
+#undef TRA_FETCH
+#undef TRA_PUT
 
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     if (qreal) {
-        float *o = out + qtok * D;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll

@@ -94,6 +94,9 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--only-layer", action="store_true",
                     help="time the layer only (for profiler runs)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (a known-size "
+                         "reference for hardware traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer shards "
@@ -117,6 +120,15 @@ def main():
     qd, kd, vd = dev(q), dev(k), dev(v)
     out = torch.empty(heads, T, H, W, d, dtype=torch.float32, device="cuda")
     flops_pair = 4 * 64 * 64 * d
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: {args.calib_copy_mib} MiB read + {args.calib_copy_mib} MiB written")
+        del src, dst
 
     def layer(r_min, r_max):
         tra.tra_attention(qd, kd, vd, T, H, W, heads, d, 64, r_min, r_max, out)

@@ -28,7 +28,10 @@ int make_grid(int T, int H, int W, int block, tra::Grid *g) {
     const int64_t nby = (H + tra::kTileSide - 1) / tra::kTileSide;
     const int64_t nbx = (W + tra::kTileSide - 1) / tra::kTileSide;
     const int64_t nb = (int64_t)T * nby * nbx;
-    if (nb > INT32_MAX || (int64_t)T * H * W > INT32_MAX) return TRA_ERR_UNSUPPORTED;
+    // block ids stay below 2^24 and tile counts per axis below 2^15 (the
+    // attention kernel's multiply-shift division is exact in that range)
+    if (nb >= (int64_t(1) << 24) || nby >= (1 << 15) || nbx >= (1 << 15)) return TRA_ERR_UNSUPPORTED;
+    if ((int64_t)T * H * W > INT32_MAX) return TRA_ERR_UNSUPPORTED;
     g->T = T; g->H = H; g->W = W;
     g->nby = (int)nby; g->nbx = (int)nbx; g->nb = (int)nb;
     return TRA_OK;

@@ -7,9 +7,11 @@
 // kept blocks come from the radius mask and run on a block-sparse backend,
 // which this kernel is.
 //
-// One workgroup (two wave64) per (head, query block); wave w owns query rows
-// 32 w .. 32 w + 31 of the tile.  For each kept key block, its packed K tile
-// (bf16) and V^T tile (fp16) are copied into LDS, then every wave computes
+// One wave64 workgroup per (head, query block), holding all 64 queries as two
+// 32-query tiles.  Each kept key block is processed as two 32-key halves: the
+// packed K rows (bf16) and V^T rows (fp16) of a half are copied straight from
+// global memory into a two-slot LDS ring (the next half lands while the
+// current one is computed), and the wave computes
 //   S^T = K Q^T        v_mfma_f32_32x32x16_bf16, fp32 accumulation
 //   online softmax     per query = per lane column, exp2 with the scale folded
 //   O^T += V^T P^T     v_mfma_f32_32x32x16_f16 (P rounded to fp16)
@@ -25,6 +27,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -33,92 +36,149 @@ __device__ __forceinline__ T lds_load16(const uint16_t *p) {
     return *reinterpret_cast<const T *>(p);
 }
 
-constexpr int kAttnThreads = 128;
+// Exact n / d for 0 <= n < 2^24 and 1 <= d < 2^15 with m = ceil(2^39 / d):
+// the product's error term is below n / 2^39 < 1 / d, so the floor is exact.
+struct FastDiv {
+    uint64_t m;
+    uint32_t d;
+};
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+    return (uint32_t)(((uint64_t)n * f.m) >> 39);
+}
+
+constexpr int kAttnThreads = 256;
+// s_waitcnt immediates for gfx9 (vmcnt bits [3:0] and [15:14], expcnt [6:4],
+// lgkmcnt [11:8]); counters not waited on are left at their no-wait maxima.
+constexpr int wait_vmcnt(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
+constexpr int kWaitVmcnt0 = wait_vmcnt(0);
+constexpr int kWaitLgkmcnt0 = 0xC07F;
 // The running max is only moved (and O, l rescaled) when a tile's max exceeds
 // it by more than this many powers of two; in between, probabilities are
 // taken against the stale max (at most 2^8, exact in fp16) and the final
 // normalisation by l uses the same reference, so the result is unchanged.
 constexpr float kRescaleLog2 = 8.0f;
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void global_void_t;
+// The key lists are never written while the kernel runs; reading them through
+// the constant address space lets wave-uniform reads use scalar loads, which
+// do not share the vector-memory counter with the in-flight LDS copies.
+typedef __attribute__((address_space(4))) const int32_t const_i32_t;
+
+// A query block's key list read through scalar loads: entries outside
+// [0, nb) are skipped; `cur` is the block at the cursor or INT32_MAX once the
+// list is exhausted (so the smaller of two cursors is the next union entry).
+struct ListCursor {
+    const const_i32_t *list;  // nullptr: every block 0 .. nb-1 (dense)
+    int n, j, cur;
+};
+
+__device__ __forceinline__ void list_seek(ListCursor &c, int nb) {
+    while (c.j < c.n) {
+        const int b = c.list ? c.list[c.j] : c.j;
+        if ((unsigned)b < (unsigned)nb) {
+            c.cur = b;
+            return;
+        }
+        ++c.j;
+    }
+    c.cur = INT32_MAX;
+}
+
 template <int D>
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
+__global__ __launch_bounds__(kAttnThreads, 3) void attn_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kt,
     const uint16_t *__restrict__ vt, const int32_t *__restrict__ idx,
-    const int32_t *__restrict__ cnt, int64_t maxcnt, Grid g, int heads, int per_xcd,
-    float *__restrict__ out, float scale_log2) {
+    const int32_t *__restrict__ cnt, int64_t maxcnt, Grid g, int heads, int pairs_per_head,
+    int per_xcd, FastDiv div_nbx, FastDiv div_nby, float *__restrict__ out, float scale_log2) {
     constexpr int KS = D / 16;                  // k-steps of Q.K^T
     constexpr int MT = D / 32;                  // 32-row tiles of O^T
     constexpr int CH = D / 8;                   // 16-byte chunks per K row
     constexpr int KSW = (CH < 16 ? CH : 16) - 1;
-    constexpr int TILE = kBlockTokens * D;      // elements of one K or V^T tile
-    constexpr int CPT = TILE / 8 / kAttnThreads;  // 16-byte chunks per thread per tile
+    constexpr int HALF = 32 * D;                // elements of a 32-key K or V^T half tile
+    constexpr int PIECES = HALF * 2 / 1024;     // 1 KB copies per half tile and operand
+    constexpr int WAVES = kAttnThreads / 64;
+    constexpr int PPW = PIECES / WAVES;         // pieces per wave and operand
+    static_assert(PPW * WAVES == PIECES, "every piece copied exactly once");
+    static_assert(PIECES * 512 == HALF, "pieces tile the half exactly (no copy past a slot)");
 
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t v_lds[TILE];
+    // Two-slot ring of half tiles: [slot][0 = K rows, 1 = V^T rows].
+    __shared__ __attribute__((aligned(1024))) uint16_t ring[2][2][HALF];
 
+    // Work item: a pair of neighbouring query blocks (2p, 2p + 1) of one head.
     // Consecutive workgroup ids land on different XCDs; give every XCD a
-    // contiguous range of (head, query block) so its L2 sees neighbouring
-    // query blocks, whose key lists overlap.
-    const int64_t total = (int64_t)heads * g.nb;
-    const int64_t wg = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    if (wg >= total) return;
-    const int h = (int)(wg / g.nb);
-    const int qb = (int)(wg % g.nb);
+    // contiguous range of items so its L2 sees neighbouring query blocks.
+    const int64_t total = (int64_t)heads * pairs_per_head;
+    const int64_t item = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (item >= total) return;
+    const int h = (int)(item / pairs_per_head);
+    const int pair = (int)(item % pairs_per_head);
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int hl = lane >> 5, l32 = lane & 31;
+    const int side = wave >> 1;          // 0: block 2 pair, 1: block 2 pair + 1
+    const int qb = 2 * pair + side;      // this wave's query block (may be nb: absent)
 
-    int n;
-    const int32_t *list = nullptr;
-    if (idx) {
-        const int64_t c = cnt[wg];
-        n = (int)(c < 0 ? 0 : (c > maxcnt ? maxcnt : c));
-        list = idx + wg * maxcnt;
-    } else {
-        n = g.nb;
+    // Both cursors are tracked (redundantly) by every wave.
+    ListCursor ca, cb;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        ListCursor &c = k ? cb : ca;
+        const int b = 2 * pair + k;
+        c.j = 0;
+        c.list = nullptr;
+        if (b >= g.nb) {
+            c.n = 0;
+        } else if (idx) {
+            const int64_t row = (int64_t)h * g.nb + b;
+            const int64_t m = ((const const_i32_t *)cnt)[row];
+            c.n = (int)(m < 0 ? 0 : (m > maxcnt ? maxcnt : m));
+            c.list = (const const_i32_t *)idx + row * maxcnt;
+        } else {
+            c.n = g.nb;
+        }
+        list_seek(c, g.nb);
     }
 
     // This lane's query token (clamped into the grid for the missing cells of
-    // an edge tile; such rows are computed but never stored).
+    // an edge tile, and for an absent block; such rows are never stored).
     const int plane = g.nby * g.nbx;
-    const int t = qb / plane, by = (qb / g.nbx) % g.nby, bx = qb % g.nbx;
-    const int qi = 32 * wave + l32;
+    const int qbc = qb < g.nb ? qb : g.nb - 1;
+    const int t = qbc / plane, by = (qbc / g.nbx) % g.nby, bx = qbc % g.nbx;
+    const int qi = 32 * (wave & 1) + l32;
     const int qy = kTileSide * by + (qi >> 3), qx = kTileSide * bx + (qi & 7);
-    const bool qreal = qy < g.H && qx < g.W;
+    const bool qreal = qb < g.nb && qy < g.H && qx < g.W;
     const size_t qtok = (size_t)h * g.T * g.H * g.W +
                         ((size_t)t * g.H + min(qy, g.H - 1)) * g.W + min(qx, g.W - 1);
-
-    auto block_at = [&](int j) -> int { return list ? list[j] : j; };
-    auto next_valid = [&](int j) -> int {
-        while (j < n && (unsigned)block_at(j) >= (unsigned)g.nb) ++j;
-        return j;
-    };
-
-    // Register staging of one 16 KB tile: global -> VGPR -> LDS.  (Written as
-    // macros over a fixed-size array so it stays in registers.)
-    u32x4_t stage[CPT];
-    const size_t head_tiles = (size_t)h * g.nb;
-#define TRA_FETCH(base, blk)                                                                 \
-    do {                                                                                     \
-        const u32x4_t *src_ = reinterpret_cast<const u32x4_t *>((base) + (head_tiles + (blk)) * TILE); \
-        _Pragma("unroll") for (int i_ = 0; i_ < CPT; ++i_) stage[i_] = src_[tid + kAttnThreads * i_]; \
-    } while (0)
-#define TRA_PUT(dst)                                                                         \
-    do {                                                                                     \
-        _Pragma("unroll") for (int i_ = 0; i_ < CPT; ++i_)                                   \
-            reinterpret_cast<u32x4_t *>(dst)[tid + kAttnThreads * i_] = stage[i_];            \
-    } while (0)
-
-    int j = next_valid(0);
-    int kb = j < n ? block_at(j) : -1;
     float *o = out + qtok * D;
-    if (kb < 0) {  // nothing kept: zeros
+
+    int kb = min(ca.cur, cb.cur);
+    if (kb == INT32_MAX) {  // neither block keeps anything: zeros
         if (qreal)
             for (int c = 0; c < D / 2; c += 4)
                 *reinterpret_cast<float4 *>(o + c + (D / 2) * hl) = make_float4(0.f, 0.f, 0.f, 0.f);
         return;
     }
+
+    // Direct global -> LDS copy of half tile `hf` of block `blk` into ring slot
+    // `slot`: each wave moves PPW 1 KB pieces of K and of V^T; lane l lands 16
+    // bytes at piece base + 16 l.
+    const size_t head_tiles = (size_t)h * g.nb;
+#define TRA_ISSUE(blk, hf, slot)                                                              \
+    do {                                                                                      \
+        const char *ks_ = reinterpret_cast<const char *>(kt + ((head_tiles + (blk)) * 64 + 32 * (hf)) * D); \
+        const char *vs_ = reinterpret_cast<const char *>(vt + (head_tiles + (blk)) * 64 * D + (hf) * HALF); \
+        _Pragma("unroll") for (int i_ = 0; i_ < PPW; ++i_) {                                 \
+            const int piece_ = wave * PPW + i_;                                              \
+            __builtin_amdgcn_global_load_lds(                                                \
+                (const global_void_t *)(ks_ + piece_ * 1024 + lane * 16),                    \
+                (lds_void_t *)&ring[slot][0][piece_ * 512], 16, 0, 0);                       \
+            __builtin_amdgcn_global_load_lds(                                                \
+                (const global_void_t *)(vs_ + piece_ * 1024 + lane * 16),                    \
+                (lds_void_t *)&ring[slot][1][piece_ * 512], 16, 0, 0);                       \
+        }                                                                                     \
+    } while (0)
 
     bf16x8_t qreg[KS];
 #pragma unroll
@@ -132,110 +192,136 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
         for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
     float m_ref = -1e30f, l_run = 0.f;
 
-    // prologue: tile 0 into LDS, K of tile 1 in flight
-    TRA_FETCH(kt, kb);
-    TRA_PUT(k_lds);
-    TRA_FETCH(vt, kb);
-    TRA_PUT(v_lds);
-    int jn = next_valid(j + 1);
-    int kbn = jn < n ? block_at(jn) : -1;
-    TRA_FETCH(kt, kbn >= 0 ? kbn : kb);
+    // Union walk: the copy cursor (pa, pb, pkb, phf) runs two half tiles ahead
+    // of the compute cursor (ca, cb, kb, hf).
+    ListCursor pa = ca, pb = cb;
+    int pkb = kb, phf = 0;
+    auto advance = [&](ListCursor &xa, ListCursor &xb, int &xkb, int &xhf) {
+        if (xhf == 0) {
+            xhf = 1;
+            return;
+        }
+        if (xa.cur == xkb) { ++xa.j; list_seek(xa, g.nb); }
+        if (xb.cur == xkb) { ++xb.j; list_seek(xb, g.nb); }
+        xkb = min(xa.cur, xb.cur);
+        xhf = 0;
+    };
+    TRA_ISSUE(pkb, phf, 0);
+    advance(pa, pb, pkb, phf);
+    TRA_ISSUE(pkb, phf, 1);  // every block has two halves
+    advance(pa, pb, pkb, phf);
+    // The compiler does not order LDS copies against LDS reads: wait for this
+    // wave's copies explicitly (vmcnt(0)), then the barrier publishes them.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
 
+    int hf = 0, slot = 0;
+    int kny = kTileSide, knx = kTileSide;
     while (true) {
-        // ---- S^T = K Q^T (keys 0..31 and 32..63 of the tile) ----
-        f32x16_t s[2];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
-            const int key = 32 * mt + l32;
+        const bool mine = (side ? cb.cur : ca.cur) == kb;
+        if (mine) {
+            if (hf == 0) {
+                const uint32_t row = fdiv((uint32_t)kb, div_nbx);
+                const int kbx = (int)((uint32_t)kb - row * div_nbx.d);
+                const int kby = (int)(row - fdiv(row, div_nby) * div_nby.d);
+                kny = min(kTileSide, g.H - kTileSide * kby);
+                knx = min(kTileSide, g.W - kTileSide * kbx);
+            }
+            const uint16_t *Kh = ring[slot][0];
+            const uint16_t *Vh = ring[slot][1];
+
+            // ---- S^T = K Q^T for keys 32 hf .. 32 hf + 31 ----
+            bf16x8_t ka[KS];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const int cs = (2 * ks + hl) ^ (key & KSW);
-                const bf16x8_t a = lds_load16<bf16x8_t>(k_lds + key * D + 8 * cs);
-                s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s[mt], 0, 0, 0);
+                const int cs = (2 * ks + hl) ^ (l32 & KSW);
+                ka[ks] = lds_load16<bf16x8_t>(Kh + l32 * D + 8 * cs);
             }
-        }
-        __syncthreads();  // every wave is done with k_lds; v_lds holds this tile's V
-        // (past the end of the list this restages the current tile: harmless)
-        TRA_PUT(k_lds);
-        TRA_FETCH(vt, kbn >= 0 ? kbn : kb);
-
-        // ---- missing key cells of an edge tile -> -inf ----
-        const int kby = (kb / g.nbx) % g.nby, kbx = kb % g.nbx;
-        const int kny = min(kTileSide, g.H - kTileSide * kby);
-        const int knx = min(kTileSide, g.W - kTileSide * kbx);
-        if (kny < kTileSide || knx < kTileSide) {
+            f32x16_t s;
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+            for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qreg[ks], s, 0, 0, 0);
+
+            // ---- missing key cells of an edge tile -> -inf ----
+            // Register r holds key row ky = 4 hf + r / 4 and key column kx = 4 hl + r % 4.
+            if (kny < kTileSide || knx < kTileSide) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int ky = 4 * mt + (r >> 2);
-                    const int kx = 4 * hl + (r & 3);
-                    if (ky >= kny || kx >= knx) s[mt][r] = -INFINITY;
+                    const bool bad = (4 * hf + (r >> 2) >= kny) || (4 * hl + (r & 3) >= knx);
+                    s[r] = bad ? -INFINITY : s[r];
                 }
-        }
-
-        // ---- online softmax, base 2 with the scale folded into one FMA ----
-        float mx = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
-        const bool grow = mx > m_ref + kRescaleLog2;
-        if (__any(grow)) {
-            const float m_new = grow ? mx : m_ref;
-            const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-            l_run *= alpha;
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[mt][r] *= alpha;
-            m_ref = m_new;
-        }
-        float psum = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][r], scale_log2, -m_ref));
-                s[mt][r] = p;
-                psum += p;
             }
-        l_run += psum;
 
-        // P^T as the B operand: k-step ks2 covers keys 16 ks2 .. 16 ks2 + 15,
-        // held in s[ks2 / 2] registers 8 (ks2 % 2) .. + 7.
-        f16x8_t pk[4];
+            // ---- online softmax, base 2 with the scale folded into one FMA ----
+            float mx = -INFINITY;
 #pragma unroll
-        for (int ks2 = 0; ks2 < 4; ++ks2)
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+            const bool grow = mx > m_ref + kRescaleLog2;
+            if (__any(grow)) {
+                const float m_new = grow ? mx : m_ref;
+                const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+                l_run *= alpha;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pk[ks2][e] = (_Float16)s[ks2 >> 1][8 * (ks2 & 1) + e];
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[mt][r] *= alpha;
+                m_ref = m_new;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], scale_log2, -m_ref));
 
-        // ---- O^T += V^T P^T ----
+            // P^T as the B operand: k-step ks2 covers keys 32 hf + 16 ks2 .. + 15,
+            // held in registers 8 ks2 .. 8 ks2 + 7.  The row sum l is taken over
+            // the same fp16-rounded values (fp32 dot2 accumulation), so
+            // numerator and denominator see identical probabilities.
+            f16x8_t pk[2];
+            float psum0 = 0.f, psum1 = 0.f;
+            const f16x2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int d = 32 * mt + l32;
+            for (int ks2 = 0; ks2 < 2; ++ks2) {
 #pragma unroll
-            for (int ks2 = 0; ks2 < 4; ++ks2) {
-                const int cs = (2 * ks2 + hl) ^ ((d >> 1) & 7);
-                const f16x8_t a = lds_load16<f16x8_t>(v_lds + d * 64 + 8 * cs);
-                acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pk[ks2], acc[mt], 0, 0, 0);
+                for (int e = 0; e < 8; ++e) pk[ks2][e] = (_Float16)s[8 * ks2 + e];
+#pragma unroll
+                for (int e = 0; e < 8; e += 4) {
+                    const f16x2_t a = {pk[ks2][e], pk[ks2][e + 1]};
+                    const f16x2_t b = {pk[ks2][e + 2], pk[ks2][e + 3]};
+                    psum0 = __builtin_amdgcn_fdot2(a, one2, psum0, false);
+                    psum1 = __builtin_amdgcn_fdot2(b, one2, psum1, false);
+                }
+            }
+            l_run += psum0 + psum1;
+
+            // ---- O^T += V^T P^T ----
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const int d = 32 * mt + l32;
+#pragma unroll
+                for (int ks2 = 0; ks2 < 2; ++ks2) {
+                    const int cs = (2 * ks2 + hl) ^ ((d >> 2) & 3);
+                    const f16x8_t a = lds_load16<f16x8_t>(Vh + d * 32 + 8 * cs);
+                    acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pk[ks2], acc[mt], 0, 0, 0);
+                }
             }
         }
-        if (kbn < 0) break;
-        __syncthreads();  // every wave is done with v_lds; k_lds holds the next K
-        TRA_PUT(v_lds);
-        j = jn;
-        kb = kbn;
-        jn = next_valid(j + 1);
-        kbn = jn < n ? block_at(jn) : -1;
-        TRA_FETCH(kt, kbn >= 0 ? kbn : kb);
+
+        advance(ca, cb, kb, hf);
+        if (kb == INT32_MAX) break;
+        // Every wave is done with this slot and its copy of the next half tile
+        // has landed (explicit vmcnt(0)); the barrier publishes both, then the
+        // slot is refilled.
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __syncthreads();
+        if (pkb != INT32_MAX) {
+            TRA_ISSUE(pkb, phf, slot);
+            advance(pa, pb, pkb, phf);
+        }
+        slot ^= 1;
     }
-#undef TRA_FETCH
-#undef TRA_PUT
+#undef TRA_ISSUE
 
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
@@ -257,16 +343,24 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
 hipError_t launch_attn(int D, const uint16_t *q, const uint16_t *kt, const uint16_t *vt,
                        const int32_t *idx, const int32_t *cnt, int64_t maxcnt, const Grid &g,
                        int heads, float *out, hipStream_t s) {
-    const int64_t total = (int64_t)heads * g.nb;
+    const int pairs_per_head = (g.nb + 1) / 2;
+    const int64_t total = (int64_t)heads * pairs_per_head;
     const int per_xcd = (int)((total + 7) / 8);
     const dim3 grid((unsigned)(8 * (int64_t)per_xcd)), block(kAttnThreads);
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+    auto magic = [](int d) {
+        FastDiv f;
+        f.d = (uint32_t)d;
+        f.m = (((uint64_t)1 << 39) + (uint64_t)d - 1) / (uint64_t)d;
+        return f;
+    };
+    const FastDiv div_nbx = magic(g.nbx), div_nby = magic(g.nby);
     if (D == 128)
         hipLaunchKernelGGL(attn_kernel<128>, grid, block, 0, s, q, kt, vt, idx, cnt, maxcnt, g,
-                           heads, per_xcd, out, scale_log2);
+                           heads, pairs_per_head, per_xcd, div_nbx, div_nby, out, scale_log2);
     else if (D == 64)
         hipLaunchKernelGGL(attn_kernel<64>, grid, block, 0, s, q, kt, vt, idx, cnt, maxcnt, g,
-                           heads, per_xcd, out, scale_log2);
+                           heads, pairs_per_head, per_xcd, div_nbx, div_nby, out, scale_log2);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -22,10 +22,10 @@ struct Grid {
 //       cells zero; the 16-byte chunk c of row w is stored at chunk c ^ (w & KSW)
 //       with KSW = min(D/8, 16) - 1 so that the matrix-core operand reads of 16
 //       consecutive key rows hit distinct LDS banks.
-//   vt  fp16 [heads][nb][D][64 positions] (V transposed), position p of a
-//       16-key group holds key p with bits 2 and 3 swapped, so that the 8 keys
-//       one lane feeds to the P.V product are contiguous; chunk c of row d is
-//       stored at chunk c ^ ((d >> 1) & 7).
+//   vt  fp16 [heads][nb][2 halves][D][32 positions] (V transposed, keys
+//       0..31 then 32..63), position p of a half holds key p with bits 2 and 3
+//       swapped, so that the 8 keys one lane feeds to the P.V product are
+//       contiguous; the 16-byte chunk c of row d is stored at c ^ ((d >> 2) & 3).
 size_t packed_tile_elems(int D);
 
 hipError_t launch_pack_pool(int D, bool pool, bool pack, const uint16_t *q, const uint16_t *k,

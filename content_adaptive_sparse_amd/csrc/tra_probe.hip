@@ -119,19 +119,22 @@ __global__ __launch_bounds__(256) void pack_pool_kernel(
         }
     }
     if (PACK) {
-        // V^T tile: D rows of 64 key positions, written as 8 chunks per row.
-        for (int o = tid; o < D * 8; o += 256) {
-            const int dd = o >> 3;
-            const int cs = o & 7;                 // stored chunk
-            const int cc = cs ^ ((dd >> 1) & 7);  // logical chunk held there
+        // V^T tile as two 32-key halves, each D rows of 32 key positions
+        // (64 bytes = 4 chunks per row), chunk c of row d stored at
+        // c ^ ((d >> 2) & 3).
+        for (int o = tid; o < 2 * D * 4; o += 256) {
+            const int hf = o / (D * 4);
+            const int dd = (o >> 2) % D;
+            const int cs = o & 3;                 // stored chunk
+            const int cc = cs ^ ((dd >> 2) & 3);  // logical chunk held there
             uint32_t w32[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int k0 = swap_bits23(8 * cc + 2 * e);
-                const int k1 = swap_bits23(8 * cc + 2 * e + 1);
+                const int k0 = 32 * hf + swap_bits23(8 * cc + 2 * e);
+                const int k1 = 32 * hf + swap_bits23(8 * cc + 2 * e + 1);
                 w32[e] = (uint32_t)vs[k0][dd] | ((uint32_t)vs[k1][dd] << 16);
             }
-            *reinterpret_cast<uint4 *>(vt + (tile * D + dd) * 64 + 8 * cs) =
+            *reinterpret_cast<uint4 *>(vt + tile * 64 * D + hf * 32 * D + dd * 32 + 8 * cs) =
                 make_uint4(w32[0], w32[1], w32[2], w32[3]);
         }
     }

@@ -47,6 +47,7 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
 }
 
 constexpr int kAttnThreads = 256;
+constexpr int kRingSlots = 3;
 // s_waitcnt immediates for gfx9 (vmcnt bits [3:0] and [15:14], expcnt [6:4],
 // lgkmcnt [11:8]); counters not waited on are left at their no-wait maxima.
 constexpr int wait_vmcnt(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
@@ -64,6 +65,11 @@ typedef __attribute__((address_space(1))) void global_void_t;
 // the constant address space lets wave-uniform reads use scalar loads, which
 // do not share the vector-memory counter with the in-flight LDS copies.
 typedef __attribute__((address_space(4))) const int32_t const_i32_t;
+
+template <int N>
+struct SlotTag {
+    static constexpr int value = N;
+};
 
 // A query block's key list read through scalar loads: entries outside
 // [0, nb) are skipped; `cur` is the block at the cursor or INT32_MAX once the
@@ -102,8 +108,9 @@ __global__ __launch_bounds__(kAttnThreads, 3) void attn_kernel(
     static_assert(PPW * WAVES == PIECES, "every piece copied exactly once");
     static_assert(PIECES * 512 == HALF, "pieces tile the half exactly (no copy past a slot)");
 
-    // Two-slot ring of half tiles: [slot][0 = K rows, 1 = V^T rows].
-    __shared__ __attribute__((aligned(1024))) uint16_t ring[2][2][HALF];
+    // Ring of half tiles: [slot][0 = K rows, 1 = V^T rows]; copies run up to
+    // two half tiles ahead of the one being computed.
+    __shared__ __attribute__((aligned(1024))) uint16_t ring[kRingSlots][2][HALF];
 
     // Work item: a pair of neighbouring query blocks (2p, 2p + 1) of one head.
     // Consecutive workgroup ids land on different XCDs; give every XCD a
@@ -167,18 +174,33 @@ __global__ __launch_bounds__(kAttnThreads, 3) void attn_kernel(
     const size_t head_tiles = (size_t)h * g.nb;
 #define TRA_ISSUE(blk, hf, slot)                                                              \
     do {                                                                                      \
-        const char *ks_ = reinterpret_cast<const char *>(kt + ((head_tiles + (blk)) * 64 + 32 * (hf)) * D); \
-        const char *vs_ = reinterpret_cast<const char *>(vt + (head_tiles + (blk)) * 64 * D + (hf) * HALF); \
+        const char *ks_ = reinterpret_cast<const char *>(kt + ((head_tiles + (blk)) * 64 + 32 * (hf)) * D) + wave_piece_bytes; \
+        const char *vs_ = reinterpret_cast<const char *>(vt + (head_tiles + (blk)) * 64 * D + (hf) * HALF) + wave_piece_bytes; \
         _Pragma("unroll") for (int i_ = 0; i_ < PPW; ++i_) {                                 \
-            const int piece_ = wave * PPW + i_;                                              \
-            __builtin_amdgcn_global_load_lds(                                                \
-                (const global_void_t *)(ks_ + piece_ * 1024 + lane * 16),                    \
-                (lds_void_t *)&ring[slot][0][piece_ * 512], 16, 0, 0);                       \
-            __builtin_amdgcn_global_load_lds(                                                \
-                (const global_void_t *)(vs_ + piece_ * 1024 + lane * 16),                    \
-                (lds_void_t *)&ring[slot][1][piece_ * 512], 16, 0, 0);                       \
+            __builtin_amdgcn_global_load_lds((const global_void_t *)(ks_ + lane16 + i_ * 1024), \
+                                             (lds_void_t *)&ring[slot][0][wave_piece_elems + i_ * 512], 16, 0, 0); \
+            __builtin_amdgcn_global_load_lds((const global_void_t *)(vs_ + lane16 + i_ * 1024), \
+                                             (lds_void_t *)&ring[slot][1][wave_piece_elems + i_ * 512], 16, 0, 0); \
         }                                                                                     \
     } while (0)
+    // this wave's share of every copy, and this lane's 16 bytes of a piece
+    const int wave_piece_bytes = wave * PPW * 1024;
+    const int wave_piece_elems = wave * PPW * 512;
+    const int lane16 = lane * 16;
+
+    // Per-lane LDS element offsets of the matrix-core operands inside a slot:
+    // K row l32, chunk (2 ks + hl) swizzled; V^T row d = 32 mt + l32, chunk
+    // (2 ks2 + hl) swizzled.
+    int kofs[KS], vofs[MT][2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kofs[ks] = l32 * D + 8 * ((2 * ks + hl) ^ (l32 & KSW));
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2) {
+            const int d = 32 * mt + l32;
+            vofs[mt][ks2] = d * 32 + 8 * ((2 * ks2 + hl) ^ ((d >> 2) & 3));
+        }
 
     bf16x8_t qreg[KS];
 #pragma unroll
@@ -206,18 +228,35 @@ __global__ __launch_bounds__(kAttnThreads, 3) void attn_kernel(
         xkb = min(xa.cur, xb.cur);
         xhf = 0;
     };
-    TRA_ISSUE(pkb, phf, 0);
-    advance(pa, pb, pkb, phf);
-    TRA_ISSUE(pkb, phf, 1);  // every block has two halves
-    advance(pa, pb, pkb, phf);
-    // The compiler does not order LDS copies against LDS reads: wait for this
-    // wave's copies explicitly (vmcnt(0)), then the barrier publishes them.
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    // Each copy is 2 PPW loads per wave.  `ahead` counts the half tiles copied
+    // and not yet computed (the current one included); waiting until at most
+    // (ahead - 1) copies are outstanding means the oldest has landed.  The
+    // compiler does not order LDS copies against LDS reads, so these waits are
+    // explicit, and the barrier that follows publishes the landed copy.
+    int ahead = 0;
+    for (int i = 0; i < kRingSlots && pkb != INT32_MAX; ++i) {
+        TRA_ISSUE(pkb, phf, i);
+        advance(pa, pb, pkb, phf);
+        ++ahead;
+    }
+#define TRA_WAIT_OLDEST(a)                                                                    \
+    do {                                                                                      \
+        if ((a) >= 3)                                                                         \
+            __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * 2 * PPW));                             \
+        else if ((a) == 2)                                                                    \
+            __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * PPW));                                 \
+        else                                                                                  \
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);                                          \
+    } while (0)
+    TRA_WAIT_OLDEST(ahead);
     __syncthreads();
 
-    int hf = 0, slot = 0;
+    int hf = 0;
     int kny = kTileSide, knx = kTileSide;
-    while (true) {
+    // One half tile in ring slot SLOT (a compile-time constant, so LDS slot
+    // offsets fold into instruction immediates); returns false after the last.
+    auto half_step = [&](auto slot_tag) -> bool {
+        constexpr int slot = decltype(slot_tag)::value;
         const bool mine = (side ? cb.cur : ca.cur) == kb;
         if (mine) {
             if (hf == 0) {
@@ -234,8 +273,7 @@ __global__ __launch_bounds__(kAttnThreads, 3) void attn_kernel(
             bf16x8_t ka[KS];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const int cs = (2 * ks + hl) ^ (l32 & KSW);
-                ka[ks] = lds_load16<bf16x8_t>(Kh + l32 * D + 8 * cs);
+                ka[ks] = lds_load16<bf16x8_t>(Kh + kofs[ks]);
             }
             f32x16_t s;
 #pragma unroll
@@ -298,30 +336,34 @@ __global__ __launch_bounds__(kAttnThreads, 3) void attn_kernel(
             // ---- O^T += V^T P^T ----
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const int d = 32 * mt + l32;
 #pragma unroll
                 for (int ks2 = 0; ks2 < 2; ++ks2) {
-                    const int cs = (2 * ks2 + hl) ^ ((d >> 2) & 3);
-                    const f16x8_t a = lds_load16<f16x8_t>(Vh + d * 32 + 8 * cs);
+                    const f16x8_t a = lds_load16<f16x8_t>(Vh + vofs[mt][ks2]);
                     acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pk[ks2], acc[mt], 0, 0, 0);
                 }
             }
         }
 
         advance(ca, cb, kb, hf);
-        if (kb == INT32_MAX) break;
-        // Every wave is done with this slot and its copy of the next half tile
-        // has landed (explicit vmcnt(0)); the barrier publishes both, then the
-        // slot is refilled.
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        if (kb == INT32_MAX) return false;
+        // This half tile is done: the next one becomes the oldest copy.  Once
+        // it has landed and every wave is past this slot (barrier), the slot is
+        // refilled with the next copy.
+        --ahead;
+        TRA_WAIT_OLDEST(ahead);
         __syncthreads();
         if (pkb != INT32_MAX) {
             TRA_ISSUE(pkb, phf, slot);
             advance(pa, pb, pkb, phf);
+            ++ahead;
         }
-        slot ^= 1;
+        return true;
+    };
+    static_assert(kRingSlots == 3, "the loop below visits three slots");
+    while (half_step(SlotTag<0>{}) && half_step(SlotTag<1>{}) && half_step(SlotTag<2>{})) {
     }
 #undef TRA_ISSUE
+#undef TRA_WAIT_OLDEST
 
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;

@@ -133,6 +133,9 @@ class Scratch {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? TRA_OK : TRA_ERR_HIP; }
 
+// Work items of the attention kernel: pairs of neighbouring query blocks.
+size_t order_items(const tra::Grid &g, int heads) { return (size_t)heads * ((g.nb + 1) / 2); }
+
 // ---- optional per-kernel event timing ----
 struct ProfRecord {
     int kind;
@@ -267,18 +270,24 @@ int tra_attn(const void *q, const void *k, const void *v, int T, int H, int W, i
     Scratch ws(stream);
     const size_t tiles = (size_t)heads * g.nb * tra::packed_tile_elems(head_dim) * 2;
     const size_t o_kt = ws.reserve(tiles), o_vt = ws.reserve(tiles);
+    const size_t o_order = idx ? ws.reserve(order_items(g, heads) * sizeof(int32_t)) : 0;
     if ((rc = ws.allocate()) != TRA_OK) return rc;
     uint16_t *kt = ws.at<uint16_t>(o_kt), *vt = ws.at<uint16_t>(o_vt);
+    int32_t *order = idx ? ws.at<int32_t>(o_order) : nullptr;
     hipError_t e;
     {
         ProfScope p(TRA_KERNEL_PACK_POOL, stream);
         e = tra::launch_pack_pool(head_dim, false, true, nullptr, (const uint16_t *)k,
                                   (const uint16_t *)v, g, heads, nullptr, nullptr, kt, vt, stream);
     }
+    if (e == hipSuccess && idx) {
+        ProfScope p(TRA_KERNEL_ORDER, stream);
+        e = tra::launch_order(cnt, g, heads, maxcnt, order, stream);
+    }
     if (e == hipSuccess) {
         ProfScope p(TRA_KERNEL_ATTN, stream);
         e = tra::launch_attn(head_dim, (const uint16_t *)q, kt, vt, idx, cnt, idx ? maxcnt : g.nb,
-                             g, heads, (float *)out, stream);
+                             order, g, heads, (float *)out, stream);
     }
     return hip_status(e);
 }
@@ -299,13 +308,14 @@ int tra_attention(const void *q, const void *k, const void *v, int T, int H, int
 
     Scratch ws(stream);
     const size_t o_kt = ws.reserve(tiles), o_vt = ws.reserve(tiles);
-    size_t o_qp = 0, o_kp = 0, o_r = 0, o_idx = 0, o_cnt = 0;
+    size_t o_qp = 0, o_kp = 0, o_r = 0, o_idx = 0, o_cnt = 0, o_order = 0;
     if (!dense) {
         o_qp = ws.reserve(rows * head_dim * sizeof(float));
         o_kp = ws.reserve(rows * head_dim * sizeof(float));
         o_r = ws.reserve(rows * sizeof(int32_t));
         o_cnt = ws.reserve(rows * sizeof(int32_t));
         o_idx = ws.reserve(rows * (size_t)maxcnt * sizeof(int32_t));
+        o_order = ws.reserve(order_items(g, heads) * sizeof(int32_t));
     }
     if ((rc = ws.allocate()) != TRA_OK) return rc;
     uint16_t *kt = ws.at<uint16_t>(o_kt), *vt = ws.at<uint16_t>(o_vt);
@@ -321,7 +331,8 @@ int tra_attention(const void *q, const void *k, const void *v, int T, int H, int
         }
         if (e == hipSuccess) {
             ProfScope p(TRA_KERNEL_ATTN, stream);
-            e = tra::launch_attn(head_dim, q16, kt, vt, nullptr, nullptr, g.nb, g, heads, o32, stream);
+            e = tra::launch_attn(head_dim, q16, kt, vt, nullptr, nullptr, g.nb, nullptr, g, heads,
+                                 o32, stream);
         }
         return hip_status(e);
     }
@@ -339,9 +350,14 @@ int tra_attention(const void *q, const void *k, const void *v, int T, int H, int
         ProfScope p(TRA_KERNEL_MASK, stream);
         e = tra::launch_mask(radius, g, heads, r_max, maxcnt, idx, cnt, stream);
     }
+    int32_t *order = ws.at<int32_t>(o_order);
+    if (e == hipSuccess) {
+        ProfScope p(TRA_KERNEL_ORDER, stream);
+        e = tra::launch_order(cnt, g, heads, maxcnt, order, stream);
+    }
     if (e == hipSuccess) {
         ProfScope p(TRA_KERNEL_ATTN, stream);
-        e = tra::launch_attn(head_dim, q16, kt, vt, idx, cnt, maxcnt, g, heads, o32, stream);
+        e = tra::launch_attn(head_dim, q16, kt, vt, idx, cnt, maxcnt, order, g, heads, o32, stream);
     }
     return hip_status(e);
 }

@@ -95,8 +95,9 @@ template <int D>
 __global__ __launch_bounds__(kAttnThreads, 3) void attn_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kt,
     const uint16_t *__restrict__ vt, const int32_t *__restrict__ idx,
-    const int32_t *__restrict__ cnt, int64_t maxcnt, Grid g, int heads, int pairs_per_head,
-    int per_xcd, FastDiv div_nbx, FastDiv div_nby, float *__restrict__ out, float scale_log2) {
+    const int32_t *__restrict__ cnt, int64_t maxcnt, const int32_t *__restrict__ order, Grid g,
+    int heads, int pairs_per_head, int per_xcd, FastDiv div_nbx, FastDiv div_nby,
+    float *__restrict__ out, float scale_log2) {
     constexpr int KS = D / 16;                  // k-steps of Q.K^T
     constexpr int MT = D / 32;                  // 32-row tiles of O^T
     constexpr int CH = D / 8;                   // 16-byte chunks per K row
@@ -113,10 +114,18 @@ __global__ __launch_bounds__(kAttnThreads, 3) void attn_kernel(
     __shared__ __attribute__((aligned(1024))) uint16_t ring[kRingSlots][2][HALF];
 
     // Work item: a pair of neighbouring query blocks (2p, 2p + 1) of one head.
-    // Consecutive workgroup ids land on different XCDs; give every XCD a
-    // contiguous range of items so its L2 sees neighbouring query blocks.
+    // With a work order (lists of unequal length), items are taken longest
+    // first.  Without one (dense mode: equal work), consecutive workgroup ids,
+    // which land on different XCDs, are remapped so every XCD gets a contiguous
+    // range of items and its L2 sees neighbouring query blocks.
     const int64_t total = (int64_t)heads * pairs_per_head;
-    const int64_t item = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    int64_t item;
+    if (order) {
+        if ((int64_t)blockIdx.x >= total) return;
+        item = ((const const_i32_t *)order)[blockIdx.x];
+    } else {
+        item = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    }
     if (item >= total) return;
     const int h = (int)(item / pairs_per_head);
     const int pair = (int)(item % pairs_per_head);
@@ -383,8 +392,9 @@ __global__ __launch_bounds__(kAttnThreads, 3) void attn_kernel(
 }  // namespace
 
 hipError_t launch_attn(int D, const uint16_t *q, const uint16_t *kt, const uint16_t *vt,
-                       const int32_t *idx, const int32_t *cnt, int64_t maxcnt, const Grid &g,
-                       int heads, float *out, hipStream_t s) {
+                       const int32_t *idx, const int32_t *cnt, int64_t maxcnt,
+                       const int32_t *order, const Grid &g, int heads, float *out,
+                       hipStream_t s) {
     const int pairs_per_head = (g.nb + 1) / 2;
     const int64_t total = (int64_t)heads * pairs_per_head;
     const int per_xcd = (int)((total + 7) / 8);
@@ -398,11 +408,11 @@ hipError_t launch_attn(int D, const uint16_t *q, const uint16_t *kt, const uint1
     };
     const FastDiv div_nbx = magic(g.nbx), div_nby = magic(g.nby);
     if (D == 128)
-        hipLaunchKernelGGL(attn_kernel<128>, grid, block, 0, s, q, kt, vt, idx, cnt, maxcnt, g,
-                           heads, pairs_per_head, per_xcd, div_nbx, div_nby, out, scale_log2);
+        hipLaunchKernelGGL(attn_kernel<128>, grid, block, 0, s, q, kt, vt, idx, cnt, maxcnt, order,
+                           g, heads, pairs_per_head, per_xcd, div_nbx, div_nby, out, scale_log2);
     else if (D == 64)
-        hipLaunchKernelGGL(attn_kernel<64>, grid, block, 0, s, q, kt, vt, idx, cnt, maxcnt, g,
-                           heads, pairs_per_head, per_xcd, div_nbx, div_nby, out, scale_log2);
+        hipLaunchKernelGGL(attn_kernel<64>, grid, block, 0, s, q, kt, vt, idx, cnt, maxcnt, order,
+                           g, heads, pairs_per_head, per_xcd, div_nbx, div_nby, out, scale_log2);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

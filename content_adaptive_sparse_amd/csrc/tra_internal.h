@@ -41,8 +41,15 @@ hipError_t launch_fill_dense(const Grid &g, int heads, int32_t *radius, float *h
 hipError_t launch_mask(const int32_t *radius, const Grid &g, int heads, int r_max,
                        int64_t maxcnt, int32_t *idx, int32_t *cnt, hipStream_t s);
 
+// Longest-first order of the attention work items (query-block pairs); see
+// tra_mask.hip.  order has heads * ceil(nb / 2) entries.
+hipError_t launch_order(const int32_t *cnt, const Grid &g, int heads, int64_t maxcnt,
+                        int32_t *order, hipStream_t s);
+
+// order may be null (items in XCD-contiguous raster order, the dense mode).
 hipError_t launch_attn(int D, const uint16_t *q, const uint16_t *kt, const uint16_t *vt,
-                       const int32_t *idx, const int32_t *cnt, int64_t maxcnt, const Grid &g,
-                       int heads, float *out, hipStream_t s);
+                       const int32_t *idx, const int32_t *cnt, int64_t maxcnt,
+                       const int32_t *order, const Grid &g, int heads, float *out,
+                       hipStream_t s);
 
 }  // namespace tra

@@ -62,3 +62,64 @@ hipError_t launch_mask(const int32_t *radius, const Grid &g, int heads, int r_ma
 }
 
 }  // namespace tra
+
+namespace tra {
+namespace {
+
+// Work order for the attention kernel: the (head, query-block pair) items
+// sorted by descending list length of the longer list of the pair, so that
+// the longest items start first and the grid does not end on a long tail.
+// One workgroup: histogram of lengths in LDS, a descending prefix scan, then a
+// scatter (the order among equal lengths is arbitrary; results do not depend
+// on it).
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderMaxBin = 8191;
+
+__global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *__restrict__ cnt,
+                                                              int nb, int64_t items,
+                                                              int pairs_per_head, int maxlen,
+                                                              int32_t *__restrict__ order) {
+    extern __shared__ int32_t bins[];  // maxlen + 1 bins
+    const int tid = threadIdx.x;
+    for (int i = tid; i <= maxlen; i += kOrderThreads) bins[i] = 0;
+    __syncthreads();
+    auto length_of = [&](int64_t it) -> int {
+        const int64_t h = it / pairs_per_head;
+        const int p = (int)(it % pairs_per_head);
+        const int32_t *row = cnt + h * nb;
+        int len = row[2 * p];
+        if (2 * p + 1 < nb) len = max(len, (int)row[2 * p + 1]);
+        return len < 0 ? 0 : (len > maxlen ? maxlen : len);
+    };
+    for (int64_t it = tid; it < items; it += kOrderThreads) atomicAdd(&bins[length_of(it)], 1);
+    __syncthreads();
+    if (tid == 0) {  // descending exclusive scan: longest lengths first
+        int run = 0;
+        for (int len = maxlen; len >= 0; --len) {
+            const int c = bins[len];
+            bins[len] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    for (int64_t it = tid; it < items; it += kOrderThreads) {
+        const int slot = atomicAdd(&bins[length_of(it)], 1);
+        order[slot] = (int32_t)it;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_order(const int32_t *cnt, const Grid &g, int heads, int64_t maxcnt,
+                        int32_t *order, hipStream_t s) {
+    const int pairs_per_head = (g.nb + 1) / 2;
+    const int64_t items = (int64_t)heads * pairs_per_head;
+    // lengths above kOrderMaxBin share the top bin (they still start first)
+    const int maxlen = (int)(maxcnt < kOrderMaxBin ? maxcnt : kOrderMaxBin);
+    const size_t lds = (size_t)(maxlen + 1) * sizeof(int32_t);
+    hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), lds, s, cnt, g.nb, items,
+                       pairs_per_head, maxlen, order);
+    return hipGetLastError();
+}
+
+}  // namespace tra

@@ -166,7 +166,8 @@ enum tra_kernel_kind {
     TRA_KERNEL_MASK = 2,      /* radius -> key-block lists */
     TRA_KERNEL_ATTN = 3,      /* block-sparse attention */
     TRA_KERNEL_FILL = 4,      /* dense-mode radius fill */
-    TRA_KERNEL_KINDS = 5
+    TRA_KERNEL_ORDER = 5,     /* longest-first order of the attention work items */
+    TRA_KERNEL_KINDS = 6
 };
 int tra_profile_begin(void);
 int tra_profile_end(double *ms, int *launches, int n);

@@ -134,7 +134,7 @@ class Scratch {
 int hip_status(hipError_t e) { return e == hipSuccess ? TRA_OK : TRA_ERR_HIP; }
 
 // Work items of the attention kernel: pairs of neighbouring query blocks.
-size_t order_items(const tra::Grid &g, int heads) { return (size_t)heads * ((g.nb + 1) / 2); }
+size_t order_items(const tra::Grid &g, int heads) { return (size_t)heads * tra::pairs_per_head(g); }
 
 // ---- optional per-kernel event timing ----
 struct ProfRecord {

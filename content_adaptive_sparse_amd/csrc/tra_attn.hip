@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kAttnThreads, 3) void attn_kernel(
     // two half tiles ahead of the one being computed.
     __shared__ __attribute__((aligned(1024))) uint16_t ring[kRingSlots][2][HALF];
 
-    // Work item: a pair of neighbouring query blocks (2p, 2p + 1) of one head.
+    // Work item: a pair of vertically adjacent query blocks of one head.
     // With a work order (lists of unequal length), items are taken longest
     // first.  Without one (dense mode: equal work), consecutive workgroup ids,
     // which land on different XCDs, are remapped so every XCD gets a contiguous
@@ -128,23 +128,24 @@ __global__ __launch_bounds__(kAttnThreads, 3) void attn_kernel(
     }
     if (item >= total) return;
     const int h = (int)(item / pairs_per_head);
-    const int pair = (int)(item % pairs_per_head);
+    int blk[2];
+    pair_blocks((int)(item % pairs_per_head), g, blk[0], blk[1]);
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int hl = lane >> 5, l32 = lane & 31;
-    const int side = wave >> 1;          // 0: block 2 pair, 1: block 2 pair + 1
-    const int qb = 2 * pair + side;      // this wave's query block (may be nb: absent)
+    const int side = wave >> 1;          // which block of the pair this wave computes
+    const int qb = blk[side];            // -1: absent (odd tile-row count)
 
     // Both cursors are tracked (redundantly) by every wave.
     ListCursor ca, cb;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         ListCursor &c = k ? cb : ca;
-        const int b = 2 * pair + k;
+        const int b = blk[k];
         c.j = 0;
         c.list = nullptr;
-        if (b >= g.nb) {
+        if (b < 0) {
             c.n = 0;
         } else if (idx) {
             const int64_t row = (int64_t)h * g.nb + b;
@@ -160,11 +161,11 @@ __global__ __launch_bounds__(kAttnThreads, 3) void attn_kernel(
     // This lane's query token (clamped into the grid for the missing cells of
     // an edge tile, and for an absent block; such rows are never stored).
     const int plane = g.nby * g.nbx;
-    const int qbc = qb < g.nb ? qb : g.nb - 1;
+    const int qbc = qb >= 0 ? qb : blk[0];
     const int t = qbc / plane, by = (qbc / g.nbx) % g.nby, bx = qbc % g.nbx;
     const int qi = 32 * (wave & 1) + l32;
     const int qy = kTileSide * by + (qi >> 3), qx = kTileSide * bx + (qi & 7);
-    const bool qreal = qb < g.nb && qy < g.H && qx < g.W;
+    const bool qreal = qb >= 0 && qy < g.H && qx < g.W;
     const size_t qtok = (size_t)h * g.T * g.H * g.W +
                         ((size_t)t * g.H + min(qy, g.H - 1)) * g.W + min(qx, g.W - 1);
     float *o = out + qtok * D;
@@ -395,8 +396,8 @@ hipError_t launch_attn(int D, const uint16_t *q, const uint16_t *kt, const uint1
                        const int32_t *idx, const int32_t *cnt, int64_t maxcnt,
                        const int32_t *order, const Grid &g, int heads, float *out,
                        hipStream_t s) {
-    const int pairs_per_head = (g.nb + 1) / 2;
-    const int64_t total = (int64_t)heads * pairs_per_head;
+    const int pph = pairs_per_head(g);
+    const int64_t total = (int64_t)heads * pph;
     const int per_xcd = (int)((total + 7) / 8);
     const dim3 grid((unsigned)(8 * (int64_t)per_xcd)), block(kAttnThreads);
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
@@ -409,10 +410,10 @@ hipError_t launch_attn(int D, const uint16_t *q, const uint16_t *kt, const uint1
     const FastDiv div_nbx = magic(g.nbx), div_nby = magic(g.nby);
     if (D == 128)
         hipLaunchKernelGGL(attn_kernel<128>, grid, block, 0, s, q, kt, vt, idx, cnt, maxcnt, order,
-                           g, heads, pairs_per_head, per_xcd, div_nbx, div_nby, out, scale_log2);
+                           g, heads, pph, per_xcd, div_nbx, div_nby, out, scale_log2);
     else if (D == 64)
         hipLaunchKernelGGL(attn_kernel<64>, grid, block, 0, s, q, kt, vt, idx, cnt, maxcnt, order,
-                           g, heads, pairs_per_head, per_xcd, div_nbx, div_nby, out, scale_log2);
+                           g, heads, pph, per_xcd, div_nbx, div_nby, out, scale_log2);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

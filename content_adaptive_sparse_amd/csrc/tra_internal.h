@@ -41,8 +41,25 @@ hipError_t launch_fill_dense(const Grid &g, int heads, int32_t *radius, float *h
 hipError_t launch_mask(const int32_t *radius, const Grid &g, int heads, int r_max,
                        int64_t maxcnt, int32_t *idx, int32_t *cnt, hipStream_t s);
 
+// Attention work items are pairs of vertically adjacent query blocks: item p
+// of a head is frame t, tile-row pair pr, tile column bx, holding blocks
+// (t, 2 pr, bx) and (t, 2 pr + 1, bx) (the second is absent when nby is odd and
+// 2 pr + 1 == nby).  Tile rows are the shortest axis of a video latent, so
+// radii clip there first and the two blocks' key lists mostly coincide.
+__host__ __device__ inline int pairs_per_head(const Grid &g) {
+    return g.T * ((g.nby + 1) / 2) * g.nbx;
+}
+__host__ __device__ inline void pair_blocks(int p, const Grid &g, int &qa, int &qb) {
+    const int npy = (g.nby + 1) / 2;
+    const int t = p / (npy * g.nbx);
+    const int pr = (p / g.nbx) % npy;
+    const int bx = p % g.nbx;
+    qa = (t * g.nby + 2 * pr) * g.nbx + bx;
+    qb = 2 * pr + 1 < g.nby ? qa + g.nbx : -1;
+}
+
 // Longest-first order of the attention work items (query-block pairs); see
-// tra_mask.hip.  order has heads * ceil(nb / 2) entries.
+// tra_mask.hip.  order has heads * pairs_per_head(g) entries.
 hipError_t launch_order(const int32_t *cnt, const Grid &g, int heads, int64_t maxcnt,
                         int32_t *order, hipStream_t s);
 

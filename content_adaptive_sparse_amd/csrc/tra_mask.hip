@@ -76,7 +76,7 @@ constexpr int kOrderThreads = 1024;
 constexpr int kOrderMaxBin = 8191;
 
 __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *__restrict__ cnt,
-                                                              int nb, int64_t items,
+                                                              Grid g, int64_t items,
                                                               int pairs_per_head, int maxlen,
                                                               int32_t *__restrict__ order) {
     extern __shared__ int32_t bins[];  // maxlen + 1 bins
@@ -85,10 +85,11 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *__r
     __syncthreads();
     auto length_of = [&](int64_t it) -> int {
         const int64_t h = it / pairs_per_head;
-        const int p = (int)(it % pairs_per_head);
-        const int32_t *row = cnt + h * nb;
-        int len = row[2 * p];
-        if (2 * p + 1 < nb) len = max(len, (int)row[2 * p + 1]);
+        int qa, qb;
+        pair_blocks((int)(it % pairs_per_head), g, qa, qb);
+        const int32_t *row = cnt + h * g.nb;
+        int len = row[qa];
+        if (qb >= 0) len = max(len, (int)row[qb]);
         return len < 0 ? 0 : (len > maxlen ? maxlen : len);
     };
     for (int64_t it = tid; it < items; it += kOrderThreads) atomicAdd(&bins[length_of(it)], 1);
@@ -112,13 +113,13 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *__r
 
 hipError_t launch_order(const int32_t *cnt, const Grid &g, int heads, int64_t maxcnt,
                         int32_t *order, hipStream_t s) {
-    const int pairs_per_head = (g.nb + 1) / 2;
-    const int64_t items = (int64_t)heads * pairs_per_head;
+    const int pph = pairs_per_head(g);
+    const int64_t items = (int64_t)heads * pph;
     // lengths above kOrderMaxBin share the top bin (they still start first)
     const int maxlen = (int)(maxcnt < kOrderMaxBin ? maxcnt : kOrderMaxBin);
     const size_t lds = (size_t)(maxlen + 1) * sizeof(int32_t);
-    hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), lds, s, cnt, g.nb, items,
-                       pairs_per_head, maxlen, order);
+    hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), lds, s, cnt, g, items, pph,
+                       maxlen, order);
     return hipGetLastError();
 }
 

@@ -46,6 +46,18 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
     return (uint32_t)(((uint64_t)n * f.m) >> 39);
 }
 
+// Lanes l and l + 32 hold the same query: combine a value with the other
+// half's copy in registers (v_permlane32_swap: with the value in both
+// operands, the results are the lower-half and the upper-half copies).
+__device__ __forceinline__ float half_swap_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 constexpr int kAttnThreads = 256;
 constexpr int kRingSlots = 3;
 // s_waitcnt immediates for gfx9 (vmcnt bits [3:0] and [15:14], expcnt [6:4],
@@ -306,7 +318,7 @@ __global__ __launch_bounds__(kAttnThreads, 3) void attn_kernel(
             float mx = -INFINITY;
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+            mx = half_swap_max(mx) * scale_log2;
             const bool grow = mx > m_ref + kRescaleLog2;
             if (__any(grow)) {
                 const float m_new = grow ? mx : m_ref;
@@ -375,7 +387,7 @@ __global__ __launch_bounds__(kAttnThreads, 3) void attn_kernel(
 #undef TRA_ISSUE
 #undef TRA_WAIT_OLDEST
 
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = half_swap_sum(l_run);
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     if (qreal) {
 #pragma unroll

@@ -7,11 +7,12 @@
 // kept blocks come from the radius mask and run on a block-sparse backend,
 // which this kernel is.
 //
-// One wave64 workgroup per (head, query block), holding all 64 queries as two
-// 32-query tiles.  Each kept key block is processed as two 32-key halves: the
-// packed K rows (bf16) and V^T rows (fp16) of a half are copied straight from
-// global memory into a two-slot LDS ring (the next half lands while the
-// current one is computed), and the wave computes
+// One workgroup of four wave64 computes two vertically adjacent query blocks
+// of one head (two waves per block, 32 queries per wave) over the union of the
+// two blocks' key lists.  Every kept key block's packed K rows (bf16) and V^T
+// rows (fp16) are copied straight from global memory into a two-slot LDS ring
+// (the next block lands while the current one is computed), and each wave
+// whose block keeps it computes, per 32-key half:
 //   S^T = K Q^T        v_mfma_f32_32x32x16_bf16, fp32 accumulation
 //   online softmax     per query = per lane column, exp2 with the scale folded
 //   O^T += V^T P^T     v_mfma_f32_32x32x16_f16 (P rounded to fp16)
@@ -59,7 +60,7 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 }
 
 constexpr int kAttnThreads = 256;
-constexpr int kRingSlots = 3;
+constexpr int kRingSlots = 2;
 // s_waitcnt immediates for gfx9 (vmcnt bits [3:0] and [15:14], expcnt [6:4],
 // lgkmcnt [11:8]); counters not waited on are left at their no-wait maxima.
 constexpr int wait_vmcnt(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
@@ -104,7 +105,7 @@ __device__ __forceinline__ void list_seek(ListCursor &c, int nb) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kAttnThreads, 3) void attn_kernel(
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kt,
     const uint16_t *__restrict__ vt, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ cnt, int64_t maxcnt, const int32_t *__restrict__ order, Grid g,
@@ -121,9 +122,9 @@ __global__ __launch_bounds__(kAttnThreads, 3) void attn_kernel(
     static_assert(PPW * WAVES == PIECES, "every piece copied exactly once");
     static_assert(PIECES * 512 == HALF, "pieces tile the half exactly (no copy past a slot)");
 
-    // Ring of half tiles: [slot][0 = K rows, 1 = V^T rows]; copies run up to
-    // two half tiles ahead of the one being computed.
-    __shared__ __attribute__((aligned(1024))) uint16_t ring[kRingSlots][2][HALF];
+    // Ring of whole packed tiles: [slot][0 = K rows, 1 = V^T rows]; the copy of
+    // the next block runs while the current one is computed.
+    __shared__ __attribute__((aligned(1024))) uint16_t ring[kRingSlots][2][2 * HALF];
 
     // Work item: a pair of vertically adjacent query blocks of one head.
     // With a work order (lists of unequal length), items are taken longest
@@ -190,15 +191,15 @@ __global__ __launch_bounds__(kAttnThreads, 3) void attn_kernel(
         return;
     }
 
-    // Direct global -> LDS copy of half tile `hf` of block `blk` into ring slot
-    // `slot`: each wave moves PPW 1 KB pieces of K and of V^T; lane l lands 16
+    // Direct global -> LDS copy of block `blk`'s packed tiles into ring slot
+    // `slot`: each wave moves 2 PPW 1 KB pieces of K and of V^T; lane l lands 16
     // bytes at piece base + 16 l.
     const size_t head_tiles = (size_t)h * g.nb;
-#define TRA_ISSUE(blk, hf, slot)                                                              \
+#define TRA_ISSUE(blk, slot)                                                                  \
     do {                                                                                      \
-        const char *ks_ = reinterpret_cast<const char *>(kt + ((head_tiles + (blk)) * 64 + 32 * (hf)) * D) + wave_piece_bytes; \
-        const char *vs_ = reinterpret_cast<const char *>(vt + (head_tiles + (blk)) * 64 * D + (hf) * HALF) + wave_piece_bytes; \
-        _Pragma("unroll") for (int i_ = 0; i_ < PPW; ++i_) {                                 \
+        const char *ks_ = reinterpret_cast<const char *>(kt + (head_tiles + (blk)) * 64 * D) + wave_piece_bytes; \
+        const char *vs_ = reinterpret_cast<const char *>(vt + (head_tiles + (blk)) * 64 * D) + wave_piece_bytes; \
+        _Pragma("unroll") for (int i_ = 0; i_ < 2 * PPW; ++i_) {                             \
             __builtin_amdgcn_global_load_lds((const global_void_t *)(ks_ + lane16 + i_ * 1024), \
                                              (lds_void_t *)&ring[slot][0][wave_piece_elems + i_ * 512], 16, 0, 0); \
             __builtin_amdgcn_global_load_lds((const global_void_t *)(vs_ + lane16 + i_ * 1024), \
@@ -206,8 +207,8 @@ __global__ __launch_bounds__(kAttnThreads, 3) void attn_kernel(
         }                                                                                     \
     } while (0)
     // this wave's share of every copy, and this lane's 16 bytes of a piece
-    const int wave_piece_bytes = wave * PPW * 1024;
-    const int wave_piece_elems = wave * PPW * 512;
+    const int wave_piece_bytes = wave * 2 * PPW * 1024;
+    const int wave_piece_elems = wave * 2 * PPW * 512;
     const int lane16 = lane * 16;
 
     // Per-lane LDS element offsets of the matrix-core operands inside a slot:
@@ -236,88 +237,64 @@ __global__ __launch_bounds__(kAttnThreads, 3) void attn_kernel(
         for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
     float m_ref = -1e30f, l_run = 0.f;
 
-    // Union walk: the copy cursor (pa, pb, pkb, phf) runs two half tiles ahead
-    // of the compute cursor (ca, cb, kb, hf).
+    // Union walk over whole blocks: the copy cursor (pa, pb, pkb) runs one
+    // block ahead of the compute cursor (ca, cb, kb).
     ListCursor pa = ca, pb = cb;
-    int pkb = kb, phf = 0;
-    auto advance = [&](ListCursor &xa, ListCursor &xb, int &xkb, int &xhf) {
-        if (xhf == 0) {
-            xhf = 1;
-            return;
-        }
+    int pkb = kb;
+    auto advance = [&](ListCursor &xa, ListCursor &xb, int &xkb) {
         if (xa.cur == xkb) { ++xa.j; list_seek(xa, g.nb); }
         if (xb.cur == xkb) { ++xb.j; list_seek(xb, g.nb); }
         xkb = min(xa.cur, xb.cur);
-        xhf = 0;
     };
-    // Each copy is 2 PPW loads per wave.  `ahead` counts the half tiles copied
-    // and not yet computed (the current one included); waiting until at most
-    // (ahead - 1) copies are outstanding means the oldest has landed.  The
-    // compiler does not order LDS copies against LDS reads, so these waits are
-    // explicit, and the barrier that follows publishes the landed copy.
-    int ahead = 0;
-    for (int i = 0; i < kRingSlots && pkb != INT32_MAX; ++i) {
-        TRA_ISSUE(pkb, phf, i);
-        advance(pa, pb, pkb, phf);
-        ++ahead;
+    TRA_ISSUE(pkb, 0);
+    advance(pa, pb, pkb);
+    const bool two = pkb != INT32_MAX;
+    if (two) {
+        TRA_ISSUE(pkb, 1);
+        advance(pa, pb, pkb);
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(4 * PPW));  // block 0 landed
+    } else {
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     }
-#define TRA_WAIT_OLDEST(a)                                                                    \
-    do {                                                                                      \
-        if ((a) >= 3)                                                                         \
-            __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * 2 * PPW));                             \
-        else if ((a) == 2)                                                                    \
-            __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * PPW));                                 \
-        else                                                                                  \
-            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);                                          \
-    } while (0)
-    TRA_WAIT_OLDEST(ahead);
     __syncthreads();
 
-    int hf = 0;
-    int kny = kTileSide, knx = kTileSide;
-    // One half tile in ring slot SLOT (a compile-time constant, so LDS slot
-    // offsets fold into instruction immediates); returns false after the last.
-    auto half_step = [&](auto slot_tag) -> bool {
+    auto block_step = [&](auto slot_tag) -> bool {
         constexpr int slot = decltype(slot_tag)::value;
         const bool mine = (side ? cb.cur : ca.cur) == kb;
         if (mine) {
-            if (hf == 0) {
-                const uint32_t row = fdiv((uint32_t)kb, div_nbx);
-                const int kbx = (int)((uint32_t)kb - row * div_nbx.d);
-                const int kby = (int)(row - fdiv(row, div_nby) * div_nby.d);
-                kny = min(kTileSide, g.H - kTileSide * kby);
-                knx = min(kTileSide, g.W - kTileSide * kbx);
+            const uint32_t row = fdiv((uint32_t)kb, div_nbx);
+            const int kbx = (int)((uint32_t)kb - row * div_nbx.d);
+            const int kby = (int)(row - fdiv(row, div_nby) * div_nby.d);
+            const int kny = min(kTileSide, g.H - kTileSide * kby);
+            const int knx = min(kTileSide, g.W - kTileSide * kbx);
+            const uint16_t *Kt = ring[slot][0];
+            const uint16_t *Vt = ring[slot][1];
+            f32x16_t s[2];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                bf16x8_t ka[KS];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) ka[ks] = lds_load16<bf16x8_t>(Kt + hf * 32 * D + kofs[ks]);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[hf][r] = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    s[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qreg[ks], s[hf], 0, 0, 0);
             }
-            const uint16_t *Kh = ring[slot][0];
-            const uint16_t *Vh = ring[slot][1];
-
-            // ---- S^T = K Q^T for keys 32 hf .. 32 hf + 31 ----
-            bf16x8_t ka[KS];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                ka[ks] = lds_load16<bf16x8_t>(Kh + kofs[ks]);
-            }
-            f32x16_t s;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[r] = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qreg[ks], s, 0, 0, 0);
-
-            // ---- missing key cells of an edge tile -> -inf ----
-            // Register r holds key row ky = 4 hf + r / 4 and key column kx = 4 hl + r % 4.
             if (kny < kTileSide || knx < kTileSide) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const bool bad = (4 * hf + (r >> 2) >= kny) || (4 * hl + (r & 3) >= knx);
-                    s[r] = bad ? -INFINITY : s[r];
-                }
+                for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const bool bad = (4 * hf + (r >> 2) >= kny) || (4 * hl + (r & 3) >= knx);
+                        s[hf][r] = bad ? -INFINITY : s[hf][r];
+                    }
             }
-
-            // ---- online softmax, base 2 with the scale folded into one FMA ----
             float mx = -INFINITY;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[hf][r]);
             mx = half_swap_max(mx) * scale_log2;
             const bool grow = mx > m_ref + kRescaleLog2;
             if (__any(grow)) {
@@ -330,62 +307,52 @@ __global__ __launch_bounds__(kAttnThreads, 3) void attn_kernel(
                     for (int r = 0; r < 16; ++r) acc[mt][r] *= alpha;
                 m_ref = m_new;
             }
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], scale_log2, -m_ref));
-
-            // P^T as the B operand: k-step ks2 covers keys 32 hf + 16 ks2 .. + 15,
-            // held in registers 8 ks2 .. 8 ks2 + 7.  The row sum l is taken over
-            // the same fp16-rounded values (fp32 dot2 accumulation), so
-            // numerator and denominator see identical probabilities.
-            f16x8_t pk[2];
+            f16x8_t pk[2][2];
             float psum0 = 0.f, psum1 = 0.f;
             const f16x2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-            for (int ks2 = 0; ks2 < 2; ++ks2) {
+            for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) pk[ks2][e] = (_Float16)s[8 * ks2 + e];
+                for (int r = 0; r < 16; ++r)
+                    s[hf][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[hf][r], scale_log2, -m_ref));
 #pragma unroll
-                for (int e = 0; e < 8; e += 4) {
-                    const f16x2_t a = {pk[ks2][e], pk[ks2][e + 1]};
-                    const f16x2_t b = {pk[ks2][e + 2], pk[ks2][e + 3]};
-                    psum0 = __builtin_amdgcn_fdot2(a, one2, psum0, false);
-                    psum1 = __builtin_amdgcn_fdot2(b, one2, psum1, false);
+                for (int ks2 = 0; ks2 < 2; ++ks2) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) pk[hf][ks2][e] = (_Float16)s[hf][8 * ks2 + e];
+#pragma unroll
+                    for (int e = 0; e < 8; e += 4) {
+                        const f16x2_t a = {pk[hf][ks2][e], pk[hf][ks2][e + 1]};
+                        const f16x2_t b = {pk[hf][ks2][e + 2], pk[hf][ks2][e + 3]};
+                        psum0 = __builtin_amdgcn_fdot2(a, one2, psum0, false);
+                        psum1 = __builtin_amdgcn_fdot2(b, one2, psum1, false);
+                    }
                 }
             }
             l_run += psum0 + psum1;
-
-            // ---- O^T += V^T P^T ----
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
+            for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-                for (int ks2 = 0; ks2 < 2; ++ks2) {
-                    const f16x8_t a = lds_load16<f16x8_t>(Vh + vofs[mt][ks2]);
-                    acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pk[ks2], acc[mt], 0, 0, 0);
-                }
-            }
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int ks2 = 0; ks2 < 2; ++ks2) {
+                        const f16x8_t a = lds_load16<f16x8_t>(Vt + hf * HALF + vofs[mt][ks2]);
+                        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pk[hf][ks2], acc[mt], 0, 0, 0);
+                    }
         }
-
-        advance(ca, cb, kb, hf);
+        advance(ca, cb, kb);
         if (kb == INT32_MAX) return false;
-        // This half tile is done: the next one becomes the oldest copy.  Once
-        // it has landed and every wave is past this slot (barrier), the slot is
-        // refilled with the next copy.
-        --ahead;
-        TRA_WAIT_OLDEST(ahead);
+        // the next block is the only copy in flight: wait for it, then refill this slot
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
         if (pkb != INT32_MAX) {
-            TRA_ISSUE(pkb, phf, slot);
-            advance(pa, pb, pkb, phf);
-            ++ahead;
+            TRA_ISSUE(pkb, slot);
+            advance(pa, pb, pkb);
         }
         return true;
     };
-    static_assert(kRingSlots == 3, "the loop below visits three slots");
-    while (half_step(SlotTag<0>{}) && half_step(SlotTag<1>{}) && half_step(SlotTag<2>{})) {
+    while (block_step(SlotTag<0>{}) && block_step(SlotTag<1>{})) {
     }
 #undef TRA_ISSUE
-#undef TRA_WAIT_OLDEST
 
     const float l_tot = half_swap_sum(l_run);
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;

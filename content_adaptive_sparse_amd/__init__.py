@@ -22,7 +22,7 @@ __all__ = [
 ]
 
 TRA_RADIUS_INF = 2147483647
-KERNEL_KINDS = ("pack_pool", "entropy", "mask", "attn", "fill", "order")
+KERNEL_KINDS = ("pack_pool", "entropy", "mask", "attn", "fill", "order", "union")
 
 _lib = None
 

@@ -134,7 +134,7 @@ class Scratch {
 int hip_status(hipError_t e) { return e == hipSuccess ? TRA_OK : TRA_ERR_HIP; }
 
 // Work items of the attention kernel: pairs of neighbouring query blocks.
-size_t order_items(const tra::Grid &g, int heads) { return (size_t)heads * tra::pairs_per_head(g); }
+size_t order_items(const tra::Grid &g, int heads) { return (size_t)tra::order_slots(g, heads); }
 
 // ---- optional per-kernel event timing ----
 struct ProfRecord {
@@ -256,6 +256,23 @@ int tra_mask(const int32_t *radius, int T, int H, int W, int heads, int block, i
     return hip_status(tra::launch_mask(radius, g, heads, r_max, maxcnt_of(g, r_max), idx, cnt, stream));
 }
 
+// The attention walk of the lists: union of each pair's two lists, then the
+// longest-first order of the pairs.
+static hipError_t plan_walk(const int32_t *idx, const int32_t *cnt, int64_t maxcnt,
+                            const tra::Grid &g, int heads, int32_t *ulist, int32_t *ulen,
+                            int32_t *order, hipStream_t stream) {
+    hipError_t e;
+    {
+        ProfScope p(TRA_KERNEL_UNION, stream);
+        e = tra::launch_union(idx, cnt, maxcnt, g, heads, ulist, ulen, stream);
+    }
+    if (e == hipSuccess) {
+        ProfScope p(TRA_KERNEL_ORDER, stream);
+        e = tra::launch_order(ulen, g, heads, maxcnt, order, stream);
+    }
+    return e;
+}
+
 int tra_attn(const void *q, const void *k, const void *v, int T, int H, int W, int heads,
              int head_dim, int block, const int32_t *idx, const int32_t *cnt, int64_t maxcnt,
              void *out, hipStream_t stream) {
@@ -270,24 +287,30 @@ int tra_attn(const void *q, const void *k, const void *v, int T, int H, int W, i
     Scratch ws(stream);
     const size_t tiles = (size_t)heads * g.nb * tra::packed_tile_elems(head_dim) * 2;
     const size_t o_kt = ws.reserve(tiles), o_vt = ws.reserve(tiles);
-    const size_t o_order = idx ? ws.reserve(order_items(g, heads) * sizeof(int32_t)) : 0;
+    const size_t items = order_items(g, heads);
+    const int64_t ustride = idx ? tra::union_stride(maxcnt) : 0;
+    size_t o_order = 0, o_ulen = 0, o_ulist = 0;
+    if (idx) {
+        o_order = ws.reserve(items * sizeof(int32_t));
+        o_ulen = ws.reserve(items * sizeof(int32_t));
+        o_ulist = ws.reserve(items * (size_t)ustride * sizeof(int32_t));
+    }
     if ((rc = ws.allocate()) != TRA_OK) return rc;
     uint16_t *kt = ws.at<uint16_t>(o_kt), *vt = ws.at<uint16_t>(o_vt);
     int32_t *order = idx ? ws.at<int32_t>(o_order) : nullptr;
+    int32_t *ulen = idx ? ws.at<int32_t>(o_ulen) : nullptr;
+    int32_t *ulist = idx ? ws.at<int32_t>(o_ulist) : nullptr;
     hipError_t e;
     {
         ProfScope p(TRA_KERNEL_PACK_POOL, stream);
         e = tra::launch_pack_pool(head_dim, false, true, nullptr, (const uint16_t *)k,
                                   (const uint16_t *)v, g, heads, nullptr, nullptr, kt, vt, stream);
     }
-    if (e == hipSuccess && idx) {
-        ProfScope p(TRA_KERNEL_ORDER, stream);
-        e = tra::launch_order(cnt, g, heads, maxcnt, order, stream);
-    }
+    if (e == hipSuccess && idx) e = plan_walk(idx, cnt, maxcnt, g, heads, ulist, ulen, order, stream);
     if (e == hipSuccess) {
         ProfScope p(TRA_KERNEL_ATTN, stream);
-        e = tra::launch_attn(head_dim, (const uint16_t *)q, kt, vt, idx, cnt, idx ? maxcnt : g.nb,
-                             order, g, heads, (float *)out, stream);
+        e = tra::launch_attn(head_dim, (const uint16_t *)q, kt, vt, ulist, ulen, ustride, order, g,
+                             heads, (float *)out, stream);
     }
     return hip_status(e);
 }
@@ -308,7 +331,7 @@ int tra_attention(const void *q, const void *k, const void *v, int T, int H, int
 
     Scratch ws(stream);
     const size_t o_kt = ws.reserve(tiles), o_vt = ws.reserve(tiles);
-    size_t o_qp = 0, o_kp = 0, o_r = 0, o_idx = 0, o_cnt = 0, o_order = 0;
+    size_t o_qp = 0, o_kp = 0, o_r = 0, o_idx = 0, o_cnt = 0, o_order = 0, o_ulen = 0, o_ulist = 0;
     if (!dense) {
         o_qp = ws.reserve(rows * head_dim * sizeof(float));
         o_kp = ws.reserve(rows * head_dim * sizeof(float));
@@ -316,6 +339,8 @@ int tra_attention(const void *q, const void *k, const void *v, int T, int H, int
         o_cnt = ws.reserve(rows * sizeof(int32_t));
         o_idx = ws.reserve(rows * (size_t)maxcnt * sizeof(int32_t));
         o_order = ws.reserve(order_items(g, heads) * sizeof(int32_t));
+        o_ulen = ws.reserve(order_items(g, heads) * sizeof(int32_t));
+        o_ulist = ws.reserve(order_items(g, heads) * (size_t)tra::union_stride(maxcnt) * sizeof(int32_t));
     }
     if ((rc = ws.allocate()) != TRA_OK) return rc;
     uint16_t *kt = ws.at<uint16_t>(o_kt), *vt = ws.at<uint16_t>(o_vt);
@@ -331,8 +356,8 @@ int tra_attention(const void *q, const void *k, const void *v, int T, int H, int
         }
         if (e == hipSuccess) {
             ProfScope p(TRA_KERNEL_ATTN, stream);
-            e = tra::launch_attn(head_dim, q16, kt, vt, nullptr, nullptr, g.nb, nullptr, g, heads,
-                                 o32, stream);
+            e = tra::launch_attn(head_dim, q16, kt, vt, nullptr, nullptr, 0, nullptr, g, heads, o32,
+                                 stream);
         }
         return hip_status(e);
     }
@@ -350,14 +375,13 @@ int tra_attention(const void *q, const void *k, const void *v, int T, int H, int
         ProfScope p(TRA_KERNEL_MASK, stream);
         e = tra::launch_mask(radius, g, heads, r_max, maxcnt, idx, cnt, stream);
     }
-    int32_t *order = ws.at<int32_t>(o_order);
-    if (e == hipSuccess) {
-        ProfScope p(TRA_KERNEL_ORDER, stream);
-        e = tra::launch_order(cnt, g, heads, maxcnt, order, stream);
-    }
+    int32_t *order = ws.at<int32_t>(o_order), *ulen = ws.at<int32_t>(o_ulen);
+    int32_t *ulist = ws.at<int32_t>(o_ulist);
+    if (e == hipSuccess) e = plan_walk(idx, cnt, maxcnt, g, heads, ulist, ulen, order, stream);
     if (e == hipSuccess) {
         ProfScope p(TRA_KERNEL_ATTN, stream);
-        e = tra::launch_attn(head_dim, q16, kt, vt, idx, cnt, maxcnt, order, g, heads, o32, stream);
+        e = tra::launch_attn(head_dim, q16, kt, vt, ulist, ulen, tra::union_stride(maxcnt), order,
+                             g, heads, o32, stream);
     }
     return hip_status(e);
 }

@@ -60,12 +60,10 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 }
 
 constexpr int kAttnThreads = 256;
-constexpr int kRingSlots = 2;
 // s_waitcnt immediates for gfx9 (vmcnt bits [3:0] and [15:14], expcnt [6:4],
 // lgkmcnt [11:8]); counters not waited on are left at their no-wait maxima.
 constexpr int wait_vmcnt(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
 constexpr int kWaitVmcnt0 = wait_vmcnt(0);
-constexpr int kWaitLgkmcnt0 = 0xC07F;
 // The running max is only moved (and O, l rescaled) when a tile's max exceeds
 // it by more than this many powers of two; in between, probabilities are
 // taken against the stale max (at most 2^8, exact in fp16) and the final
@@ -74,9 +72,8 @@ constexpr float kRescaleLog2 = 8.0f;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void global_void_t;
-// The key lists are never written while the kernel runs; reading them through
-// the constant address space lets wave-uniform reads use scalar loads, which
-// do not share the vector-memory counter with the in-flight LDS copies.
+// The work order and union lengths are never written while the kernel runs;
+// reading them through the constant address space gives scalar loads.
 typedef __attribute__((address_space(4))) const int32_t const_i32_t;
 
 template <int N>
@@ -84,58 +81,38 @@ struct SlotTag {
     static constexpr int value = N;
 };
 
-// A query block's key list read through scalar loads: entries outside
-// [0, nb) are skipped; `cur` is the block at the cursor or INT32_MAX once the
-// list is exhausted (so the smaller of two cursors is the next union entry).
-struct ListCursor {
-    const const_i32_t *list;  // nullptr: every block 0 .. nb-1 (dense)
-    int n, j, cur;
-};
-
-__device__ __forceinline__ void list_seek(ListCursor &c, int nb) {
-    while (c.j < c.n) {
-        const int b = c.list ? c.list[c.j] : c.j;
-        if ((unsigned)b < (unsigned)nb) {
-            c.cur = b;
-            return;
-        }
-        ++c.j;
-    }
-    c.cur = INT32_MAX;
-}
-
 template <int D>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kt,
-    const uint16_t *__restrict__ vt, const int32_t *__restrict__ idx,
-    const int32_t *__restrict__ cnt, int64_t maxcnt, const int32_t *__restrict__ order, Grid g,
+    const uint16_t *__restrict__ vt, const int32_t *__restrict__ ulist,
+    const int32_t *__restrict__ ulen, int64_t ustride, const int32_t *__restrict__ order, Grid g,
     int heads, int pairs_per_head, int per_xcd, FastDiv div_nbx, FastDiv div_nby,
     float *__restrict__ out, float scale_log2) {
     constexpr int KS = D / 16;                  // k-steps of Q.K^T
     constexpr int MT = D / 32;                  // 32-row tiles of O^T
-    constexpr int CH = D / 8;                   // 16-byte chunks per K row
-    constexpr int KSW = (CH < 16 ? CH : 16) - 1;
-    constexpr int HALF = 32 * D;                // elements of a 32-key K or V^T half tile
-    constexpr int PIECES = HALF * 2 / 1024;     // 1 KB copies per half tile and operand
+    constexpr int TILE = 64 * D;                // elements of a packed K or V^T tile
+    constexpr int PIECES = TILE * 2 / 1024;     // 1 KB copies per tile
     constexpr int WAVES = kAttnThreads / 64;
-    constexpr int PPW = PIECES / WAVES;         // pieces per wave and operand
+    constexpr int PPW = PIECES / WAVES;         // pieces per wave and tile
     static_assert(PPW * WAVES == PIECES, "every piece copied exactly once");
-    static_assert(PIECES * 512 == HALF, "pieces tile the half exactly (no copy past a slot)");
+    static_assert(PIECES * 512 == TILE, "pieces tile a tile exactly (no copy past a slot)");
 
-    // Ring of whole packed tiles: [slot][0 = K rows, 1 = V^T rows]; the copy of
-    // the next block runs while the current one is computed.
-    __shared__ __attribute__((aligned(1024))) uint16_t ring[kRingSlots][2][2 * HALF];
+    // Two-slot rings of packed K tiles (bf16) and V^T tiles (fp16).  Step u
+    // reads K of union entry u and V^T of entry u - 1, while K of entry u + 1
+    // and V^T of entry u land in the other slots.
+    __shared__ __attribute__((aligned(1024))) uint16_t kring[2][TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t vring[2][TILE];
 
     // Work item: a pair of vertically adjacent query blocks of one head.
-    // With a work order (lists of unequal length), items are taken longest
-    // first.  Without one (dense mode: equal work), consecutive workgroup ids,
-    // which land on different XCDs, are remapped so every XCD gets a contiguous
-    // range of items and its L2 sees neighbouring query blocks.
+    // Consecutive workgroup ids land on different XCDs; every XCD is given a
+    // contiguous range of items so its L2 sees neighbouring query blocks.  With
+    // a work order (lists of unequal length) each range is taken longest first;
+    // without one (dense mode: equal work) in raster order.
     const int64_t total = (int64_t)heads * pairs_per_head;
     int64_t item;
     if (order) {
-        if ((int64_t)blockIdx.x >= total) return;
-        item = ((const const_i32_t *)order)[blockIdx.x];
+        item = ((const const_i32_t *)order)[blockIdx.x];  // one slot per workgroup
+        if (item < 0) return;
     } else {
         item = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     }
@@ -145,31 +122,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     pair_blocks((int)(item % pairs_per_head), g, blk[0], blk[1]);
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
     const int hl = lane >> 5, l32 = lane & 31;
     const int side = wave >> 1;          // which block of the pair this wave computes
     const int qb = blk[side];            // -1: absent (odd tile-row count)
-
-    // Both cursors are tracked (redundantly) by every wave.
-    ListCursor ca, cb;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        ListCursor &c = k ? cb : ca;
-        const int b = blk[k];
-        c.j = 0;
-        c.list = nullptr;
-        if (b < 0) {
-            c.n = 0;
-        } else if (idx) {
-            const int64_t row = (int64_t)h * g.nb + b;
-            const int64_t m = ((const const_i32_t *)cnt)[row];
-            c.n = (int)(m < 0 ? 0 : (m > maxcnt ? maxcnt : m));
-            c.list = (const const_i32_t *)idx + row * maxcnt;
-        } else {
-            c.n = g.nb;
-        }
-        list_seek(c, g.nb);
-    }
 
     // This lane's query token (clamped into the grid for the missing cells of
     // an edge tile, and for an absent block; such rows are never stored).
@@ -183,47 +140,57 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
                         ((size_t)t * g.H + min(qy, g.H - 1)) * g.W + min(qx, g.W - 1);
     float *o = out + qtok * D;
 
-    int kb = min(ca.cur, cb.cur);
-    if (kb == INT32_MAX) {  // neither block keeps anything: zeros
+    // The item's union walk: n entries (block << 2) | sides (bit 0: the upper
+    // block keeps it, bit 1: the lower one), read through a 64-entry window
+    // held one entry per lane (the next window is fetched 64 entries early).
+    // The dense mode walks every block with both sides.
+    const int32_t *ul = ulist ? ulist + item * ustride : nullptr;
+    int n = g.nb;
+    if (ul) {
+        const int64_t m = ((const const_i32_t *)ulen)[item];
+        n = (int)(m < 0 ? 0 : (m > ustride ? ustride : m));
+    }
+    if (n == 0) {  // neither block keeps anything: zeros
         if (qreal)
             for (int c = 0; c < D / 2; c += 4)
                 *reinterpret_cast<float4 *>(o + c + (D / 2) * hl) = make_float4(0.f, 0.f, 0.f, 0.f);
         return;
     }
-
-    // Direct global -> LDS copy of block `blk`'s packed tiles into ring slot
-    // `slot`: each wave moves 2 PPW 1 KB pieces of K and of V^T; lane l lands 16
-    // bytes at piece base + 16 l.
-    const size_t head_tiles = (size_t)h * g.nb;
-#define TRA_ISSUE(blk, slot)                                                                  \
-    do {                                                                                      \
-        const char *ks_ = reinterpret_cast<const char *>(kt + (head_tiles + (blk)) * 64 * D) + wave_piece_bytes; \
-        const char *vs_ = reinterpret_cast<const char *>(vt + (head_tiles + (blk)) * 64 * D) + wave_piece_bytes; \
-        _Pragma("unroll") for (int i_ = 0; i_ < 2 * PPW; ++i_) {                             \
-            __builtin_amdgcn_global_load_lds((const global_void_t *)(ks_ + lane16 + i_ * 1024), \
-                                             (lds_void_t *)&ring[slot][0][wave_piece_elems + i_ * 512], 16, 0, 0); \
-            __builtin_amdgcn_global_load_lds((const global_void_t *)(vs_ + lane16 + i_ * 1024), \
-                                             (lds_void_t *)&ring[slot][1][wave_piece_elems + i_ * 512], 16, 0, 0); \
-        }                                                                                     \
-    } while (0)
-    // this wave's share of every copy, and this lane's 16 bytes of a piece
-    const int wave_piece_bytes = wave * 2 * PPW * 1024;
-    const int wave_piece_elems = wave * 2 * PPW * 512;
-    const int lane16 = lane * 16;
-
-    // Per-lane LDS element offsets of the matrix-core operands inside a slot:
-    // K row l32, chunk (2 ks + hl) swizzled; V^T row d = 32 mt + l32, chunk
-    // (2 ks2 + hl) swizzled.
-    int kofs[KS], vofs[MT][2];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kofs[ks] = l32 * D + 8 * ((2 * ks + hl) ^ (l32 & KSW));
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int ks2 = 0; ks2 < 2; ++ks2) {
-            const int d = 32 * mt + l32;
-            vofs[mt][ks2] = d * 32 + 8 * ((2 * ks2 + hl) ^ ((d >> 2) & 3));
+    int win = 0, win_next = 0, wbase = 0;
+    if (ul) {
+        win = lane < n ? ul[lane] : 0;
+        win_next = 64 + lane < n ? ul[64 + lane] : 0;
+    }
+    // Entry i (-1 past the end); called with i = 0, 1, 2, ... in turn.
+    auto entry = [&](int i) -> int {
+        if (i >= n) return -1;
+        if (!ul) return (i << 2) | 3;
+        if (i >= wbase + 64) {
+            win = win_next;
+            wbase += 64;
+            win_next = wbase + 64 + lane < n ? ul[wbase + 64 + lane] : 0;
         }
+        return __builtin_amdgcn_readlane(win, i - wbase);
+    };
+
+    // Direct global -> LDS copy of one packed tile of block `blk` into `dst`:
+    // each wave moves PPW 1 KB pieces; lane l lands 16 bytes at piece base + 16 l.
+    const size_t head_tiles = (size_t)h * g.nb;
+    const int wave_piece_bytes = wave * PPW * 1024;
+    const int wave_piece_elems = wave * PPW * 512;
+    const int lane16 = lane * 16;
+#define TRA_ISSUE(src, dst, blk)                                                              \
+    do {                                                                                      \
+        const char *s_ = reinterpret_cast<const char *>(src + (head_tiles + (blk)) * 64 * D) + \
+                         wave_piece_bytes + lane16;                                           \
+        _Pragma("unroll") for (int i_ = 0; i_ < PPW; ++i_)                                    \
+            __builtin_amdgcn_global_load_lds((const global_void_t *)(s_ + i_ * 1024),         \
+                                             (lds_void_t *)&(dst)[wave_piece_elems + i_ * 512], 16, 0, 0); \
+    } while (0)
+
+    // Every matrix-core operand of a packed tile is a 1 KB piece in which this
+    // lane's 8 elements sit at element 8 * lane.
+    const int lane8 = lane * 8;
 
     bf16x8_t qreg[KS];
 #pragma unroll
@@ -237,88 +204,117 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
         for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
     float m_ref = -1e30f, l_run = 0.f;
 
-    // Union walk over whole blocks: the copy cursor (pa, pb, pkb) runs one
-    // block ahead of the compute cursor (ca, cb, kb).
-    ListCursor pa = ca, pb = cb;
-    int pkb = kb;
-    auto advance = [&](ListCursor &xa, ListCursor &xb, int &xkb) {
-        if (xa.cur == xkb) { ++xa.j; list_seek(xa, g.nb); }
-        if (xb.cur == xkb) { ++xb.j; list_seek(xb, g.nb); }
-        xkb = min(xa.cur, xb.cur);
-    };
-    TRA_ISSUE(pkb, 0);
-    advance(pa, pb, pkb);
-    const bool two = pkb != INT32_MAX;
-    if (two) {
-        TRA_ISSUE(pkb, 1);
-        advance(pa, pb, pkb);
-        __builtin_amdgcn_s_waitcnt(wait_vmcnt(4 * PPW));  // block 0 landed
+    int e0 = entry(0), e1 = entry(1);  // entries u and u + 1
+    TRA_ISSUE(kt, kring[0], e0 >> 2);
+    if (e1 >= 0) {
+        TRA_ISSUE(kt, kring[1], e1 >> 2);
+        TRA_ISSUE(vt, vring[0], e0 >> 2);
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * PPW));  // K of entry 0 landed
     } else {
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        TRA_ISSUE(vt, vring[0], e0 >> 2);
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(PPW));
     }
     __syncthreads();
 
-    auto block_step = [&](auto slot_tag) -> bool {
-        constexpr int slot = decltype(slot_tag)::value;
-        const bool mine = (side ? cb.cur : ca.cur) == kb;
-        if (mine) {
-            const uint32_t row = fdiv((uint32_t)kb, div_nbx);
-            const int kbx = (int)((uint32_t)kb - row * div_nbx.d);
+    // Probabilities (fp16) of the previous entry, waiting for their P.V, and
+    // the rescale of O their reference asks for.
+    f16x8_t pk[2][2];
+    bool rescale = false;
+    float alpha_o = 1.f;
+    bool prev_mine = false;  // this wave's block kept the previous entry
+
+    // One step of the software pipeline for this wave: the logits of entry u
+    // (DS) on the matrix cores; then O += V^T P^T for the previous entry (DP)
+    // on the matrix cores while the VALU turns entry u's logits into
+    // probabilities (max, reference, exp, fp16, row sums).  A move of the
+    // reference rescales O before the next product, after the previous
+    // entry's product has landed in it.
+    auto work = [&](auto slot_tag, auto ds_tag, auto dp_tag) {
+        constexpr int s = decltype(slot_tag)::value;
+        constexpr bool DS = decltype(ds_tag)::value != 0;
+        constexpr bool DP = decltype(dp_tag)::value != 0;
+        f32x16_t sb[2];
+        if constexpr (DS) {
+            const uint16_t *Kt = kring[s];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sb[hf][r] = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf16x8_t ka = lds_load16<bf16x8_t>(Kt + (hf * KS + ks) * 512 + lane8);
+                    sb[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], sb[hf], 0, 0, 0);
+                }
+            }
+            // Keys of an edge tile beyond the grid: register r of half hf holds
+            // key row 4 hf + r / 4 and key column 4 hl + r % 4 of the tile.
+            const uint32_t kb = (uint32_t)(e0 >> 2);
+            const uint32_t row = fdiv(kb, div_nbx);
+            const int kbx = (int)(kb - row * div_nbx.d);
             const int kby = (int)(row - fdiv(row, div_nby) * div_nby.d);
             const int kny = min(kTileSide, g.H - kTileSide * kby);
             const int knx = min(kTileSide, g.W - kTileSide * kbx);
-            const uint16_t *Kt = ring[slot][0];
-            const uint16_t *Vt = ring[slot][1];
-            f32x16_t s[2];
+            if (knx < kTileSide) {
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                bf16x8_t ka[KS];
+                for (int c = 0; c < 4; ++c) {
+                    const bool bad = 4 * hl + c >= knx;
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) ka[ks] = lds_load16<bf16x8_t>(Kt + hf * 32 * D + kofs[ks]);
+                    for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) s[hf][r] = 0.f;
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    s[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qreg[ks], s[hf], 0, 0, 0);
+                        for (int rg = 0; rg < 4; ++rg)
+                            sb[hf][4 * rg + c] = bad ? -INFINITY : sb[hf][4 * rg + c];
+                }
             }
-            if (kny < kTileSide || knx < kTileSide) {
+            if (kny < kTileSide) {
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const bool bad = (4 * hf + (r >> 2) >= kny) || (4 * hl + (r & 3) >= knx);
-                        s[hf][r] = bad ? -INFINITY : s[hf][r];
-                    }
+                    for (int rg = 0; rg < 4; ++rg)
+                        if (4 * hf + rg >= kny)
+#pragma unroll
+                            for (int c = 0; c < 4; ++c) sb[hf][4 * rg + c] = -INFINITY;
             }
+        }
+        if constexpr (DP) {
+            if (rescale) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[mt][r] *= alpha_o;
+            }
+            const uint16_t *Vt = vring[s ^ 1];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int ks2 = 0; ks2 < 2; ++ks2) {
+                        const f16x8_t a = lds_load16<f16x8_t>(Vt + ((hf * MT + mt) * 2 + ks2) * 512 + lane8);
+                        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pk[hf][ks2], acc[mt], 0, 0, 0);
+                    }
+        }
+        if constexpr (DS) {
             float mx = -INFINITY;
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[hf][r]);
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sb[hf][r]);
             mx = half_swap_max(mx) * scale_log2;
             const bool grow = mx > m_ref + kRescaleLog2;
-            if (__any(grow)) {
-                const float m_new = grow ? mx : m_ref;
-                const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-                l_run *= alpha;
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[mt][r] *= alpha;
-                m_ref = m_new;
-            }
-            f16x8_t pk[2][2];
+            const float m_new = grow ? mx : m_ref;
+            const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+            m_ref = m_new;
             float psum0 = 0.f, psum1 = 0.f;
             const f16x2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    s[hf][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[hf][r], scale_log2, -m_ref));
+                    sb[hf][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[hf][r], scale_log2, -m_ref));
 #pragma unroll
                 for (int ks2 = 0; ks2 < 2; ++ks2) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) pk[hf][ks2][e] = (_Float16)s[hf][8 * ks2 + e];
+                    for (int e = 0; e < 8; ++e) pk[hf][ks2][e] = (_Float16)sb[hf][8 * ks2 + e];
 #pragma unroll
                     for (int e = 0; e < 8; e += 4) {
                         const f16x2_t a = {pk[hf][ks2][e], pk[hf][ks2][e + 1]};
@@ -328,29 +324,41 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
                     }
                 }
             }
-            l_run += psum0 + psum1;
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                    for (int ks2 = 0; ks2 < 2; ++ks2) {
-                        const f16x8_t a = lds_load16<f16x8_t>(Vt + hf * HALF + vofs[mt][ks2]);
-                        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pk[hf][ks2], acc[mt], 0, 0, 0);
-                    }
+            l_run = l_run * alpha + (psum0 + psum1);
+            rescale = __any(grow);  // O follows before this entry's P.V
+            alpha_o = alpha;
         }
-        advance(ca, cb, kb);
-        if (kb == INT32_MAX) return false;
-        // the next block is the only copy in flight: wait for it, then refill this slot
+    };
+    using T0 = SlotTag<0>;
+    using T1 = SlotTag<1>;
+
+    // Step u: K of entry u is in kring[u & 1], V^T of entry u - 1 in
+    // vring[(u - 1) & 1].  One extra step after the last entry drains the
+    // pipeline (e0 == -1).
+    int u = 0;
+    auto step = [&](auto slot_tag) -> bool {
+        const bool mine = e0 >= 0 && ((e0 >> side) & 1);
+        if (mine) {
+            if (prev_mine) work(slot_tag, T1{}, T1{});
+            else work(slot_tag, T1{}, T0{});
+        } else if (prev_mine) {
+            work(slot_tag, T0{}, T1{});
+        }
+        prev_mine = mine;
+        if (e0 < 0) return false;
+        // K of entry u + 1 and V^T of entry u were the copies in flight
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
-        if (pkb != INT32_MAX) {
-            TRA_ISSUE(pkb, slot);
-            advance(pa, pb, pkb);
-        }
+        constexpr int s = decltype(slot_tag)::value;
+        const int e2 = entry(u + 2);
+        if (e2 >= 0) TRA_ISSUE(kt, kring[s], e2 >> 2);      // entry u + 2
+        if (e1 >= 0) TRA_ISSUE(vt, vring[s ^ 1], e1 >> 2);  // entry u + 1
+        e0 = e1;
+        e1 = e2;
+        ++u;
         return true;
     };
-    while (block_step(SlotTag<0>{}) && block_step(SlotTag<1>{})) {
+    while (step(T0{}) && step(T1{})) {
     }
 #undef TRA_ISSUE
 
@@ -372,7 +380,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
 }  // namespace
 
 hipError_t launch_attn(int D, const uint16_t *q, const uint16_t *kt, const uint16_t *vt,
-                       const int32_t *idx, const int32_t *cnt, int64_t maxcnt,
+                       const int32_t *ulist, const int32_t *ulen, int64_t ustride,
                        const int32_t *order, const Grid &g, int heads, float *out,
                        hipStream_t s) {
     const int pph = pairs_per_head(g);
@@ -388,11 +396,11 @@ hipError_t launch_attn(int D, const uint16_t *q, const uint16_t *kt, const uint1
     };
     const FastDiv div_nbx = magic(g.nbx), div_nby = magic(g.nby);
     if (D == 128)
-        hipLaunchKernelGGL(attn_kernel<128>, grid, block, 0, s, q, kt, vt, idx, cnt, maxcnt, order,
-                           g, heads, pph, per_xcd, div_nbx, div_nby, out, scale_log2);
+        hipLaunchKernelGGL(attn_kernel<128>, grid, block, 0, s, q, kt, vt, ulist, ulen, ustride,
+                           order, g, heads, pph, per_xcd, div_nbx, div_nby, out, scale_log2);
     else if (D == 64)
-        hipLaunchKernelGGL(attn_kernel<64>, grid, block, 0, s, q, kt, vt, idx, cnt, maxcnt, order,
-                           g, heads, pph, per_xcd, div_nbx, div_nby, out, scale_log2);
+        hipLaunchKernelGGL(attn_kernel<64>, grid, block, 0, s, q, kt, vt, ulist, ulen, ustride,
+                           order, g, heads, pph, per_xcd, div_nbx, div_nby, out, scale_log2);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -17,15 +17,17 @@ struct Grid {
     int nb;        // T * nby * nbx
 };
 
-// Packed key/value tiles (tile-major, one 64-token tile after another):
-//   kt  bf16 [heads][nb][64 keys][D], key row w = (y % 8) * 8 + x % 8, missing
-//       cells zero; the 16-byte chunk c of row w is stored at chunk c ^ (w & KSW)
-//       with KSW = min(D/8, 16) - 1 so that the matrix-core operand reads of 16
-//       consecutive key rows hit distinct LDS banks.
-//   vt  fp16 [heads][nb][2 halves][D][32 positions] (V transposed, keys
-//       0..31 then 32..63), position p of a half holds key p with bits 2 and 3
-//       swapped, so that the 8 keys one lane feeds to the P.V product are
-//       contiguous; the 16-byte chunk c of row d is stored at c ^ ((d >> 2) & 3).
+// Packed key/value tiles (tile-major, one 64-token tile after another), each
+// tile a sequence of 1 KB matrix-core operand pieces in which lane l of a
+// wave64 finds its 8 operand elements at element 8 l, so that every operand
+// read is one contiguous, conflict-free 1 KB LDS access.  Key row w of a tile
+// is (y % 8) * 8 + x % 8; missing cells are zero.
+//   kt  bf16 [heads][nb][2 halves][D/16 k-steps][64 lanes][8]: piece (hf, ks),
+//       lane l holds K[32 hf + l % 32][16 ks + 8 (l / 32) + e], e = 0..7.
+//   vt  fp16 [heads][nb][2 halves][D/32 row tiles][2 k-steps][64 lanes][8]:
+//       piece (hf, mt, ks2), lane l holds V[32 hf + swap23(8 (2 ks2 + l / 32) + e)]
+//       [32 mt + l % 32], where swap23 exchanges bits 2 and 3 of a key position
+//       (so that the keys of a lane match the probabilities that lane holds).
 size_t packed_tile_elems(int D);
 
 hipError_t launch_pack_pool(int D, bool pool, bool pack, const uint16_t *q, const uint16_t *k,
@@ -58,14 +60,24 @@ __host__ __device__ inline void pair_blocks(int p, const Grid &g, int &qa, int &
     qb = 2 * pr + 1 < g.nby ? qa + g.nbx : -1;
 }
 
-// Longest-first order of the attention work items (query-block pairs); see
-// tra_mask.hip.  order has heads * pairs_per_head(g) entries.
-hipError_t launch_order(const int32_t *cnt, const Grid &g, int heads, int64_t maxcnt,
+// Union walk of each work item (see tra_mask.hip): ulist holds, at row stride
+// union_stride(maxcnt), entries (block << 2) | sides, ulen their counts.
+int64_t union_stride(int64_t maxcnt);
+hipError_t launch_union(const int32_t *idx, const int32_t *cnt, int64_t maxcnt, const Grid &g,
+                        int heads, int32_t *ulist, int32_t *ulen, hipStream_t s);
+
+// XCD-aware, longest-first order of the attention work items by union length:
+// order holds order_slots(g, heads) grid slots (-1: no item).
+inline int64_t order_slots(const Grid &g, int heads) {
+    return ((int64_t)heads * pairs_per_head(g) + 7) / 8 * 8;
+}
+hipError_t launch_order(const int32_t *ulen, const Grid &g, int heads, int64_t maxcnt,
                         int32_t *order, hipStream_t s);
 
-// order may be null (items in XCD-contiguous raster order, the dense mode).
+// ulist == nullptr: the dense mode (every block, both sides; order null, items
+// in XCD-contiguous raster order).
 hipError_t launch_attn(int D, const uint16_t *q, const uint16_t *kt, const uint16_t *vt,
-                       const int32_t *idx, const int32_t *cnt, int64_t maxcnt,
+                       const int32_t *ulist, const int32_t *ulen, int64_t ustride,
                        const int32_t *order, const Grid &g, int heads, float *out,
                        hipStream_t s);
 

@@ -66,33 +66,143 @@ hipError_t launch_mask(const int32_t *radius, const Grid &g, int heads, int r_ma
 namespace tra {
 namespace {
 
-// Work order for the attention kernel: the (head, query-block pair) items
-// sorted by descending list length of the longer list of the pair, so that
-// the longest items start first and the grid does not end on a long tail.
-// One workgroup: histogram of lengths in LDS, a descending prefix scan, then a
-// scatter (the order among equal lengths is arbitrary; results do not depend
-// on it).
+// Union of the two key lists of a work item (a pair of vertically adjacent
+// query blocks), the walk the attention kernel takes: entries
+// (block << 2) | sides, bit 0 set when the upper block keeps the block, bit 1
+// when the lower one does.  One wave64 per item.  For strictly ascending lists
+// inside [0, nb) (as the radius mask writes them) the union is ascending and
+// every block appears once: entry x = A[i] lands at
+//   i + |{b in B : b < x}| - |{a in A[0 .. i) : a in B}|
+// and an entry y = B[j] that A lacks at j + |{a in A : a < y}| - |{b in B[0 .. j) : b in A}|
+// (merge path by binary search).  Other lists are concatenated (the valid
+// entries of A, then those of B, each with its own side bit), which keeps the
+// attention exact: every query block still sees exactly its own entries.
+constexpr int kUnionWaves = 4;
+
+__device__ __forceinline__ int lanes_before(uint64_t bal) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+}
+
+__device__ int lower_bound_list(const int32_t *l, int n, int x) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (l[mid] < x) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// True when l[0 .. n) is strictly ascending with every entry in [0, nb).
+__device__ bool list_ascending(const int32_t *l, int n, int nb, int lane) {
+    int last = -1;
+    for (int i0 = 0; i0 < n; i0 += 64) {
+        const int i = i0 + lane;
+        const int x = i < n ? l[i] : INT32_MAX;
+        int prev = __shfl_up(x, 1);
+        if (lane == 0) prev = last;
+        const bool good = i >= n || ((unsigned)x < (unsigned)nb && x > prev);
+        if (__any(!good)) return false;
+        last = __shfl(x, min(63, n - 1 - i0));
+    }
+    return true;
+}
+
+__global__ __launch_bounds__(64 * kUnionWaves) void union_kernel(
+    const int32_t *__restrict__ idx, const int32_t *__restrict__ cnt, int64_t maxcnt, Grid g,
+    int64_t items, int pairs_per_head, int64_t ustride, int32_t *__restrict__ ulist,
+    int32_t *__restrict__ ulen) {
+    const int64_t item = (int64_t)blockIdx.x * kUnionWaves + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (item >= items) return;
+    const int64_t h = item / pairs_per_head;
+    int qa, qb;
+    pair_blocks((int)(item % pairs_per_head), g, qa, qb);
+    auto len = [&](int b) -> int {
+        if (b < 0) return 0;
+        const int64_t m = cnt[h * g.nb + b];
+        return (int)(m < 0 ? 0 : (m > maxcnt ? maxcnt : m));
+    };
+    const int32_t *A = idx + (h * g.nb + qa) * maxcnt;
+    const int32_t *B = qb >= 0 ? idx + (h * g.nb + qb) * maxcnt : A;
+    const int a = len(qa), b = len(qb);
+    int32_t *out = ulist + item * ustride;
+    int n = 0;
+    if (list_ascending(A, a, g.nb, lane) && list_ascending(B, b, g.nb, lane)) {
+        int common = 0;
+        for (int i0 = 0; i0 < a; i0 += 64) {
+            const int i = i0 + lane;
+            int x = 0, pos = 0;
+            bool in_b = false;
+            if (i < a) {
+                x = A[i];
+                pos = lower_bound_list(B, b, x);
+                in_b = pos < b && B[pos] == x;
+            }
+            const uint64_t bal = __ballot(in_b);
+            if (i < a) out[i + pos - common - lanes_before(bal)] = (x << 2) | 1 | (in_b ? 2 : 0);
+            common += __popcll(bal);
+        }
+        int common_b = 0;
+        for (int j0 = 0; j0 < b; j0 += 64) {
+            const int j = j0 + lane;
+            int y = 0, pos = 0;
+            bool in_a = false;
+            if (j < b) {
+                y = B[j];
+                pos = lower_bound_list(A, a, y);
+                in_a = pos < a && A[pos] == y;
+            }
+            const uint64_t bal = __ballot(in_a);
+            if (j < b && !in_a) out[j + pos - common_b - lanes_before(bal)] = (y << 2) | 2;
+            common_b += __popcll(bal);
+        }
+        n = a + b - common;
+    } else {
+#pragma unroll
+        for (int side = 0; side < 2; ++side) {
+            const int32_t *l = side ? B : A;
+            const int m = side ? b : a;
+            for (int i0 = 0; i0 < m; i0 += 64) {
+                const int i = i0 + lane;
+                const int x = i < m ? l[i] : -1;
+                const bool keep = i < m && (unsigned)x < (unsigned)g.nb;
+                const uint64_t bal = __ballot(keep);
+                if (keep) out[n + lanes_before(bal)] = (x << 2) | (1 << side);
+                n += __popcll(bal);
+            }
+        }
+    }
+    if (lane == 0) ulen[item] = n;
+}
+
+// Work order for the attention kernel.  Workgroup ids are dealt to the eight
+// XCDs round robin (id % 8), each XCD with its own L2, so XCD x is given the
+// contiguous raster range x of the items (neighbouring query blocks of the
+// same head share most key tiles) and takes it longest first, so that long
+// items do not start last and leave a tail: the k-th longest item of range x
+// goes to grid slot 8 k + x, slots past a short range hold -1.  One workgroup
+// per XCD: histogram of lengths in LDS, a descending prefix scan, a scatter
+// (the order among equal lengths is arbitrary; results do not depend on it).
 constexpr int kOrderThreads = 1024;
 constexpr int kOrderMaxBin = 8191;
+constexpr int kXcds = 8;
 
-__global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *__restrict__ cnt,
-                                                              Grid g, int64_t items,
-                                                              int pairs_per_head, int maxlen,
+__global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *__restrict__ ulen,
+                                                              int64_t items, int maxlen,
                                                               int32_t *__restrict__ order) {
     extern __shared__ int32_t bins[];  // maxlen + 1 bins
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, x = blockIdx.x;
+    const int64_t per = (items + kXcds - 1) / kXcds;
+    const int64_t lo = x * per, hi = min(items, lo + per);
     for (int i = tid; i <= maxlen; i += kOrderThreads) bins[i] = 0;
     __syncthreads();
     auto length_of = [&](int64_t it) -> int {
-        const int64_t h = it / pairs_per_head;
-        int qa, qb;
-        pair_blocks((int)(it % pairs_per_head), g, qa, qb);
-        const int32_t *row = cnt + h * g.nb;
-        int len = row[qa];
-        if (qb >= 0) len = max(len, (int)row[qb]);
+        const int len = ulen[it];
         return len < 0 ? 0 : (len > maxlen ? maxlen : len);
     };
-    for (int64_t it = tid; it < items; it += kOrderThreads) atomicAdd(&bins[length_of(it)], 1);
+    for (int64_t it = lo + tid; it < hi; it += kOrderThreads) atomicAdd(&bins[length_of(it)], 1);
     __syncthreads();
     if (tid == 0) {  // descending exclusive scan: longest lengths first
         int run = 0;
@@ -103,23 +213,36 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *__r
         }
     }
     __syncthreads();
-    for (int64_t it = tid; it < items; it += kOrderThreads) {
-        const int slot = atomicAdd(&bins[length_of(it)], 1);
-        order[slot] = (int32_t)it;
+    for (int64_t it = lo + tid; it < hi; it += kOrderThreads) {
+        const int64_t k = atomicAdd(&bins[length_of(it)], 1);
+        order[kXcds * k + x] = (int32_t)it;
     }
+    for (int64_t k = (hi > lo ? hi - lo : 0) + tid; k < per; k += kOrderThreads)
+        order[kXcds * k + x] = -1;
 }
 
 }  // namespace
 
-hipError_t launch_order(const int32_t *cnt, const Grid &g, int heads, int64_t maxcnt,
-                        int32_t *order, hipStream_t s) {
+int64_t union_stride(int64_t maxcnt) { return (2 * maxcnt + 63) / 64 * 64; }
+
+hipError_t launch_union(const int32_t *idx, const int32_t *cnt, int64_t maxcnt, const Grid &g,
+                        int heads, int32_t *ulist, int32_t *ulen, hipStream_t s) {
     const int pph = pairs_per_head(g);
     const int64_t items = (int64_t)heads * pph;
+    hipLaunchKernelGGL(union_kernel, dim3((unsigned)((items + kUnionWaves - 1) / kUnionWaves)),
+                       dim3(64 * kUnionWaves), 0, s, idx, cnt, maxcnt, g, items, pph,
+                       union_stride(maxcnt), ulist, ulen);
+    return hipGetLastError();
+}
+
+hipError_t launch_order(const int32_t *ulen, const Grid &g, int heads, int64_t maxcnt,
+                        int32_t *order, hipStream_t s) {
+    const int64_t items = (int64_t)heads * pairs_per_head(g);
     // lengths above kOrderMaxBin share the top bin (they still start first)
-    const int maxlen = (int)(maxcnt < kOrderMaxBin ? maxcnt : kOrderMaxBin);
+    const int maxlen = (int)(2 * maxcnt < kOrderMaxBin ? 2 * maxcnt : kOrderMaxBin);
     const size_t lds = (size_t)(maxlen + 1) * sizeof(int32_t);
-    hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), lds, s, cnt, g, items, pph,
-                       maxlen, order);
+    hipLaunchKernelGGL(order_kernel, dim3(kXcds), dim3(kOrderThreads), lds, s, ulen, items, maxlen,
+                       order);
     return hipGetLastError();
 }
 

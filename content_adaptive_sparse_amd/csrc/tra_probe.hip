@@ -37,7 +37,8 @@ __global__ __launch_bounds__(256) void pack_pool_kernel(
     constexpr int CH = D / 8;
     constexpr int RG = 256 / CH;
     constexpr int RPT = 64 / RG;
-    constexpr int KSW = (CH < 16 ? CH : 16) - 1;
+    constexpr int KS = D / 16;     // 16-wide k-steps of Q.K^T
+    constexpr int MT = D / 32;     // 32-row tiles of O^T
     constexpr int VPITCH = D + 8;  // fp16 elements per LDS row of the V tile
 
     __shared__ float red[POOL ? 2 : 1][POOL ? RG : 1][POOL ? D : 1];
@@ -86,7 +87,10 @@ __global__ __launch_bounds__(256) void pack_pool_kernel(
             }
         }
         if (PACK) {
-            *reinterpret_cast<uint4 *>(kt + (tile * 64 + w) * D + 8 * (c ^ (w & KSW))) = kk;
+            // K fragment piece (w / 32, c / 2), lane 32 (c % 2) + w % 32
+            const int piece = (w >> 5) * KS + (c >> 1);
+            const int lane = 32 * (c & 1) + (w & 31);
+            *reinterpret_cast<uint4 *>(kt + tile * 64 * D + (piece * 64 + lane) * 8) = kk;
             const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
             uint32_t hw[4];
 #pragma unroll
@@ -119,14 +123,13 @@ __global__ __launch_bounds__(256) void pack_pool_kernel(
         }
     }
     if (PACK) {
-        // V^T tile as two 32-key halves, each D rows of 32 key positions
-        // (64 bytes = 4 chunks per row), chunk c of row d stored at
-        // c ^ ((d >> 2) & 3).
-        for (int o = tid; o < 2 * D * 4; o += 256) {
-            const int hf = o / (D * 4);
-            const int dd = (o >> 2) % D;
-            const int cs = o & 3;                 // stored chunk
-            const int cc = cs ^ ((dd >> 2) & 3);  // logical chunk held there
+        // V^T fragment pieces (hf, mt, ks2): lane l holds row d = 32 mt + l % 32
+        // at the eight keys 32 hf + swap_bits23(8 (2 ks2 + l / 32) + e).
+        for (int o = tid; o < 2 * MT * 2 * 64; o += 256) {
+            const int piece = o >> 6, lane = o & 63;
+            const int hf = piece / (2 * MT), mt = (piece >> 1) % MT, ks2 = piece & 1;
+            const int dd = 32 * mt + (lane & 31);
+            const int cc = 2 * ks2 + (lane >> 5);
             uint32_t w32[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -134,7 +137,7 @@ __global__ __launch_bounds__(256) void pack_pool_kernel(
                 const int k1 = 32 * hf + swap_bits23(8 * cc + 2 * e + 1);
                 w32[e] = (uint32_t)vs[k0][dd] | ((uint32_t)vs[k1][dd] << 16);
             }
-            *reinterpret_cast<uint4 *>(vt + tile * 64 * D + hf * 32 * D + dd * 32 + 8 * cs) =
+            *reinterpret_cast<uint4 *>(vt + tile * 64 * D + (size_t)o * 8) =
                 make_uint4(w32[0], w32[1], w32[2], w32[3]);
         }
     }

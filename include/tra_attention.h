@@ -167,7 +167,8 @@ enum tra_kernel_kind {
     TRA_KERNEL_ATTN = 3,      /* block-sparse attention */
     TRA_KERNEL_FILL = 4,      /* dense-mode radius fill */
     TRA_KERNEL_ORDER = 5,     /* longest-first order of the attention work items */
-    TRA_KERNEL_KINDS = 6
+    TRA_KERNEL_UNION = 6,     /* union walk of each pair of query blocks' lists */
+    TRA_KERNEL_KINDS = 7
 };
 int tra_profile_begin(void);
 int tra_profile_end(double *ms, int *launches, int n);

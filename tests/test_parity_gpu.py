@@ -248,6 +248,51 @@ def test_list_edge_cases():
         assert_close(out[0, blocks[b]], ref_rows(b, [b]), f"own block {b}")
 
 
+def test_list_walk_cases():
+    # Each attention work item walks the union of a vertically adjacent pair
+    # of query blocks' lists: ascending lists merge (overlaps computed once,
+    # unions longer than 64 entries), other lists (descending, duplicates)
+    # are walked as they stand.  Every block must still see exactly its own
+    # list, a duplicate counting twice.
+    T, H, W, heads, d = 20, 16, 16, 1, 128
+    shp = (heads, T, H, W, d)
+    print(f"[case] list walk cases {shp}", flush=True)
+    q, k, v = ti.random_qkv(T, H, W, heads, d, seed=11)
+    qd, kd, vd = dev16(q), dev16(k), dev16(v)
+    nb = tra.tra_grid(T, H, W)[2]
+    assert nb == 80
+    maxcnt = nb
+    lists = {b: [b] for b in range(nb)}
+    lists[0] = list(range(nb - 1, -1, -1))          # descending: walked as is
+    lists[2] = [5, 5, 7]                            # duplicate counts twice
+    lists[1] = list(range(0, nb, 2))                # pair (1, 3): overlapping merge
+    lists[3] = list(range(0, nb, 3))
+    lists[4] = list(range(nb))                      # pair (4, 6): union of 80 entries
+    lists[6] = []
+    lists[5] = [nb - 1]                             # pair (5, 7): disjoint
+    lists[7] = [0]
+    idx = np.full((heads, nb, maxcnt), -1, dtype=np.int32)
+    cnt = np.zeros((heads, nb), dtype=np.int32)
+    for b, l in lists.items():
+        idx[0, b, :len(l)] = l
+        cnt[0, b] = len(l)
+    out = gpu_attn(qd, kd, vd, shp, torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(),
+                   maxcnt).cpu().numpy().reshape(heads, -1, d)
+    tok = np.arange(T * H * W).reshape(T, H, W)
+    blocks = [tok[t, 8 * by:8 * by + 8, 8 * bx:8 * bx + 8].ravel()
+              for t in range(T) for by in range(2) for bx in range(2)]
+    qf, kf, vf = (ti.bf16_to_f32(a).astype(np.float64).reshape(heads, -1, d) for a in (q, k, v))
+    for b in range(nb):
+        if not lists[b]:
+            assert (out[0, blocks[b]] == 0).all()
+            continue
+        keys = np.concatenate([blocks[kb] for kb in lists[b]])
+        s = qf[0, blocks[b]] @ kf[0, keys].T / math.sqrt(d)
+        w = np.exp(s - s.max(axis=1, keepdims=True))
+        ref = (w / w.sum(axis=1, keepdims=True)) @ vf[0, keys]
+        assert_close(out[0, blocks[b]], ref, f"walk block {b} ({len(lists[b])} entries)")
+
+
 def test_mask_clamps_radius_to_r_max():
     T, H, W, heads = 6, 24, 40, 1
     shp = (heads, T, H, W, 64)

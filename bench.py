@@ -212,6 +212,48 @@ def main():
             log(f"[bench] sweep {sweep[-1]}")
             del ix, cn
 
+    # ---- cross-step reuse: probe, mask and walk plan once (the warm-up step);
+    # every later step packs k, v and runs the attention along the stored plan ----
+    reuse, routing = None, None
+    if not args.no_sweep:
+        idx = torch.empty(heads, nb, maxcnt, dtype=torch.int32, device="cuda")
+        tra.tra_mask(radius, T, H, W, heads, 64, c.r_max, idx, cnt)
+        plan = torch.empty(tra.tra_plan_bytes(T, H, W, heads, 64, maxcnt), dtype=torch.uint8,
+                           device="cuda")
+        tra.tra_plan(idx, cnt, maxcnt, T, H, W, heads, 64, plan)
+        step = lambda: tra.tra_attn_plan(qd, kd, vd, T, H, W, heads, d, 64, plan, maxcnt, out)
+        ms_reuse, _ = timed(step, max(5, args.steps // 2), 2)
+        reuse = {"ms_per_step": round(ms_reuse, 4),
+                 "speedup_vs_dense_layer": round(ms_dense / ms_reuse, 3),
+                 "plan_bytes": int(plan.numel())}
+        log(f"[bench] cross-step reuse {reuse}")
+        del idx, plan
+
+        # ---- binary routing: the 20% of blocks per head with the highest
+        # pooled-probe entropy attend densely, the rest with radius 1 ----
+        hn = torch.empty(heads, nb, dtype=torch.float32, device="cuda")
+        rtmp = torch.empty(heads, nb, dtype=torch.int32, device="cuda")
+        tra.tra_probe(qd, kd, T, H, W, heads, d, 64, c.r_min, c.r_max, rtmp, hn)
+        hnn = hn.cpu().numpy()
+        cut = np.quantile(hnn, 0.8, axis=1, keepdims=True)
+        rr = np.where(hnn >= cut, INF, 1).astype(np.int32)
+        rd = torch.from_numpy(rr).cuda()
+        ix = torch.empty(heads, nb, nb, dtype=torch.int32, device="cuda")
+        cn = torch.empty(heads, nb, dtype=torch.int32, device="cuda")
+        tra.tra_mask(rd, T, H, W, heads, 64, INF, ix, cn)
+        torch.cuda.synchronize()
+        cnn = cn.cpu().numpy()
+        p = int(cnn.sum())
+        kk = profiled(lambda: tra.tra_attn(qd, kd, vd, T, H, W, heads, d, 64, ix, cn, nb, out), 5)
+        routing = {"dense_blocks": round(float((rr == INF).mean()), 4), "local_radius": 1,
+                   "density": round(p / (heads * nb * nb), 4),
+                   "list_len_min_mean_max": [int(cnn.min()), round(float(cnn.mean()), 1), int(cnn.max())],
+                   "attn_ms": round(kk["attn"], 4),
+                   "tflops": round(flops_pair * p / (kk["attn"] * 1e-3) / 1e12, 1),
+                   "speedup_vs_dense_attn": round(kd_["attn"] / kk["attn"], 2)}
+        log(f"[bench] binary routing {routing}")
+        del ix, cn, rd
+
     # HBM bandwidth of the probe/pack kernel (algorithmic bytes: read q, k, v,
     # write the packed k and v^T tiles and the pooled means)
     pack_bytes = 3 * heads * c.N * d * 2 + 2 * heads * nb * 64 * d * 2 + 2 * heads * nb * d * 4
@@ -262,6 +304,8 @@ def main():
             "pack_pool_gbs": round(pack_gbs, 1),
             "mask_gbs": None if mask_gbs is None else round(mask_gbs, 2),
             "density_sweep": sweep,
+            "cross_step_reuse": reuse,
+            "binary_routing": routing,
             "wall_ms_per_step": round(ms_wall, 4),
             "pv_dtype": "fp16",
         },

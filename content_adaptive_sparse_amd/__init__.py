@@ -18,6 +18,7 @@ from .build import LIB_PATH
 __all__ = [
     "TRA_RADIUS_INF", "TraError", "library", "tra_attention", "tra_probe", "tra_mask",
     "tra_attn", "tra_grid", "tra_maxcnt", "tra_status_string", "tra_version",
+    "tra_plan_bytes", "tra_plan", "tra_attn_plan",
     "tra_profile_begin", "tra_profile_end", "KERNEL_KINDS",
 ]
 
@@ -59,6 +60,12 @@ def library() -> ctypes.CDLL:
         lib.tra_mask.restype = I
         lib.tra_attn.argtypes = [P, P, P, I, I, I, I, I, I, P, P, L, P, P]
         lib.tra_attn.restype = I
+        lib.tra_plan_bytes.argtypes = [I, I, I, I, I, L]
+        lib.tra_plan_bytes.restype = L
+        lib.tra_plan.argtypes = [P, P, L, I, I, I, I, I, P, P]
+        lib.tra_plan.restype = I
+        lib.tra_attn_plan.argtypes = [P, P, P, I, I, I, I, I, I, P, L, P, P]
+        lib.tra_attn_plan.restype = I
         lib.tra_profile_begin.argtypes = []
         lib.tra_profile_begin.restype = I
         lib.tra_profile_end.argtypes = [P, P, I]
@@ -159,6 +166,27 @@ def tra_attn(q, k, v, T, H, W, heads, head_dim, block, idx, cnt, maxcnt, out, st
         _ptr(q, _bf16(), "q"), _ptr(k, _bf16(), "k"), _ptr(v, _bf16(), "v"), T, H, W, heads,
         head_dim, block, _ptr(idx, _i32(), "idx"), _ptr(cnt, _i32(), "cnt"), int(maxcnt),
         _ptr(out, _f32(), "out"), _stream(stream)), "tra_attn")
+
+
+def tra_plan_bytes(T: int, H: int, W: int, heads: int, block: int, maxcnt: int) -> int:
+    n = library().tra_plan_bytes(T, H, W, heads, block, int(maxcnt))
+    if n < 0:
+        raise TraError(int(n), "tra_plan_bytes")
+    return n
+
+
+def tra_plan(idx, cnt, maxcnt, T, H, W, heads, block, plan, stream=None):
+    """Walk plan of the lists into ``plan`` (a GPU uint8 tensor of tra_plan_bytes bytes)."""
+    _check(library().tra_plan(
+        _ptr(idx, _i32(), "idx"), _ptr(cnt, _i32(), "cnt"), int(maxcnt), T, H, W, heads, block,
+        _ptr(plan, None, "plan"), _stream(stream)), "tra_plan")
+
+
+def tra_attn_plan(q, k, v, T, H, W, heads, head_dim, block, plan, maxcnt, out, stream=None):
+    _check(library().tra_attn_plan(
+        _ptr(q, _bf16(), "q"), _ptr(k, _bf16(), "k"), _ptr(v, _bf16(), "v"), T, H, W, heads,
+        head_dim, block, _ptr(plan, None, "plan"), int(maxcnt), _ptr(out, _f32(), "out"),
+        _stream(stream)), "tra_attn_plan")
 
 
 def tra_profile_begin():

@@ -273,6 +273,96 @@ static hipError_t plan_walk(const int32_t *idx, const int32_t *cnt, int64_t maxc
     return e;
 }
 
+// Layout of a walk plan in one buffer: work order, walk lengths, walks; each part
+// 256-byte aligned.
+struct PlanLayout {
+    size_t o_order, o_ulen, o_ulist, bytes;
+    int64_t ustride;
+};
+
+static PlanLayout plan_layout(const tra::Grid &g, int heads, int64_t maxcnt) {
+    auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+    PlanLayout L;
+    const size_t slots = order_items(g, heads);
+    L.ustride = tra::union_stride(maxcnt);
+    L.o_order = 0;
+    L.o_ulen = up(slots * sizeof(int32_t));
+    L.o_ulist = L.o_ulen + up(slots * sizeof(int32_t));
+    L.bytes = L.o_ulist + up(slots * (size_t)L.ustride * sizeof(int32_t));
+    return L;
+}
+
+// Pack k and v, then attention along a walk plan (nullptr: dense mode).
+static int attn_with_plan(const void *q, const void *k, const void *v, const tra::Grid &g,
+                          int heads, int head_dim, const char *plan, const PlanLayout &L,
+                          void *out, hipStream_t stream) {
+    Scratch ws(stream);
+    const size_t tiles = (size_t)heads * g.nb * tra::packed_tile_elems(head_dim) * 2;
+    const size_t o_kt = ws.reserve(tiles), o_vt = ws.reserve(tiles);
+    int rc = ws.allocate();
+    if (rc != TRA_OK) return rc;
+    uint16_t *kt = ws.at<uint16_t>(o_kt), *vt = ws.at<uint16_t>(o_vt);
+    hipError_t e;
+    {
+        ProfScope p(TRA_KERNEL_PACK_POOL, stream);
+        e = tra::launch_pack_pool(head_dim, false, true, nullptr, (const uint16_t *)k,
+                                  (const uint16_t *)v, g, heads, nullptr, nullptr, kt, vt, stream);
+    }
+    if (e == hipSuccess) {
+        ProfScope p(TRA_KERNEL_ATTN, stream);
+        const int32_t *order = plan ? (const int32_t *)(plan + L.o_order) : nullptr;
+        const int32_t *ulen = plan ? (const int32_t *)(plan + L.o_ulen) : nullptr;
+        const int32_t *ulist = plan ? (const int32_t *)(plan + L.o_ulist) : nullptr;
+        e = tra::launch_attn(head_dim, (const uint16_t *)q, kt, vt, ulist, ulen,
+                             plan ? L.ustride : 0, order, g, heads, (float *)out, stream);
+    }
+    return hip_status(e);
+}
+
+// Walk plans above 2^44 bytes are refused (they could not be allocated anyway).
+static int check_plan(const tra::Grid &g, int heads, int64_t maxcnt) {
+    if (maxcnt < 1 || maxcnt > (int64_t)1 << 30) return TRA_ERR_INVALID_ARG;
+    const double bytes = (double)order_items(g, heads) * (double)tra::union_stride(maxcnt) * 4.0;
+    return bytes > (double)((int64_t)1 << 44) ? TRA_ERR_UNSUPPORTED : TRA_OK;
+}
+
+int64_t tra_plan_bytes(int T, int H, int W, int heads, int block, int64_t maxcnt) {
+    tra::Grid g;
+    int rc = make_grid(T, H, W, block, &g);
+    if (rc == TRA_OK) rc = check_dims(heads, 64, g);
+    if (rc == TRA_OK) rc = check_plan(g, heads, maxcnt);
+    if (rc != TRA_OK) return rc;
+    return (int64_t)plan_layout(g, heads, maxcnt).bytes;
+}
+
+int tra_plan(const int32_t *idx, const int32_t *cnt, int64_t maxcnt, int T, int H, int W,
+             int heads, int block, void *plan, hipStream_t stream) {
+    tra::Grid g;
+    int rc = make_grid(T, H, W, block, &g);
+    if (rc == TRA_OK) rc = check_dims(heads, 64, g);
+    if (rc == TRA_OK) rc = check_plan(g, heads, maxcnt);
+    if (rc != TRA_OK) return rc;
+    if (!idx || !cnt || !plan) return TRA_ERR_INVALID_ARG;
+    const PlanLayout L = plan_layout(g, heads, maxcnt);
+    char *pb = static_cast<char *>(plan);
+    return hip_status(plan_walk(idx, cnt, maxcnt, g, heads, (int32_t *)(pb + L.o_ulist),
+                                (int32_t *)(pb + L.o_ulen), (int32_t *)(pb + L.o_order), stream));
+}
+
+int tra_attn_plan(const void *q, const void *k, const void *v, int T, int H, int W, int heads,
+                  int head_dim, int block, const void *plan, int64_t maxcnt, void *out,
+                  hipStream_t stream) {
+    tra::Grid g;
+    int rc = make_grid(T, H, W, block, &g);
+    if (rc == TRA_OK) rc = check_dims(heads, head_dim, g);
+    if (rc != TRA_OK) return rc;
+    if (rc == TRA_OK) rc = check_plan(g, heads, maxcnt);
+    if (rc != TRA_OK) return rc;
+    if (!q || !k || !v || !out || !plan) return TRA_ERR_INVALID_ARG;
+    return attn_with_plan(q, k, v, g, heads, head_dim, static_cast<const char *>(plan),
+                          plan_layout(g, heads, maxcnt), out, stream);
+}
+
 int tra_attn(const void *q, const void *k, const void *v, int T, int H, int W, int heads,
              int head_dim, int block, const int32_t *idx, const int32_t *cnt, int64_t maxcnt,
              void *out, hipStream_t stream) {
@@ -282,37 +372,19 @@ int tra_attn(const void *q, const void *k, const void *v, int T, int H, int W, i
     if (rc != TRA_OK) return rc;
     if (!q || !k || !v || !out) return TRA_ERR_INVALID_ARG;
     if ((idx == nullptr) != (cnt == nullptr)) return TRA_ERR_INVALID_ARG;
-    if (idx && maxcnt < 1) return TRA_ERR_INVALID_ARG;
+    if (idx && (rc = check_plan(g, heads, maxcnt)) != TRA_OK) return rc;
+    if (!idx) return attn_with_plan(q, k, v, g, heads, head_dim, nullptr, PlanLayout{}, out, stream);
 
+    const PlanLayout L = plan_layout(g, heads, maxcnt);
     Scratch ws(stream);
-    const size_t tiles = (size_t)heads * g.nb * tra::packed_tile_elems(head_dim) * 2;
-    const size_t o_kt = ws.reserve(tiles), o_vt = ws.reserve(tiles);
-    const size_t items = order_items(g, heads);
-    const int64_t ustride = idx ? tra::union_stride(maxcnt) : 0;
-    size_t o_order = 0, o_ulen = 0, o_ulist = 0;
-    if (idx) {
-        o_order = ws.reserve(items * sizeof(int32_t));
-        o_ulen = ws.reserve(items * sizeof(int32_t));
-        o_ulist = ws.reserve(items * (size_t)ustride * sizeof(int32_t));
-    }
+    const size_t o_plan = ws.reserve(L.bytes);
     if ((rc = ws.allocate()) != TRA_OK) return rc;
-    uint16_t *kt = ws.at<uint16_t>(o_kt), *vt = ws.at<uint16_t>(o_vt);
-    int32_t *order = idx ? ws.at<int32_t>(o_order) : nullptr;
-    int32_t *ulen = idx ? ws.at<int32_t>(o_ulen) : nullptr;
-    int32_t *ulist = idx ? ws.at<int32_t>(o_ulist) : nullptr;
-    hipError_t e;
-    {
-        ProfScope p(TRA_KERNEL_PACK_POOL, stream);
-        e = tra::launch_pack_pool(head_dim, false, true, nullptr, (const uint16_t *)k,
-                                  (const uint16_t *)v, g, heads, nullptr, nullptr, kt, vt, stream);
-    }
-    if (e == hipSuccess && idx) e = plan_walk(idx, cnt, maxcnt, g, heads, ulist, ulen, order, stream);
-    if (e == hipSuccess) {
-        ProfScope p(TRA_KERNEL_ATTN, stream);
-        e = tra::launch_attn(head_dim, (const uint16_t *)q, kt, vt, ulist, ulen, ustride, order, g,
-                             heads, (float *)out, stream);
-    }
-    return hip_status(e);
+    char *plan = ws.at<char>(o_plan);
+    const hipError_t e = plan_walk(idx, cnt, maxcnt, g, heads, (int32_t *)(plan + L.o_ulist),
+                                   (int32_t *)(plan + L.o_ulen), (int32_t *)(plan + L.o_order),
+                                   stream);
+    if (e != hipSuccess) return hip_status(e);
+    return attn_with_plan(q, k, v, g, heads, head_dim, plan, L, out, stream);
 }
 
 int tra_attention(const void *q, const void *k, const void *v, int T, int H, int W, int heads,

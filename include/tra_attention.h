@@ -142,7 +142,9 @@ int tra_mask(const int32_t *radius, int T, int H, int W, int heads, int block, i
  *           both NULL selects the dense mode (every block, ascending)
  *   out      device fp32 [heads][T][H][W][head_dim]
  * List entries outside [0, nb) are skipped and cnt is clamped to [0, maxcnt];
- * a query block whose list keeps no key gets zeros.
+ * any other entry counts once per occurrence, in any order (a duplicate block
+ * enters the softmax twice); a query block whose list keeps no key gets zeros.
+ * maxcnt must lie in [1, 2^30] when lists are given.
  * Arithmetic: q.k on bf16 matrix cores with fp32 accumulation; online softmax
  * in fp32; probabilities rounded to fp16 and multiplied with v (converted
  * exactly bf16 -> fp16) on fp16 matrix cores with fp32 accumulation.
@@ -150,6 +152,32 @@ int tra_mask(const int32_t *radius, int T, int H, int W, int heads, int block, i
 int tra_attn(const void *q, const void *k, const void *v, int T, int H, int W, int heads,
              int head_dim, int block, const int32_t *idx, const int32_t *cnt, int64_t maxcnt,
              void *out, hipStream_t stream);
+
+/*
+ * Plan / execute split with cross-step reuse (Token Radius Attention ...,
+ * "The TRA Pipeline: Cross-Step Reuse": the sparsity decided in a warm-up step
+ * is reused by the later denoising steps).  tra_plan turns key-block lists into
+ * the attention walk (per pair of vertically adjacent query blocks: the union of
+ * their two lists; then the work order) and stores it in a caller-owned device
+ * buffer of tra_plan_bytes bytes; tra_attn_plan then runs the attention of new
+ * q, k, v along that walk, so later steps skip the list processing.
+ * tra_attn(idx, cnt) is tra_plan followed by tra_attn_plan on library scratch.
+ *   plan      device buffer, tra_plan_bytes(T,H,W,heads,block,maxcnt) bytes,
+ *             owned by the caller; written by tra_plan, read by tra_attn_plan.
+ *             Its content is opaque; it is valid for the T, H, W, heads, block
+ *             and maxcnt it was made with and must be passed back with exactly
+ *             those (anything else is undefined, not detected).
+ *   idx, cnt, maxcnt  as for tra_attn (maxcnt in [1, 2^30]; lists as for tra_attn).
+ * tra_plan_bytes returns the size, or a negative status for invalid sizes.
+ * Plans are written on `stream`; using one on another stream needs the caller's
+ * own synchronisation.
+ */
+int64_t tra_plan_bytes(int T, int H, int W, int heads, int block, int64_t maxcnt);
+int tra_plan(const int32_t *idx, const int32_t *cnt, int64_t maxcnt, int T, int H, int W,
+             int heads, int block, void *plan, hipStream_t stream);
+int tra_attn_plan(const void *q, const void *k, const void *v, int T, int H, int W, int heads,
+                  int head_dim, int block, const void *plan, int64_t maxcnt, void *out,
+                  hipStream_t stream);
 
 /*
  * Optional per-kernel timing, for benchmarks.  Between tra_profile_begin and

@@ -34,7 +34,8 @@ def declared_functions():
 def test_header_declares_the_documented_entry_points():
     names = declared_functions()
     for n in ["tra_attention", "tra_probe", "tra_mask", "tra_attn", "tra_maxcnt", "tra_grid",
-              "tra_status_string", "tra_version", "tra_profile_begin", "tra_profile_end"]:
+              "tra_status_string", "tra_version", "tra_profile_begin", "tra_profile_end",
+              "tra_plan_bytes", "tra_plan", "tra_attn_plan"]:
         assert n in names
 
 
@@ -105,6 +106,32 @@ def test_staged_entry_point_argument_errors(lib):
     assert lib.tra_attn(FAKE, FAKE, FAKE, 4, 16, 16, 2, 128, 64, FAKE, None, 5, FAKE, None) == EINVAL
     assert lib.tra_attn(FAKE, FAKE, FAKE, 4, 16, 16, 2, 128, 64, FAKE, FAKE, 0, FAKE, None) == EINVAL
     assert lib.tra_attn(FAKE, FAKE, FAKE, 4, 16, 16, 2, 64, 64, None, None, 0, None, None) == EINVAL
+
+
+def test_plan_bytes_closed_form(lib):
+    def up(x):
+        return (x + 255) // 256 * 256
+
+    for (T, H, W, heads, maxcnt) in [(21, 30, 52, 12, 476), (8, 8, 8, 1, 7), (3, 20, 28, 2, 1)]:
+        nby, nbx = -(-H // 8), -(-W // 8)
+        items = heads * T * ((nby + 1) // 2) * nbx
+        slots = -(-items // 8) * 8
+        stride = -(-(2 * maxcnt) // 64) * 64
+        want = up(4 * slots) + up(4 * slots) + up(4 * slots * stride)
+        assert tra.tra_plan_bytes(T, H, W, heads, 64, maxcnt) == want
+
+
+def test_plan_argument_errors(lib):
+    assert lib.tra_plan_bytes(4, 16, 16, 2, 64, 0) == EINVAL
+    assert lib.tra_plan_bytes(4, 16, 16, 2, 64, (1 << 30) + 1) == EINVAL
+    assert lib.tra_plan_bytes(4, 16, 16, 2, 16, 5) == EUNSUP
+    assert lib.tra_plan_bytes(21, 30, 52, 12, 64, 1 << 30) == EUNSUP  # > 2^44 bytes
+    assert lib.tra_plan(FAKE, FAKE, 5, 4, 16, 16, 2, 64, None, None) == EINVAL
+    assert lib.tra_plan(None, FAKE, 5, 4, 16, 16, 2, 64, FAKE, None) == EINVAL
+    assert lib.tra_plan(FAKE, FAKE, 0, 4, 16, 16, 2, 64, FAKE, None) == EINVAL
+    assert lib.tra_attn_plan(FAKE, FAKE, FAKE, 4, 16, 16, 2, 128, 64, None, 5, FAKE, None) == EINVAL
+    assert lib.tra_attn_plan(FAKE, FAKE, FAKE, 4, 16, 16, 2, 80, 64, FAKE, 5, FAKE, None) == EUNSUP
+    assert lib.tra_attn_plan(FAKE, FAKE, FAKE, 4, 16, 16, 2, 128, 64, FAKE, 0, FAKE, None) == EINVAL
 
 
 def test_profile_switch_without_launches(lib):

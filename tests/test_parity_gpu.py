@@ -293,6 +293,56 @@ def test_list_walk_cases():
         assert_close(out[0, blocks[b]], ref, f"walk block {b} ({len(lists[b])} entries)")
 
 
+def test_plan_reuse_across_steps():
+    # Cross-step reuse: lists decided once (probe + mask on the first step's q, k),
+    # turned into a walk plan once, then attention of later steps' q, k, v along
+    # the stored plan.  Each step must equal tra_attn with the same lists
+    # bit for bit, and the oracle with the same radii within tolerance.
+    T, H, W, heads, d = 4, 24, 40, 2, 128
+    shp = (heads, T, H, W, d)
+    print(f"[case] plan reuse {shp}", flush=True)
+    r_min, r_max = 0, 3
+    q0, k0, _ = ti.make_inputs(T, H, W, heads, d, seed=3, cfg=31)
+    hn, radii = gpu_probe(dev16(q0), dev16(k0), shp, r_min, r_max)
+    idx, cnt, maxcnt = gpu_mask(radii, shp, r_max)
+    plan = torch.empty(tra.tra_plan_bytes(T, H, W, heads, 64, maxcnt), dtype=torch.uint8,
+                       device="cuda")
+    tra.tra_plan(idx, cnt, maxcnt, T, H, W, heads, 64, plan)
+    for step in range(2):
+        q, k, v = ti.make_inputs(T, H, W, heads, d, seed=40 + step, cfg=31)
+        qd, kd, vd = dev16(q), dev16(k), dev16(v)
+        out = torch.full(shp, float("nan"), dtype=torch.float32, device="cuda")
+        tra.tra_attn_plan(qd, kd, vd, T, H, W, heads, d, 64, plan, maxcnt, out)
+        ref_gpu = gpu_attn(qd, kd, vd, shp, idx, cnt, maxcnt)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_gpu), f"step {step}: planned walk differs from tra_attn"
+        rows = sample_rows(shp, 600, seed=step)
+        ref = oracle.attention_rows(q, k, v, radii, rows)
+        assert_close(out.cpu().numpy().reshape(-1, d)[rows], ref, f"plan reuse step {step}")
+
+
+def test_binary_routing():
+    # HetA-style routing: every block either local (radius 1) or dense (radius
+    # infinite) from a supplied difficulty map; the mask with r_max infinite
+    # gives full lists for the dense blocks (lists of 27 vs nb entries).
+    T, H, W, heads, d = 6, 32, 48, 2, 128
+    shp = (heads, T, H, W, d)
+    print(f"[case] binary routing {shp}", flush=True)
+    q, k, v = ti.make_inputs(T, H, W, heads, d, seed=5, cfg=32)
+    nb = tra.tra_grid(T, H, W)[2]
+    rng = np.random.default_rng(17)
+    radii = np.where(rng.random((heads, nb)) < 0.2, INF, 1).astype(np.int32)
+    idx, cnt, maxcnt = gpu_mask(radii, shp, INF)
+    assert maxcnt == nb
+    check_lists(idx, cnt, radii, shp, maxcnt, "binary routing lists")
+    c = cnt.cpu().numpy()
+    assert (c[radii == INF] == nb).all()
+    out = gpu_attn(dev16(q), dev16(k), dev16(v), shp, idx, cnt, maxcnt).cpu().numpy()
+    rows = sample_rows(shp, 800, seed=4)
+    ref = oracle.attention_rows(q, k, v, radii, rows)
+    assert_close(out.reshape(-1, d)[rows], ref, "binary routing attention")
+
+
 def test_mask_clamps_radius_to_r_max():
     T, H, W, heads = 6, 24, 40, 1
     shp = (heads, T, H, W, 64)

@@ -61,6 +61,15 @@ def _load():
         lib.orc_attention_rows.restype = I
         lib.orc_attention.argtypes = [P, P, P, I, I, I, I, I, I, P, P]
         lib.orc_attention.restype = I
+        D = ctypes.c_double
+        lib.orc_token_entropy_rows.argtypes = [P, P, I, I, I, I, I, I, L, P, P]
+        lib.orc_token_entropy_rows.restype = I
+        lib.orc_token_radius.argtypes = [P, I, I, I, I, D, D, P]
+        lib.orc_token_radius.restype = I
+        lib.orc_token_lists.argtypes = [P, I, I, I, I, I, D, I, D, L, P, L, P, P]
+        lib.orc_token_lists.restype = I
+        lib.orc_attention_lists_rows.argtypes = [P, P, P, I, I, I, I, I, I, P, P, L, L, P, P]
+        lib.orc_attention_lists_rows.restype = I
         lib.orc_num_threads.argtypes = []
         lib.orc_num_threads.restype = I
         _lib = lib
@@ -166,3 +175,67 @@ def attention_rows(q, k, v, radii, rows, block: int = 64) -> np.ndarray:
 
 def dense_radii(heads: int, nb: int) -> np.ndarray:
     return np.full((heads, nb), RADIUS_INF, dtype=np.int32)
+
+
+# ---------------------------------------------- token-level radius policy --
+
+def token_entropy_rows(q, k, rows, block: int = 64) -> np.ndarray:
+    """Entropy of the dense attention row of each ``head * N + token`` row, fp64."""
+    q, k = _u16(q), _u16(k)
+    heads, T, H, W, d = _dims(q)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    ent = np.empty(rows.size, dtype=np.float64)
+    _check(_load().orc_token_entropy_rows(_ptr(q), _ptr(k), T, H, W, heads, d, block, rows.size,
+                                          _ptr(rows), _ptr(ent)), "token_entropy_rows")
+    return ent
+
+
+def token_entropy(q, k, block: int = 64) -> np.ndarray:
+    """Entropy of every token's dense attention row, fp64 ``[heads][T][H][W]``."""
+    heads, T, H, W, d = _dims(q)
+    ent = token_entropy_rows(q, k, np.arange(heads * T * H * W), block)
+    return ent.reshape(heads, T, H, W)
+
+
+def token_radius(ent, tau: float, gamma: float) -> np.ndarray:
+    """Base radius of every token from its entropy ``[heads][T][H][W]``, fp64."""
+    ent = np.ascontiguousarray(ent, dtype=np.float64)
+    heads, T, H, W = ent.shape
+    r0 = np.empty_like(ent)
+    _check(_load().orc_token_radius(_ptr(ent), T, H, W, heads, float(tau), float(gamma), _ptr(r0)),
+           "token_radius")
+    return r0
+
+
+def token_lists(r0, gamma: float, min_votes: int = 1, block: int = 64, rows=None,
+                r2_scale: float = 1.0, maxcnt: int | None = None):
+    """Voting lists of the ``head * nb + query block`` rows (all by default):
+    (idx int32 ``[rows][maxcnt]`` with -1 past cnt, cnt int32 ``[rows]``)."""
+    r0 = np.ascontiguousarray(r0, dtype=np.float64)
+    heads, T, H, W = r0.shape
+    nb = grid_blocks(T, H, W, block)[2]
+    rows = np.arange(heads * nb) if rows is None else rows
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    maxcnt = nb if maxcnt is None else maxcnt
+    idx = np.full((rows.size, maxcnt), -1, dtype=np.int32)
+    cnt = np.empty(rows.size, dtype=np.int32)
+    _check(_load().orc_token_lists(_ptr(r0), T, H, W, heads, block, float(gamma), int(min_votes),
+                                   float(r2_scale), rows.size, _ptr(rows), maxcnt, _ptr(idx),
+                                   _ptr(cnt)), "token_lists")
+    return idx, cnt
+
+
+def attention_lists_rows(q, k, v, idx, cnt, rows, block: int = 64) -> np.ndarray:
+    """Softmax attention of the ``head * N + token`` rows over explicit key-block
+    lists ``idx[heads][nb][maxcnt]``, ``cnt[heads][nb]``; fp64 ``[len(rows)][d]``."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    heads, T, H, W, d = _dims(q)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    cnt = np.ascontiguousarray(cnt, dtype=np.int32)
+    maxcnt = idx.shape[-1]
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((rows.size, d), dtype=np.float64)
+    _check(_load().orc_attention_lists_rows(_ptr(q), _ptr(k), _ptr(v), T, H, W, heads, d, block,
+                                            _ptr(idx), _ptr(cnt), maxcnt, rows.size, _ptr(rows),
+                                            _ptr(out)), "attention_lists_rows")
+    return out

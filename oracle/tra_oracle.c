@@ -352,4 +352,232 @@ int orc_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     return rc;
 }
 
+/*
+ * Token-level radius policy (Token Radius Attention for Efficient Video
+ * Generation, "Insight I", "Insight II" and "The TRA Pipeline":
+ * Entropy-to-Budget, Budget-to-Radius, Fused CUDA Kernels), per head:
+ *
+ *   entropy     H_i = -sum_j p_ij ln p_ij with p_i = softmax_j(q_i . k_j / sqrt(d))
+ *               over every real key token j: the entropy of query i's dense
+ *               attention row (the warm-up step).
+ *   budget      b_i = tau exp(H_i) keys, clamped to [1, N]: exp(H_i) is the
+ *               row's effective number of keys, and b_i / N the retained
+ *               fraction the page writes as tau exp(H_i) / N.
+ *   radius      base radius r0_i with sum_{t'} pi (r0_i phi(|t' - t_i|))^2 = b_i
+ *               over the T frames, phi(delta) = exp(-gamma delta):
+ *               r0_i = sqrt(b_i / (pi S(t_i))), S(t) = sum_{t'} exp(-2 gamma |t' - t|).
+ *   support     key token j is in query i's support iff
+ *               (y_j - y_i)^2 + (x_j - x_i)^2 <= (r0_i phi(|t_j - t_i|))^2:
+ *               a disk in every frame, shrinking with temporal distance.
+ *   voting      key block K is kept for query block Q iff at least min_votes
+ *               real query tokens of Q have a real key token of K in their
+ *               support; lists ascending.
+ *   attention   exact softmax attention of each query over every real key
+ *               token of the blocks in its block's list.
+ */
+
+/* Entropy of the dense attention row of each selected query row (head * N + token). */
+int orc_token_entropy_rows(const uint16_t *q, const uint16_t *k, int T, int H, int W, int heads,
+                           int d, int block, long nrows, const int64_t *rows, double *ent)
+{
+    orc_grid g;
+    if (!q || !k || !rows || !ent || heads < 1 || d < 1 || nrows < 0) return ORC_EINVAL;
+    if (orc_grid_make(&g, T, H, W, block)) return ORC_EINVAL;
+    for (long n = 0; n < nrows; ++n)
+        if (rows[n] < 0 || rows[n] >= (int64_t)heads * g.N) return ORC_EINVAL;
+    orc_init_lut();
+    const double inv_sqrt_d = 1.0 / sqrt((double)d);
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)g.N);
+        double *qi = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!s || !qi) {
+#pragma omp atomic write
+            fail = 1;
+        }
+#pragma omp for schedule(dynamic, 4)
+        for (long n = 0; n < nrows; ++n) {
+            if (!s || !qi) continue;
+            int h = (int)(rows[n] / g.N);
+            long i = rows[n] % g.N;
+            const uint16_t *qh = q + (size_t)h * g.N * d;
+            const uint16_t *kh = k + (size_t)h * g.N * d;
+            for (int c = 0; c < d; ++c) qi[c] = orc_lut[qh[i * d + c]];
+            double m = -INFINITY;
+            for (long j = 0; j < g.N; ++j) {
+                double dot = 0.0;
+                for (int c = 0; c < d; ++c) dot += qi[c] * orc_lut[kh[j * d + c]];
+                s[j] = dot * inv_sqrt_d;
+                if (s[j] > m) m = s[j];
+            }
+            double Z = 0.0;
+            for (long j = 0; j < g.N; ++j) Z += exp(s[j] - m);
+            double Hi = 0.0;
+            for (long j = 0; j < g.N; ++j) {
+                double p = exp(s[j] - m) / Z;
+                if (p > 0.0) Hi -= p * log(p);
+            }
+            ent[n] = Hi;
+        }
+        free(s); free(qi);
+    }
+    return fail ? ORC_ENOMEM : ORC_OK;
+}
+
+/* Base radius of every token from its entropy: ent, r0 are [heads][N]. */
+int orc_token_radius(const double *ent, int T, int H, int W, int heads, double tau,
+                     double gamma, double *r0)
+{
+    if (!ent || !r0 || T < 1 || H < 1 || W < 1 || heads < 1 || !(tau > 0.0) || !(gamma >= 0.0))
+        return ORC_EINVAL;
+    const long N = (long)T * H * W;
+    const double pi = 3.14159265358979323846;
+    for (int h = 0; h < heads; ++h)
+        for (long i = 0; i < N; ++i) {
+            int ti = (int)(i / ((long)H * W));
+            double S = 0.0;
+            for (int t = 0; t < T; ++t) S += exp(-2.0 * gamma * (double)orc_labs((long)t - ti));
+            double b = tau * exp(ent[(size_t)h * N + i]);
+            if (b < 1.0) b = 1.0;
+            if (b > (double)N) b = (double)N;
+            r0[(size_t)h * N + i] = sqrt(b / (pi * S));
+        }
+    return ORC_OK;
+}
+
+/*
+ * Voting lists for the selected (head * nb + query block) rows, by the
+ * definition: every real query token of the block against every real key token
+ * of every key block.  r0 is [heads][N]; the support test uses the squared
+ * radius times r2_scale (1 for the definition; 1 -+ eps brackets rounding).
+ * idx[nrows][maxcnt] (first cnt entries written), cnt[nrows].
+ */
+int orc_token_lists(const double *r0, int T, int H, int W, int heads, int block, double gamma,
+                    int min_votes, double r2_scale, long nrows, const int64_t *rows, long maxcnt,
+                    int32_t *idx, int32_t *cnt)
+{
+    orc_grid g;
+    if (!r0 || !rows || !idx || !cnt || heads < 1 || maxcnt < 1 || min_votes < 1) return ORC_EINVAL;
+    if (orc_grid_make(&g, T, H, W, block) || !(gamma >= 0.0)) return ORC_EINVAL;
+    for (long n = 0; n < nrows; ++n)
+        if (rows[n] < 0 || rows[n] >= (int64_t)heads * g.nb) return ORC_EINVAL;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long n = 0; n < nrows; ++n) {
+        int h = (int)(rows[n] / g.nb);
+        long qb = rows[n] % g.nb;
+        int tq = (int)(qb / ((long)g.nby * g.nbx));
+        int byq = (int)((qb / g.nbx) % g.nby), bxq = (int)(qb % g.nbx);
+        long c = 0;
+        for (long kb = 0; kb < g.nb; ++kb) {
+            int tk = (int)(kb / ((long)g.nby * g.nbx));
+            int byk = (int)((kb / g.nbx) % g.nby), bxk = (int)(kb % g.nbx);
+            double phi = exp(-gamma * (double)orc_labs((long)tk - tq));
+            int votes = 0;
+            for (int yi = byq * g.s; yi < (byq + 1) * g.s && yi < H; ++yi)
+                for (int xi = bxq * g.s; xi < (bxq + 1) * g.s && xi < W; ++xi) {
+                    double r = r0[(size_t)h * g.N + ((long)tq * H + yi) * W + xi] * phi;
+                    double r2 = r * r * r2_scale;
+                    int hit = 0;
+                    for (int yj = byk * g.s; yj < (byk + 1) * g.s && yj < H && !hit; ++yj)
+                        for (int xj = bxk * g.s; xj < (bxk + 1) * g.s && xj < W && !hit; ++xj) {
+                            double dy = (double)(yj - yi), dx = (double)(xj - xi);
+                            if (dy * dy + dx * dx <= r2) hit = 1;
+                        }
+                    votes += hit;
+                }
+            if (votes >= min_votes) {
+                if (c >= maxcnt) {
+#pragma omp atomic write
+                    bad = 1;
+                    break;
+                }
+                idx[(size_t)n * maxcnt + c++] = (int32_t)kb;
+            }
+        }
+        cnt[n] = (int32_t)c;
+    }
+    return bad ? ORC_EINVAL : ORC_OK;
+}
+
+/*
+ * Softmax attention of selected rows over explicit key-block lists:
+ * idx[heads][nb][maxcnt], cnt[heads][nb]; entries outside [0, nb) are skipped,
+ * every other entry adds all real tokens of its block once more (a duplicate
+ * counts twice); an empty row gives zeros.  out[nrows][d] fp64.
+ */
+int orc_attention_lists_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                             int T, int H, int W, int heads, int d, int block,
+                             const int32_t *idx, const int32_t *cnt, long maxcnt,
+                             long nrows, const int64_t *rows, double *out)
+{
+    orc_grid g;
+    if (!q || !k || !v || !idx || !cnt || !rows || !out || heads < 1 || d < 1 || maxcnt < 1)
+        return ORC_EINVAL;
+    if (orc_grid_make(&g, T, H, W, block)) return ORC_EINVAL;
+    for (long n = 0; n < nrows; ++n)
+        if (rows[n] < 0 || rows[n] >= (int64_t)heads * g.N) return ORC_EINVAL;
+    orc_init_lut();
+    const double inv_sqrt_d = 1.0 / sqrt((double)d);
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *qi = (double *)malloc(sizeof(double) * (size_t)d);
+        double *acc = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!qi || !acc) {
+#pragma omp atomic write
+            fail = 1;
+        }
+#pragma omp for schedule(dynamic, 4)
+        for (long n = 0; n < nrows; ++n) {
+            if (!qi || !acc) continue;
+            int h = (int)(rows[n] / g.N);
+            long i = rows[n] % g.N;
+            int ti = (int)(i / ((long)H * W)), yi = (int)((i / W) % H), xi = (int)(i % W);
+            long bi = ((long)ti * g.nby + yi / g.s) * g.nbx + xi / g.s;
+            const uint16_t *qh = q + (size_t)h * g.N * d;
+            const uint16_t *kh = k + (size_t)h * g.N * d;
+            const uint16_t *vh = v + (size_t)h * g.N * d;
+            for (int c = 0; c < d; ++c) qi[c] = orc_lut[qh[i * d + c]];
+            long m_ = cnt[(size_t)h * g.nb + bi];
+            if (m_ < 0) m_ = 0;
+            if (m_ > maxcnt) m_ = maxcnt;
+            const int32_t *row = idx + ((size_t)h * g.nb + bi) * maxcnt;
+            /* two passes over the listed keys: max, then weights */
+            double m = -INFINITY;
+            for (int pass = 0; pass < 2; ++pass) {
+                double Z = 0.0;
+                for (int c = 0; c < d; ++c) acc[c] = 0.0;
+                for (long e = 0; e < m_; ++e) {
+                    long kb = row[e];
+                    if (kb < 0 || kb >= g.nb) continue;
+                    int tk = (int)(kb / ((long)g.nby * g.nbx));
+                    int byk = (int)((kb / g.nbx) % g.nby), bxk = (int)(kb % g.nbx);
+                    for (int yj = byk * g.s; yj < (byk + 1) * g.s && yj < H; ++yj)
+                        for (int xj = bxk * g.s; xj < (bxk + 1) * g.s && xj < W; ++xj) {
+                            long j = ((long)tk * H + yj) * W + xj;
+                            double dot = 0.0;
+                            for (int c = 0; c < d; ++c) dot += qi[c] * orc_lut[kh[(size_t)j * d + c]];
+                            double sj = dot * inv_sqrt_d;
+                            if (pass == 0) {
+                                if (sj > m) m = sj;
+                            } else {
+                                double w = exp(sj - m);
+                                Z += w;
+                                for (int c = 0; c < d; ++c) acc[c] += w * orc_lut[vh[(size_t)j * d + c]];
+                            }
+                        }
+                }
+                if (pass == 1) {
+                    double *o = out + (size_t)n * d;
+                    for (int c = 0; c < d; ++c) o[c] = Z > 0.0 ? acc[c] / Z : 0.0;
+                }
+            }
+        }
+        free(qi); free(acc);
+    }
+    return fail ? ORC_ENOMEM : ORC_OK;
+}
+
 int orc_num_threads(void) { return omp_get_max_threads(); }

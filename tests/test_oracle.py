@@ -302,3 +302,179 @@ def test_attention_rows_agree_with_full():
     full = oracle.attention(q, k, v, radii).reshape(heads * T * H * W, d)
     rows = np.array([0, 5, 77, 269, 270, 539])
     np.testing.assert_array_equal(oracle.attention_rows(q, k, v, radii, rows), full[rows])
+
+
+# ------------------------------------------------ token-level radius policy --
+
+def test_token_entropy_matches_scipy():
+    T, H, W, heads, d = 2, 8, 12, 2, 16
+    q, k, _ = ti.random_qkv(T, H, W, heads, d, seed=21, scale=2.0)
+    got = oracle.token_entropy(q, k).reshape(heads, -1)
+    qf, kf = f64(q).reshape(heads, -1, d), f64(k).reshape(heads, -1, d)
+    for h in range(heads):
+        p = scipy.special.softmax(qf[h] @ kf[h].T / math.sqrt(d), axis=1)
+        np.testing.assert_allclose(got[h], scipy.stats.entropy(p, axis=1), rtol=1e-12, atol=1e-12)
+
+
+def test_token_entropy_closed_forms():
+    T, H, W, heads, d = 2, 5, 7, 1, 16
+    N = T * H * W
+    q, _, _ = ti.random_qkv(T, H, W, heads, d, seed=22)
+    k0 = np.zeros_like(q)  # every logit 0: uniform rows
+    np.testing.assert_allclose(oracle.token_entropy(q, k0), math.log(N), rtol=1e-13)
+    # one dominant key: a logit of 100 * 100 / 4 against zeros -> a one-hot row
+    big = int(ti.bf16_from_f32(np.array([100.0], dtype=np.float32))[0])
+    qb = np.zeros_like(q)
+    qb[..., 0] = big
+    kb = np.zeros_like(q)
+    kb[0, 1, 2, 3, 0] = big
+    assert np.abs(oracle.token_entropy(qb, kb)).max() < 1e-12
+
+
+def test_token_radius_closed_forms():
+    rng = np.random.default_rng(3)
+    T, H, W, heads = 5, 4, 6, 2
+    N = T * H * W
+    ent = rng.uniform(0.0, math.log(N), size=(heads, T, H, W))
+    tau = 0.7
+    b = np.clip(tau * np.exp(ent), 1.0, N)
+    # no temporal decay: the disk has the same area in all T frames
+    np.testing.assert_allclose(oracle.token_radius(ent, tau, 0.0), np.sqrt(b / (math.pi * T)),
+                               rtol=1e-14)
+    # with decay, the disks' areas over the frames add up to the budget
+    gamma = 0.35
+    r0 = oracle.token_radius(ent, tau, gamma)
+    t = np.arange(T)
+    for ti_ in range(T):
+        area = (math.pi * (r0[:, ti_][..., None] * np.exp(-gamma * np.abs(t - ti_))) ** 2).sum(-1)
+        np.testing.assert_allclose(area, b[:, ti_], rtol=1e-12)
+    # budget clamps: at least one key, at most all N
+    one = oracle.token_radius(np.zeros((1, 1, 3, 3)), 1e-9, 0.0)
+    np.testing.assert_allclose(one, math.sqrt(1.0 / math.pi), rtol=1e-14)
+    alln = oracle.token_radius(np.full((1, 1, 3, 3), 50.0), 1.0, 0.0)
+    np.testing.assert_allclose(alln, math.sqrt(9.0 / math.pi), rtol=1e-14)
+
+
+def lists_of(idx, cnt):
+    return [idx[n, :cnt[n]].tolist() for n in range(len(cnt))]
+
+
+def test_token_lists_geometry_by_hand():
+    # two tiles side by side (x 0..7 | 8..15): the closest tokens are 1 apart
+    r = np.full((1, 1, 8, 16), 1.0)
+    assert lists_of(*oracle.token_lists(r, 0.0)) == [[0, 1], [0, 1]]
+    assert lists_of(*oracle.token_lists(r * 0.99, 0.0)) == [[0], [1]]
+    # one token of the left tile reaches across: one vote
+    r = np.full((1, 1, 8, 16), 0.1)
+    r[0, 0, 3, 7] = 1.0
+    assert lists_of(*oracle.token_lists(r, 0.0, min_votes=1)) == [[0, 1], [1]]
+    assert lists_of(*oracle.token_lists(r, 0.0, min_votes=2)) == [[0], [1]]
+    # 2 x 2 tiles: the diagonal tile is sqrt(2) away (Euclidean, not Chebyshev)
+    r = np.full((1, 1, 16, 16), 1.0)
+    assert lists_of(*oracle.token_lists(r, 0.0))[0] == [0, 1, 2]
+    assert lists_of(*oracle.token_lists(r * 1.42, 0.0))[0] == [0, 1, 2, 3]
+    assert lists_of(*oracle.token_lists(r * 1.41, 0.0))[0] == [0, 1, 2]
+
+
+def test_token_lists_decay_and_query_frame_radius():
+    # two tiles side by side per frame, 3 frames: radius 1 reaches the
+    # neighbouring tile in its own frame; decayed to exp(-0.1) < 1 it does not
+    # in the next frames (the co-located tiles stay)
+    r = np.full((1, 3, 8, 16), 1.0)
+    lists = lists_of(*oracle.token_lists(r, 0.1))
+    assert lists[2] == [0, 2, 3, 4]
+    assert lists[0] == [0, 1, 2, 4]
+    assert lists_of(*oracle.token_lists(r, 0.0))[2] == [0, 1, 2, 3, 4, 5]
+    # the radius is the query token's, whatever frame the key lies in
+    r = np.full((1, 2, 8, 16), 0.1)
+    r[0, 0] = 1.0
+    lists = lists_of(*oracle.token_lists(r, 0.0))
+    assert lists[0] == [0, 1, 2, 3]
+    assert lists[2] == [0, 2]
+
+
+def test_token_lists_temporal_reach_and_extremes():
+    # one tile per frame: a shrinking disk still holds the co-located token, so
+    # every frame's tile is kept however small the radius or fast the decay
+    r = np.full((1, 3, 8, 8), 0.01)
+    for gamma in (0.0, 5.0):
+        assert lists_of(*oracle.token_lists(r, gamma)) == [[0, 1, 2]] * 3
+    # tiny radii on a larger grid: exactly the co-located tile of each frame
+    T, H, W = 3, 16, 24
+    idx, cnt = oracle.token_lists(np.full((1, T, H, W), 0.3), 1.0)
+    nb = oracle.grid_blocks(T, H, W)[2]
+    per = nb // T
+    assert (cnt == T).all()
+    assert lists_of(idx, cnt)[4] == [4 % per + per * t for t in range(T)]
+    # huge radii without decay: everything
+    idx, cnt = oracle.token_lists(np.full((1, T, H, W), 100.0), 0.0)
+    assert (cnt == nb).all()
+    # votes needed beyond the real tokens of a partial tile: nothing kept
+    idx, cnt = oracle.token_lists(np.full((1, 1, 5, 8), 100.0), 0.0, min_votes=41)
+    assert (cnt == 0).all()
+    idx, cnt = oracle.token_lists(np.full((1, 1, 5, 8), 100.0), 0.0, min_votes=40)
+    assert (cnt == 1).all()
+
+
+def test_token_lists_symmetric_and_monotone():
+    rng = np.random.default_rng(8)
+    T, H, W = 3, 16, 16
+    nb = oracle.grid_blocks(T, H, W)[2]
+    r = np.full((1, T, H, W), 6.5)
+    idx, cnt = oracle.token_lists(r, 0.4)
+    keep = np.zeros((nb, nb), dtype=bool)
+    for q_, l in enumerate(lists_of(idx, cnt)):
+        keep[q_, l] = True
+    assert (keep == keep.T).all() and keep.diagonal().all()
+    r = rng.uniform(0.5, 9.0, size=(2, T, H, W))
+    small = lists_of(*oracle.token_lists(r, 0.3, r2_scale=0.9))
+    big = lists_of(*oracle.token_lists(r, 0.3, r2_scale=1.1))
+    assert all(set(a) <= set(b) for a, b in zip(small, big))
+
+
+def block_key_mask(T, H, W, lists):
+    """N x N mask: key j kept for query i iff block(j) is in block(i)'s list."""
+    ids, _ = tile_membership(T, H, W)
+    nb = ids.max() + 1
+    keep = np.zeros((nb, nb), dtype=bool)
+    for b, l in enumerate(lists):
+        keep[b, l] = True
+    return keep[ids][:, ids]
+
+
+def test_attention_lists_vs_masked_sdpa():
+    T, H, W, heads, d = 2, 12, 16, 1, 8
+    q, k, v = ti.random_qkv(T, H, W, heads, d, seed=24)
+    nb = oracle.grid_blocks(T, H, W)[2]
+    rng = np.random.default_rng(5)
+    lists = [sorted(set([b] + rng.choice(nb, size=rng.integers(0, nb), replace=False).tolist()))
+             for b in range(nb)]
+    maxcnt = nb
+    idx = np.full((1, nb, maxcnt), -1, dtype=np.int32)
+    cnt = np.zeros((1, nb), dtype=np.int32)
+    for b, l in enumerate(lists):
+        idx[0, b, :len(l)] = l
+        cnt[0, b] = len(l)
+    rows = np.arange(T * H * W)
+    got = oracle.attention_lists_rows(q, k, v, idx, cnt, rows)
+    mask = block_key_mask(T, H, W, lists)
+    ref = sdpa(f64(q).reshape(1, -1, d), f64(k).reshape(1, -1, d), f64(v).reshape(1, -1, d), mask)[0]
+    np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-12)
+    # every entry twice: uniform doubling of the weights leaves the softmax unchanged
+    idx2 = np.full((1, nb, 2 * maxcnt), -1, dtype=np.int32)
+    for b, l in enumerate(lists):
+        idx2[0, b, :2 * len(l)] = l + l
+    got2 = oracle.attention_lists_rows(q, k, v, idx2, 2 * cnt, rows)
+    np.testing.assert_allclose(got2, got, rtol=1e-12, atol=1e-13)
+    # an empty list gives zeros; entries outside [0, nb) are skipped
+    cnt0 = cnt.copy()
+    cnt0[0, 0] = 0
+    z = oracle.attention_lists_rows(q, k, v, idx, cnt0, rows)
+    ids, _ = tile_membership(T, H, W)
+    assert (z[ids == 0] == 0).all()
+    cnt3 = np.full_like(cnt, maxcnt)
+    idx3 = np.where(np.arange(maxcnt) % 2 == 0, -5, nb + 3).astype(np.int32)[None, None, :].repeat(nb, 1)
+    for b, l in enumerate(lists):
+        idx3[0, b, :len(l)] = l
+    np.testing.assert_allclose(oracle.attention_lists_rows(q, k, v, idx3, cnt3, rows), got,
+                               rtol=1e-12, atol=1e-13)

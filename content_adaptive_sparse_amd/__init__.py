@@ -18,12 +18,14 @@ from .build import LIB_PATH
 __all__ = [
     "TRA_RADIUS_INF", "TraError", "library", "tra_attention", "tra_probe", "tra_mask",
     "tra_attn", "tra_grid", "tra_maxcnt", "tra_status_string", "tra_version",
-    "tra_plan_bytes", "tra_plan", "tra_attn_plan",
+    "tra_plan_bytes", "tra_plan", "tra_attn_plan", "tra_token_probe", "tra_token_mask",
+    "tra_token_attention",
     "tra_profile_begin", "tra_profile_end", "KERNEL_KINDS",
 ]
 
 TRA_RADIUS_INF = 2147483647
-KERNEL_KINDS = ("pack_pool", "entropy", "mask", "attn", "fill", "order", "union")
+KERNEL_KINDS = ("pack_pool", "entropy", "mask", "attn", "fill", "order", "union",
+                "token_entropy", "token_mask")
 
 _lib = None
 
@@ -66,6 +68,13 @@ def library() -> ctypes.CDLL:
         lib.tra_plan.restype = I
         lib.tra_attn_plan.argtypes = [P, P, P, I, I, I, I, I, I, P, L, P, P]
         lib.tra_attn_plan.restype = I
+        F = ctypes.c_float
+        lib.tra_token_probe.argtypes = [P, P, I, I, I, I, I, I, F, F, P, P, P]
+        lib.tra_token_probe.restype = I
+        lib.tra_token_mask.argtypes = [P, I, I, I, I, I, F, I, P, P, P]
+        lib.tra_token_mask.restype = I
+        lib.tra_token_attention.argtypes = [P, P, P, I, I, I, I, I, I, F, F, I, P, P]
+        lib.tra_token_attention.restype = I
         lib.tra_profile_begin.argtypes = []
         lib.tra_profile_begin.restype = I
         lib.tra_profile_end.argtypes = [P, P, I]
@@ -187,6 +196,28 @@ def tra_attn_plan(q, k, v, T, H, W, heads, head_dim, block, plan, maxcnt, out, s
         _ptr(q, _bf16(), "q"), _ptr(k, _bf16(), "k"), _ptr(v, _bf16(), "v"), T, H, W, heads,
         head_dim, block, _ptr(plan, None, "plan"), int(maxcnt), _ptr(out, _f32(), "out"),
         _stream(stream)), "tra_attn_plan")
+
+
+def tra_token_probe(q, k, T, H, W, heads, head_dim, block, tau, gamma, entropy, r0,
+                    stream=None):
+    _check(library().tra_token_probe(
+        _ptr(q, _bf16(), "q"), _ptr(k, _bf16(), "k"), T, H, W, heads, head_dim, block, float(tau),
+        float(gamma), _ptr(entropy, _f32(), "entropy"), _ptr(r0, _f32(), "r0"), _stream(stream)),
+        "tra_token_probe")
+
+
+def tra_token_mask(r0, T, H, W, heads, block, gamma, min_votes, idx, cnt, stream=None):
+    _check(library().tra_token_mask(
+        _ptr(r0, _f32(), "r0"), T, H, W, heads, block, float(gamma), int(min_votes),
+        _ptr(idx, _i32(), "idx"), _ptr(cnt, _i32(), "cnt"), _stream(stream)), "tra_token_mask")
+
+
+def tra_token_attention(q, k, v, T, H, W, heads, head_dim, block, tau, gamma, min_votes, out,
+                        stream=None):
+    _check(library().tra_token_attention(
+        _ptr(q, _bf16(), "q"), _ptr(k, _bf16(), "k"), _ptr(v, _bf16(), "v"), T, H, W, heads,
+        head_dim, block, float(tau), float(gamma), int(min_votes), _ptr(out, _f32(), "out"),
+        _stream(stream)), "tra_token_attention")
 
 
 def tra_profile_begin():

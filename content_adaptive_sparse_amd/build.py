@@ -22,7 +22,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libtra_attention.so")
 
-SOURCES = ["tra_probe.hip", "tra_mask.hip", "tra_attn.hip", "tra_api.cpp"]
+SOURCES = ["tra_probe.hip", "tra_mask.hip", "tra_attn.hip", "tra_token.hip", "tra_api.cpp"]
 ARCH = "gfx950"
 
 

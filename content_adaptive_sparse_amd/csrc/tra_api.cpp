@@ -387,6 +387,107 @@ int tra_attn(const void *q, const void *k, const void *v, int T, int H, int W, i
     return attn_with_plan(q, k, v, g, heads, head_dim, plan, L, out, stream);
 }
 
+static int check_token_params(float tau, float gamma) {
+    if (!(tau > 0.f) || !isfinite(tau) || !(gamma >= 0.f) || !isfinite(gamma))
+        return TRA_ERR_INVALID_ARG;
+    return TRA_OK;
+}
+
+int tra_token_probe(const void *q, const void *k, int T, int H, int W, int heads, int head_dim,
+                    int block, float tau, float gamma, float *entropy, float *r0,
+                    hipStream_t stream) {
+    tra::Grid g;
+    int rc = make_grid(T, H, W, block, &g);
+    if (rc == TRA_OK) rc = check_dims(heads, head_dim, g);
+    if (rc == TRA_OK) rc = check_token_params(tau, gamma);
+    if (rc != TRA_OK) return rc;
+    if (!q || !k || !r0) return TRA_ERR_INVALID_ARG;
+    Scratch ws(stream);
+    const size_t tiles = (size_t)heads * g.nb * tra::packed_tile_elems(head_dim) * 2;
+    const size_t o_kt = ws.reserve(tiles);
+    const size_t o_ent = entropy ? 0 : ws.reserve((size_t)heads * T * H * W * sizeof(float));
+    if ((rc = ws.allocate()) != TRA_OK) return rc;
+    uint16_t *kt = ws.at<uint16_t>(o_kt);
+    float *ent = entropy ? entropy : ws.at<float>(o_ent);
+    hipError_t e;
+    {
+        ProfScope p(TRA_KERNEL_PACK_POOL, stream);
+        e = tra::launch_pack_k(head_dim, (const uint16_t *)k, g, heads, kt, stream);
+    }
+    if (e == hipSuccess) {
+        ProfScope p(TRA_KERNEL_TOKEN_ENTROPY, stream);
+        e = tra::launch_token_entropy(head_dim, (const uint16_t *)q, kt, g, heads, tau, gamma, ent,
+                                      r0, stream);
+    }
+    return hip_status(e);
+}
+
+int tra_token_mask(const float *r0, int T, int H, int W, int heads, int block, float gamma,
+                   int min_votes, int32_t *idx, int32_t *cnt, hipStream_t stream) {
+    tra::Grid g;
+    int rc = make_grid(T, H, W, block, &g);
+    if (rc == TRA_OK) rc = check_dims(heads, 64, g);
+    if (rc == TRA_OK) rc = check_token_params(1.f, gamma);
+    if (rc != TRA_OK) return rc;
+    if (!r0 || !idx || !cnt || min_votes < 1 || min_votes > tra::kBlockTokens)
+        return TRA_ERR_INVALID_ARG;
+    ProfScope p(TRA_KERNEL_TOKEN_MASK, stream);
+    return hip_status(tra::launch_token_mask(r0, g, heads, gamma, min_votes, g.nb, idx, cnt, stream));
+}
+
+int tra_token_attention(const void *q, const void *k, const void *v, int T, int H, int W,
+                        int heads, int head_dim, int block, float tau, float gamma,
+                        int min_votes, void *out, hipStream_t stream) {
+    tra::Grid g;
+    int rc = make_grid(T, H, W, block, &g);
+    if (rc == TRA_OK) rc = check_dims(heads, head_dim, g);
+    if (rc == TRA_OK) rc = check_token_params(tau, gamma);
+    if (rc == TRA_OK) rc = check_plan(g, heads, g.nb);
+    if (rc != TRA_OK) return rc;
+    if (!q || !k || !v || !out || min_votes < 1 || min_votes > tra::kBlockTokens)
+        return TRA_ERR_INVALID_ARG;
+    const size_t rows = (size_t)heads * g.nb;
+    const size_t toks = (size_t)heads * T * H * W;
+    const size_t tiles = rows * tra::packed_tile_elems(head_dim) * 2;
+    const PlanLayout L = plan_layout(g, heads, g.nb);
+    Scratch ws(stream);
+    const size_t o_kt = ws.reserve(tiles), o_vt = ws.reserve(tiles);
+    const size_t o_ent = ws.reserve(toks * sizeof(float)), o_r0 = ws.reserve(toks * sizeof(float));
+    const size_t o_idx = ws.reserve(rows * (size_t)g.nb * sizeof(int32_t));
+    const size_t o_cnt = ws.reserve(rows * sizeof(int32_t));
+    const size_t o_plan = ws.reserve(L.bytes);
+    if ((rc = ws.allocate()) != TRA_OK) return rc;
+    uint16_t *kt = ws.at<uint16_t>(o_kt), *vt = ws.at<uint16_t>(o_vt);
+    float *ent = ws.at<float>(o_ent), *r0 = ws.at<float>(o_r0);
+    int32_t *idx = ws.at<int32_t>(o_idx), *cnt = ws.at<int32_t>(o_cnt);
+    char *plan = ws.at<char>(o_plan);
+    hipError_t e;
+    {
+        ProfScope p(TRA_KERNEL_PACK_POOL, stream);
+        e = tra::launch_pack_pool(head_dim, false, true, nullptr, (const uint16_t *)k,
+                                  (const uint16_t *)v, g, heads, nullptr, nullptr, kt, vt, stream);
+    }
+    if (e == hipSuccess) {
+        ProfScope p(TRA_KERNEL_TOKEN_ENTROPY, stream);
+        e = tra::launch_token_entropy(head_dim, (const uint16_t *)q, kt, g, heads, tau, gamma, ent,
+                                      r0, stream);
+    }
+    if (e == hipSuccess) {
+        ProfScope p(TRA_KERNEL_TOKEN_MASK, stream);
+        e = tra::launch_token_mask(r0, g, heads, gamma, min_votes, g.nb, idx, cnt, stream);
+    }
+    if (e == hipSuccess)
+        e = plan_walk(idx, cnt, g.nb, g, heads, (int32_t *)(plan + L.o_ulist),
+                      (int32_t *)(plan + L.o_ulen), (int32_t *)(plan + L.o_order), stream);
+    if (e == hipSuccess) {
+        ProfScope p(TRA_KERNEL_ATTN, stream);
+        e = tra::launch_attn(head_dim, (const uint16_t *)q, kt, vt, (const int32_t *)(plan + L.o_ulist),
+                             (const int32_t *)(plan + L.o_ulen), L.ustride,
+                             (const int32_t *)(plan + L.o_order), g, heads, (float *)out, stream);
+    }
+    return hip_status(e);
+}
+
 int tra_attention(const void *q, const void *k, const void *v, int T, int H, int W, int heads,
                   int head_dim, int block, int r_min, int r_max, void *out, hipStream_t stream) {
     tra::Grid g;

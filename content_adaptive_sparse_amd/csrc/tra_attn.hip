@@ -21,65 +21,17 @@
 // exchange per tile and P feeds the second product without moving data.
 #include <math.h>
 
-#include "tra_internal.h"
+#include "tra_device.h"
 
 namespace tra {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
-template <typename T>
-__device__ __forceinline__ T lds_load16(const uint16_t *p) {
-    return *reinterpret_cast<const T *>(p);
-}
-
-// Exact n / d for 0 <= n < 2^24 and 1 <= d < 2^15 with m = ceil(2^39 / d):
-// the product's error term is below n / 2^39 < 1 / d, so the floor is exact.
-struct FastDiv {
-    uint64_t m;
-    uint32_t d;
-};
-__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
-    return (uint32_t)(((uint64_t)n * f.m) >> 39);
-}
-
-// Lanes l and l + 32 hold the same query: combine a value with the other
-// half's copy in registers (v_permlane32_swap: with the value in both
-// operands, the results are the lower-half and the upper-half copies).
-__device__ __forceinline__ float half_swap_max(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float half_swap_sum(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 constexpr int kAttnThreads = 256;
-// s_waitcnt immediates for gfx9 (vmcnt bits [3:0] and [15:14], expcnt [6:4],
-// lgkmcnt [11:8]); counters not waited on are left at their no-wait maxima.
-constexpr int wait_vmcnt(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
-constexpr int kWaitVmcnt0 = wait_vmcnt(0);
 // The running max is only moved (and O, l rescaled) when a tile's max exceeds
 // it by more than this many powers of two; in between, probabilities are
 // taken against the stale max (at most 2^8, exact in fp16) and the final
 // normalisation by l uses the same reference, so the result is unchanged.
 constexpr float kRescaleLog2 = 8.0f;
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void global_void_t;
-// The work order and union lengths are never written while the kernel runs;
-// reading them through the constant address space gives scalar loads.
-typedef __attribute__((address_space(4))) const int32_t const_i32_t;
-
-template <int N>
-struct SlotTag {
-    static constexpr int value = N;
-};
 
 template <int D>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
@@ -246,34 +198,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
                     sb[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], sb[hf], 0, 0, 0);
                 }
             }
-            // Keys of an edge tile beyond the grid: register r of half hf holds
-            // key row 4 hf + r / 4 and key column 4 hl + r % 4 of the tile.
             const uint32_t kb = (uint32_t)(e0 >> 2);
             const uint32_t row = fdiv(kb, div_nbx);
             const int kbx = (int)(kb - row * div_nbx.d);
             const int kby = (int)(row - fdiv(row, div_nby) * div_nby.d);
-            const int kny = min(kTileSide, g.H - kTileSide * kby);
-            const int knx = min(kTileSide, g.W - kTileSide * kbx);
-            if (knx < kTileSide) {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const bool bad = 4 * hl + c >= knx;
-#pragma unroll
-                    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-                        for (int rg = 0; rg < 4; ++rg)
-                            sb[hf][4 * rg + c] = bad ? -INFINITY : sb[hf][4 * rg + c];
-                }
-            }
-            if (kny < kTileSide) {
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-                    for (int rg = 0; rg < 4; ++rg)
-                        if (4 * hf + rg >= kny)
-#pragma unroll
-                            for (int c = 0; c < 4; ++c) sb[hf][4 * rg + c] = -INFINITY;
-            }
+            mask_edge_keys(sb, min(kTileSide, g.H - kTileSide * kby),
+                           min(kTileSide, g.W - kTileSide * kbx), hl, -INFINITY);
         }
         if constexpr (DP) {
             if (rescale) {
@@ -388,13 +318,7 @@ hipError_t launch_attn(int D, const uint16_t *q, const uint16_t *kt, const uint1
     const int per_xcd = (int)((total + 7) / 8);
     const dim3 grid((unsigned)(8 * (int64_t)per_xcd)), block(kAttnThreads);
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
-    auto magic = [](int d) {
-        FastDiv f;
-        f.d = (uint32_t)d;
-        f.m = (((uint64_t)1 << 39) + (uint64_t)d - 1) / (uint64_t)d;
-        return f;
-    };
-    const FastDiv div_nbx = magic(g.nbx), div_nby = magic(g.nby);
+    const FastDiv div_nbx = make_fastdiv(g.nbx), div_nby = make_fastdiv(g.nby);
     if (D == 128)
         hipLaunchKernelGGL(attn_kernel<128>, grid, block, 0, s, q, kt, vt, ulist, ulen, ustride,
                            order, g, heads, pph, per_xcd, div_nbx, div_nby, out, scale_log2);

@@ -43,6 +43,19 @@ hipError_t launch_fill_dense(const Grid &g, int heads, int32_t *radius, float *h
 hipError_t launch_mask(const int32_t *radius, const Grid &g, int heads, int r_max,
                        int64_t maxcnt, int32_t *idx, int32_t *cnt, hipStream_t s);
 
+// Packed K tiles only (the token-entropy warm-up reads no v).
+hipError_t launch_pack_k(int D, const uint16_t *k, const Grid &g, int heads, uint16_t *kt,
+                         hipStream_t s);
+
+// Token-level policy (tra_token.hip): entropy and base radius of every token
+// ([heads][T][H][W] fp32) from packed K; voting lists ([heads][nb][maxcnt]).
+hipError_t launch_token_entropy(int D, const uint16_t *q, const uint16_t *kt, const Grid &g,
+                                int heads, float tau, float gamma, float *ent, float *r0,
+                                hipStream_t s);
+hipError_t launch_token_mask(const float *r0, const Grid &g, int heads, float gamma,
+                             int min_votes, int64_t maxcnt, int32_t *idx, int32_t *cnt,
+                             hipStream_t s);
+
 // Attention work items are pairs of vertically adjacent query blocks: item p
 // of a head is frame t, tile-row pair pr, tile column bx, holding blocks
 // (t, 2 pr, bx) and (t, 2 pr + 1, bx) (the second is absent when nby is odd and

@@ -28,8 +28,9 @@ __device__ __forceinline__ int swap_bits23(int p) {
 }
 
 // One workgroup per (head, block).  256 threads; thread tid owns the 16-byte
-// chunk c = tid % (D/8) of rows w = tid / (D/8) + i * (256 / (D/8)).
-template <int D, bool POOL, bool PACK>
+// chunk c = tid % (D/8) of rows w = tid / (D/8) + i * (256 / (D/8)).  PACK
+// writes the packed K tile, PACKV also the packed V^T tile.
+template <int D, bool POOL, bool PACK, bool PACKV = PACK>
 __global__ __launch_bounds__(256) void pack_pool_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, Grid g, float *__restrict__ qp, float *__restrict__ kp,
@@ -42,7 +43,7 @@ __global__ __launch_bounds__(256) void pack_pool_kernel(
     constexpr int VPITCH = D + 8;  // fp16 elements per LDS row of the V tile
 
     __shared__ float red[POOL ? 2 : 1][POOL ? RG : 1][POOL ? D : 1];
-    __shared__ __attribute__((aligned(16))) uint16_t vs[PACK ? 64 : 1][PACK ? VPITCH : 1];
+    __shared__ __attribute__((aligned(16))) uint16_t vs[PACKV ? 64 : 1][PACKV ? VPITCH : 1];
 
     const int b = blockIdx.x;
     const int h = blockIdx.y;
@@ -73,7 +74,7 @@ __global__ __launch_bounds__(256) void pack_pool_kernel(
             const size_t off = tok * D + 8 * c;
             kk = *reinterpret_cast<const uint4 *>(k + off);
             if (POOL) qq = *reinterpret_cast<const uint4 *>(q + off);
-            if (PACK) vv = *reinterpret_cast<const uint4 *>(v + off);
+            if (PACKV) vv = *reinterpret_cast<const uint4 *>(v + off);
         }
         if (POOL) {
             const uint32_t qw[4] = {qq.x, qq.y, qq.z, qq.w};
@@ -91,6 +92,8 @@ __global__ __launch_bounds__(256) void pack_pool_kernel(
             const int piece = (w >> 5) * KS + (c >> 1);
             const int lane = 32 * (c & 1) + (w & 31);
             *reinterpret_cast<uint4 *>(kt + tile * 64 * D + (piece * 64 + lane) * 8) = kk;
+        }
+        if (PACKV) {
             const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
             uint32_t hw[4];
 #pragma unroll
@@ -122,7 +125,7 @@ __global__ __launch_bounds__(256) void pack_pool_kernel(
             (which ? kp : qp)[tile * D + dd] = s * inv_n;
         }
     }
-    if (PACK) {
+    if (PACKV) {
         // V^T fragment pieces (hf, mt, ks2): lane l holds row d = 32 mt + l % 32
         // at the eight keys 32 hf + swap_bits23(8 (2 ks2 + l / 32) + e).
         for (int o = tid; o < 2 * MT * 2 * 64; o += 256) {
@@ -290,6 +293,20 @@ hipError_t pack_pool_dispatch(bool pool, bool pack, const uint16_t *q, const uin
 }  // namespace
 
 size_t packed_tile_elems(int D) { return (size_t)kBlockTokens * D; }
+
+hipError_t launch_pack_k(int D, const uint16_t *k, const Grid &g, int heads, uint16_t *kt,
+                         hipStream_t s) {
+    const dim3 grid(g.nb, heads), block(256);
+    if (D == 128)
+        hipLaunchKernelGGL((pack_pool_kernel<128, false, true, false>), grid, block, 0, s, nullptr,
+                           k, nullptr, g, nullptr, nullptr, kt, nullptr);
+    else if (D == 64)
+        hipLaunchKernelGGL((pack_pool_kernel<64, false, true, false>), grid, block, 0, s, nullptr,
+                           k, nullptr, g, nullptr, nullptr, kt, nullptr);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
 
 hipError_t launch_pack_pool(int D, bool pool, bool pack, const uint16_t *q, const uint16_t *k,
                             const uint16_t *v, const Grid &g, int heads, float *qp, float *kp,

@@ -154,6 +154,42 @@ int tra_attn(const void *q, const void *k, const void *v, int T, int H, int W, i
              void *out, hipStream_t stream);
 
 /*
+ * Token-level radius policy (Token Radius Attention for Efficient Video
+ * Generation, "Insight I", "Insight II" and "The TRA Pipeline":
+ * Entropy-to-Budget, Budget-to-Radius, Fused CUDA Kernels), per head:
+ *   tra_token_probe (the dense warm-up), per real query token i:
+ *     H_i  = entropy (natural log) of softmax_j(q_i . k_j / sqrt(head_dim)) over
+ *            every real key token j of the head;
+ *     b_i  = tau exp(H_i) keys, clamped to [1, N]  (N = T H W);
+ *     r0_i = sqrt(b_i / (pi S(t_i))),  S(t) = sum_{t'=0}^{T-1} exp(-2 gamma |t' - t|):
+ *            the base radius whose disks r0_i exp(-gamma |t' - t_i|) over the
+ *            T frames have a total area of b_i tokens.
+ *     entropy, r0  device fp32 [heads][T][H][W] (written; entropy may be NULL)
+ *   tra_token_mask: key block K is kept for query block Q when at least
+ *     min_votes real query tokens i of Q have a real key token j of K with
+ *     (y_j - y_i)^2 + (x_j - x_i)^2 <= (r0_i exp(-gamma |t_j - t_i|))^2
+ *     (a Euclidean disk in every frame); lists ascending.
+ *     r0       device fp32 [heads][T][H][W]
+ *     idx      device int32 [heads][nb][nb] (row stride nb; first cnt entries written)
+ *     cnt      device int32 [heads][nb]
+ *     The squared radius is formed in fp32: decisions within rounding of a
+ *     lattice distance may differ from exact arithmetic.
+ *   tra_token_attention: tra_token_probe, tra_token_mask, then tra_attn with
+ *     those lists, on one stream (library scratch, nothing else written).
+ * tau > 0 and gamma >= 0 finite; min_votes in [1, 64]; other arguments as for
+ * tra_attention.  The warm-up costs a dense Q.K^T pass; the page computes it
+ * once and reuses the lists across denoising steps (tra_plan / tra_attn_plan).
+ */
+int tra_token_probe(const void *q, const void *k, int T, int H, int W, int heads, int head_dim,
+                    int block, float tau, float gamma, float *entropy, float *r0,
+                    hipStream_t stream);
+int tra_token_mask(const float *r0, int T, int H, int W, int heads, int block, float gamma,
+                   int min_votes, int32_t *idx, int32_t *cnt, hipStream_t stream);
+int tra_token_attention(const void *q, const void *k, const void *v, int T, int H, int W,
+                        int heads, int head_dim, int block, float tau, float gamma,
+                        int min_votes, void *out, hipStream_t stream);
+
+/*
  * Plan / execute split with cross-step reuse (Token Radius Attention ...,
  * "The TRA Pipeline: Cross-Step Reuse": the sparsity decided in a warm-up step
  * is reused by the later denoising steps).  tra_plan turns key-block lists into
@@ -196,7 +232,9 @@ enum tra_kernel_kind {
     TRA_KERNEL_FILL = 4,      /* dense-mode radius fill */
     TRA_KERNEL_ORDER = 5,     /* longest-first order of the attention work items */
     TRA_KERNEL_UNION = 6,     /* union walk of each pair of query blocks' lists */
-    TRA_KERNEL_KINDS = 7
+    TRA_KERNEL_TOKEN_ENTROPY = 7, /* per-token entropy and base radius (warm-up) */
+    TRA_KERNEL_TOKEN_MASK = 8,    /* token-disk voting lists */
+    TRA_KERNEL_KINDS = 9
 };
 int tra_profile_begin(void);
 int tra_profile_end(double *ms, int *launches, int n);

@@ -13,6 +13,7 @@ the fp64 CPU oracle timed on a bounded sample of the same workload.
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -254,6 +255,43 @@ def main():
         log(f"[bench] binary routing {routing}")
         del ix, cn, rd
 
+    # ---- token-level radius policy: entropy warm-up, voting mask, attention on
+    # the voted lists (first step), then steps reusing those lists ----
+    token = None
+    if not args.no_sweep:
+        tau, gamma, mv = 1.0, 0.5, 1
+        N = T * H * W
+        ent = torch.empty(heads, T, H, W, dtype=torch.float32, device="cuda")
+        r0 = torch.empty_like(ent)
+        kp = profiled(lambda: tra.tra_token_probe(qd, kd, T, H, W, heads, d, 64, tau, gamma, ent, r0), 3)
+        ix = torch.empty(heads, nb, nb, dtype=torch.int32, device="cuda")
+        cn = torch.empty(heads, nb, dtype=torch.int32, device="cuda")
+        km = profiled(lambda: tra.tra_token_mask(r0, T, H, W, heads, 64, gamma, mv, ix, cn), 3)
+        torch.cuda.synchronize()
+        p = int(cn.sum().item())
+        ka = profiled(lambda: tra.tra_attn(qd, kd, vd, T, H, W, heads, d, 64, ix, cn, nb, out), 5)
+        ms_first, _ = timed(lambda: tra.tra_token_attention(qd, kd, vd, T, H, W, heads, d, 64, tau,
+                                                            gamma, mv, out), 3, 1)
+        plan = torch.empty(tra.tra_plan_bytes(T, H, W, heads, 64, nb), dtype=torch.uint8, device="cuda")
+        tra.tra_plan(ix, cn, nb, T, H, W, heads, 64, plan)
+        ms_step, _ = timed(lambda: tra.tra_attn_plan(qd, kd, vd, T, H, W, heads, d, 64, plan, nb, out),
+                           max(5, args.steps // 2), 2)
+        # the warm-up's Q.K^T covers every key tile of every query block pair
+        ent_flops = 2 * 64 * 64 * d * heads * nb * nb
+        token = {"tau": tau, "gamma": gamma, "min_votes": mv,
+                 "entropy_h_mean": round(float(ent.mean().item()), 3), "ln_N": round(math.log(N), 3),
+                 "density": round(p / (heads * nb * nb), 4),
+                 "warmup_entropy_ms": round(kp["token_entropy"], 4),
+                 "warmup_entropy_tflops": round(ent_flops / (kp["token_entropy"] * 1e-3) / 1e12, 1),
+                 "mask_ms": round(km["token_mask"], 4),
+                 "attn_ms": round(ka["attn"], 4),
+                 "attn_tflops": round(flops_pair * p / (ka["attn"] * 1e-3) / 1e12, 1),
+                 "first_step_ms": round(ms_first, 4),
+                 "reuse_step_ms": round(ms_step, 4),
+                 "reuse_speedup_vs_dense_layer": round(ms_dense / ms_step, 3)}
+        log(f"[bench] token policy {token}")
+        del ix, cn, plan, ent, r0
+
     # HBM bandwidth of the probe/pack kernel (algorithmic bytes: read q, k, v,
     # write the packed k and v^T tiles and the pooled means)
     pack_bytes = 3 * heads * c.N * d * 2 + 2 * heads * nb * 64 * d * 2 + 2 * heads * nb * d * 4
@@ -306,6 +344,7 @@ def main():
             "density_sweep": sweep,
             "cross_step_reuse": reuse,
             "binary_routing": routing,
+            "token_policy": token,
             "wall_ms_per_step": round(ms_wall, 4),
             "pv_dtype": "fp16",
         },

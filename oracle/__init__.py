@@ -68,7 +68,9 @@ def _load():
         lib.orc_token_radius.restype = I
         lib.orc_token_lists.argtypes = [P, I, I, I, I, I, D, I, D, L, P, L, P, P]
         lib.orc_token_lists.restype = I
-        lib.orc_attention_lists_rows.argtypes = [P, P, P, I, I, I, I, I, I, P, P, L, L, P, P]
+        lib.orc_attention_lists_rows.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P, L, L, P, P]
+        lib.orc_sip_lists.argtypes = [P, P, P, I, I, I, I, I, I, D, D, L, P, P, P]
+        lib.orc_sip_lists.restype = I
         lib.orc_attention_lists_rows.restype = I
         lib.orc_num_threads.argtypes = []
         lib.orc_num_threads.restype = I
@@ -225,17 +227,39 @@ def token_lists(r0, gamma: float, min_votes: int = 1, block: int = 64, rows=None
     return idx, cnt
 
 
-def attention_lists_rows(q, k, v, idx, cnt, rows, block: int = 64) -> np.ndarray:
+def attention_lists_rows(q, k, v, idx, cnt, rows, block: int = 64, lw=None) -> np.ndarray:
     """Softmax attention of the ``head * N + token`` rows over explicit key-block
-    lists ``idx[heads][nb][maxcnt]``, ``cnt[heads][nb]``; fp64 ``[len(rows)][d]``."""
+    lists ``idx[heads][nb][maxcnt]``, ``cnt[heads][nb]``, with optional per-entry
+    log-weights ``lw`` (same shape as idx); fp64 ``[len(rows)][d]``."""
     q, k, v = _u16(q), _u16(k), _u16(v)
     heads, T, H, W, d = _dims(q)
     idx = np.ascontiguousarray(idx, dtype=np.int32)
     cnt = np.ascontiguousarray(cnt, dtype=np.int32)
     maxcnt = idx.shape[-1]
+    lwp = None
+    if lw is not None:
+        lw = np.ascontiguousarray(lw, dtype=np.float64)
+        assert lw.shape == idx.shape
+        lwp = _ptr(lw)
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     out = np.empty((rows.size, d), dtype=np.float64)
     _check(_load().orc_attention_lists_rows(_ptr(q), _ptr(k), _ptr(v), T, H, W, heads, d, block,
-                                            _ptr(idx), _ptr(cnt), maxcnt, rows.size, _ptr(rows),
-                                            _ptr(out)), "attention_lists_rows")
+                                            _ptr(idx), _ptr(cnt), lwp, maxcnt, rows.size,
+                                            _ptr(rows), _ptr(out)), "attention_lists_rows")
     return out
+
+
+def sip_lists(q, k, u, m: float, block: int = 64, pi_scale: float = 1.0):
+    """Sampled key-block lists with log-weights: (idx int32, cnt int32, lw fp64),
+    idx/lw ``[heads][nb][nb]`` (-1 / 0 past cnt), for uniforms ``u[heads][nb][nb]``."""
+    q, k = _u16(q), _u16(k)
+    heads, T, H, W, d = _dims(q)
+    nb = grid_blocks(T, H, W, block)[2]
+    u = np.ascontiguousarray(u, dtype=np.float64)
+    assert u.shape == (heads, nb, nb)
+    idx = np.full((heads, nb, nb), -1, dtype=np.int32)
+    cnt = np.empty((heads, nb), dtype=np.int32)
+    lw = np.zeros((heads, nb, nb), dtype=np.float64)
+    _check(_load().orc_sip_lists(_ptr(q), _ptr(k), _ptr(u), T, H, W, heads, d, block, float(m),
+                                 float(pi_scale), nb, _ptr(idx), _ptr(cnt), _ptr(lw)), "sip_lists")
+    return idx, cnt, lw

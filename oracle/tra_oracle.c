@@ -505,11 +505,13 @@ int orc_token_lists(const double *r0, int T, int H, int W, int heads, int block,
  * Softmax attention of selected rows over explicit key-block lists:
  * idx[heads][nb][maxcnt], cnt[heads][nb]; entries outside [0, nb) are skipped,
  * every other entry adds all real tokens of its block once more (a duplicate
- * counts twice); an empty row gives zeros.  out[nrows][d] fp64.
+ * counts twice); an empty row gives zeros.  lw[heads][nb][maxcnt] (or NULL)
+ * adds the entry's log-weight to the logits of its keys: the entry's keys
+ * count exp(lw) times in numerator and denominator.  out[nrows][d] fp64.
  */
 int orc_attention_lists_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                              int T, int H, int W, int heads, int d, int block,
-                             const int32_t *idx, const int32_t *cnt, long maxcnt,
+                             const int32_t *idx, const int32_t *cnt, const double *lw, long maxcnt,
                              long nrows, const int64_t *rows, double *out)
 {
     orc_grid g;
@@ -544,6 +546,7 @@ int orc_attention_lists_rows(const uint16_t *q, const uint16_t *k, const uint16_
             if (m_ < 0) m_ = 0;
             if (m_ > maxcnt) m_ = maxcnt;
             const int32_t *row = idx + ((size_t)h * g.nb + bi) * maxcnt;
+            const double *lrow = lw ? lw + ((size_t)h * g.nb + bi) * maxcnt : NULL;
             /* two passes over the listed keys: max, then weights */
             double m = -INFINITY;
             for (int pass = 0; pass < 2; ++pass) {
@@ -554,12 +557,13 @@ int orc_attention_lists_rows(const uint16_t *q, const uint16_t *k, const uint16_
                     if (kb < 0 || kb >= g.nb) continue;
                     int tk = (int)(kb / ((long)g.nby * g.nbx));
                     int byk = (int)((kb / g.nbx) % g.nby), bxk = (int)(kb % g.nbx);
+                    const double bias = lrow ? lrow[e] : 0.0;
                     for (int yj = byk * g.s; yj < (byk + 1) * g.s && yj < H; ++yj)
                         for (int xj = bxk * g.s; xj < (bxk + 1) * g.s && xj < W; ++xj) {
                             long j = ((long)tk * H + yj) * W + xj;
                             double dot = 0.0;
                             for (int c = 0; c < d; ++c) dot += qi[c] * orc_lut[kh[(size_t)j * d + c]];
-                            double sj = dot * inv_sqrt_d;
+                            double sj = dot * inv_sqrt_d + bias;
                             if (pass == 0) {
                                 if (sj > m) m = sj;
                             } else {
@@ -578,6 +582,88 @@ int orc_attention_lists_rows(const uint16_t *q, const uint16_t *k, const uint16_
         free(qi); free(acc);
     }
     return fail ? ORC_ENOMEM : ORC_OK;
+}
+
+/*
+ * Sampling with inclusion-probability weighting (AB-Attention speeds up video
+ * diffusion transformers up to 2.23x, second paragraph: key blocks are sampled
+ * in proportion to importance estimates and reweighted by inverse inclusion
+ * probability, so that one pass estimates dense attention), per head and
+ * query block Q:
+ *   importance  p_QK = softmax_K(Qbar_Q . Kbar_K / sqrt(d)) over all nb key
+ *               blocks, Qbar / Kbar the means over real tokens (one query
+ *               cluster per block);
+ *   inclusion   pi_QK = min(1, m p_QK) for an expected budget of m blocks;
+ *               pi_QQ = 1 (the own block is always kept);
+ *   sample      K kept iff u_QK < pi_QK, u[heads][nb][nb] caller-supplied
+ *               uniforms in [0, 1);
+ *   weight      lw_QK = -ln pi_QK, added to the logits of K's keys: the
+ *               self-normalised inverse-inclusion estimate of dense attention.
+ * pi_scale multiplies pi before the comparison (1 for the definition; 1 -+ eps
+ * brackets rounding).  idx, lw [heads][nb][maxcnt], cnt [heads][nb]; ascending.
+ */
+int orc_sip_lists(const uint16_t *q, const uint16_t *k, const double *u, int T, int H, int W,
+                  int heads, int d, int block, double m, double pi_scale, long maxcnt,
+                  int32_t *idx, int32_t *cnt, double *lw)
+{
+    orc_grid g;
+    if (!q || !k || !u || !idx || !cnt || !lw || heads < 1 || d < 1 || maxcnt < 1 || !(m >= 0.0))
+        return ORC_EINVAL;
+    if (orc_grid_make(&g, T, H, W, block)) return ORC_EINVAL;
+    size_t pooled = (size_t)heads * g.nb * d;
+    double *qb = (double *)malloc(sizeof(double) * pooled);
+    double *kb = (double *)malloc(sizeof(double) * pooled);
+    if (!qb || !kb) { free(qb); free(kb); return ORC_ENOMEM; }
+    int rc = orc_pool(q, T, H, W, heads, d, block, qb);
+    if (!rc) rc = orc_pool(k, T, H, W, heads, d, block, kb);
+    if (rc) { free(qb); free(kb); return rc; }
+    const double inv_sqrt_d = 1.0 / sqrt((double)d);
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)g.nb);
+        if (!s) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for collapse(2) schedule(dynamic, 8)
+        for (int h = 0; h < heads; ++h)
+            for (long b = 0; b < g.nb; ++b) {
+                if (!s) continue;
+                const double *qv = qb + ((size_t)h * g.nb + b) * d;
+                double mx = -INFINITY;
+                for (long c = 0; c < g.nb; ++c) {
+                    const double *kv = kb + ((size_t)h * g.nb + c) * d;
+                    double acc = 0.0;
+                    for (int i = 0; i < d; ++i) acc += qv[i] * kv[i];
+                    s[c] = acc * inv_sqrt_d;
+                    if (s[c] > mx) mx = s[c];
+                }
+                double Z = 0.0;
+                for (long c = 0; c < g.nb; ++c) Z += exp(s[c] - mx);
+                long n = 0;
+                size_t row = (size_t)h * g.nb + b;
+                for (long c = 0; c < g.nb; ++c) {
+                    double pi = c == b ? 1.0 : m * exp(s[c] - mx) / Z;
+                    if (pi > 1.0) pi = 1.0;
+                    if (u[row * g.nb + c] < pi * pi_scale) {
+                        if (n >= maxcnt) {
+#pragma omp atomic write
+                            bad = 1;
+                            break;
+                        }
+                        idx[row * maxcnt + n] = (int32_t)c;
+                        lw[row * maxcnt + n] = -log(pi);
+                        ++n;
+                    }
+                }
+                cnt[row] = (int32_t)n;
+            }
+        free(s);
+    }
+    free(qb);
+    free(kb);
+    return bad ? ORC_EINVAL : ORC_OK;
 }
 
 int orc_num_threads(void) { return omp_get_max_threads(); }

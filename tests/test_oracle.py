@@ -478,3 +478,99 @@ def test_attention_lists_vs_masked_sdpa():
         idx3[0, b, :len(l)] = l
     np.testing.assert_allclose(oracle.attention_lists_rows(q, k, v, idx3, cnt3, rows), got,
                                rtol=1e-12, atol=1e-13)
+
+
+# --------------------------------- sampling with inclusion-probability weights --
+
+def pooled_softmax(q, k, T, H, W, d):
+    """Block-mean logits softmax, from tile slices and scipy: [nb][nb] for head 0."""
+    ids, _ = tile_membership(T, H, W)
+    nb = ids.max() + 1
+    qf, kf = f64(q)[0].reshape(-1, d), f64(k)[0].reshape(-1, d)
+    qm = np.stack([qf[ids == b].mean(0) for b in range(nb)])
+    km = np.stack([kf[ids == b].mean(0) for b in range(nb)])
+    return scipy.special.softmax(qm @ km.T / math.sqrt(d), axis=1)
+
+
+def test_sip_extremes_reduce_to_dense_and_per_tile():
+    T, H, W, d = 2, 16, 24, 16
+    q, k, v = ti.random_qkv(T, H, W, 1, d, seed=31)
+    nb = oracle.grid_blocks(T, H, W)[2]
+    u = np.random.default_rng(1).random((1, nb, nb))
+    rows = np.arange(T * H * W)
+    idx, cnt, lw = oracle.sip_lists(q, k, u, 1e12)  # every inclusion probability 1
+    assert (cnt == nb).all() and (lw == 0).all()
+    got = oracle.attention_lists_rows(q, k, v, idx, cnt, rows, lw=lw)
+    ref = sdpa(f64(q).reshape(1, -1, d), f64(k).reshape(1, -1, d), f64(v).reshape(1, -1, d))[0]
+    np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-12)
+    idx, cnt, lw = oracle.sip_lists(q, k, u, 0.0)  # only the own block
+    assert (cnt == 1).all() and (idx[0, :, 0] == np.arange(nb)).all()
+
+
+def test_sip_inclusion_follows_pooled_importance():
+    T, H, W, d = 2, 16, 24, 16
+    q, k, _ = ti.random_qkv(T, H, W, 1, d, seed=32, scale=3.0)
+    nb = oracle.grid_blocks(T, H, W)[2]
+    m = 2.5
+    idx, cnt, lw = oracle.sip_lists(q, k, np.zeros((1, nb, nb)), m)  # u = 0 keeps every pi > 0
+    assert (cnt == nb).all()
+    p = pooled_softmax(q, k, T, H, W, d)
+    pi = np.exp(-lw[0])
+    want = np.minimum(1.0, m * p)
+    np.fill_diagonal(want, 1.0)
+    np.testing.assert_allclose(pi, want, rtol=1e-10)
+    # a block is kept when its uniform falls below its inclusion probability
+    b, c = 0, int(np.argmin(want[0] + np.eye(nb)[0]))
+    assert want[b, c] < 1
+    u = np.full((1, nb, nb), 0.999999)
+    u[0, b, c] = want[b, c] * (1 + 1e-9)
+    i2, c2, _ = oracle.sip_lists(q, k, u, m)
+    assert c not in i2[0, b, :c2[0, b]].tolist()
+    u[0, b, c] = want[b, c] * (1 - 1e-9)
+    i3, c3, _ = oracle.sip_lists(q, k, u, m)
+    assert c in i3[0, b, :c3[0, b]].tolist()
+
+
+def test_sip_estimate_is_unbiased():
+    # sum over kept blocks of exp(lw) S_K estimates sum over all blocks of S_K
+    T, H, W, d = 2, 16, 16, 16
+    q, k, v = ti.random_qkv(T, H, W, 1, d, seed=33, scale=2.0)
+    nb = oracle.grid_blocks(T, H, W)[2]
+    ids, _ = tile_membership(T, H, W)
+    qf, kf = f64(q)[0].reshape(-1, d), f64(k)[0].reshape(-1, d)
+    i = 5  # a query token of block 0
+    s = kf @ qf[i] / math.sqrt(d)
+    S = np.array([np.exp(s[ids == b] - s.max()).sum() for b in range(nb)])
+    rng = np.random.default_rng(2)
+    R = 3000
+    est = np.empty(R)
+    for r in range(R):
+        idx, cnt, lw = oracle.sip_lists(q, k, rng.random((1, nb, nb)), 2.0)
+        kept = idx[0, 0, :cnt[0, 0]]
+        est[r] = (np.exp(lw[0, 0, :cnt[0, 0]]) * S[kept]).sum()
+    se = est.std() / math.sqrt(R)
+    assert se > 0
+    assert abs(est.mean() - S.sum()) < 4 * se
+
+
+def test_weighted_list_attention_identities():
+    T, H, W, d = 2, 12, 16, 8
+    q, k, v = ti.random_qkv(T, H, W, 1, d, seed=34)
+    nb = oracle.grid_blocks(T, H, W)[2]
+    rows = np.arange(T * H * W)
+    idx = np.full((1, nb, 3), -1, dtype=np.int32)
+    cnt = np.full((1, nb), 2, dtype=np.int32)
+    for b in range(nb):
+        idx[0, b, :2] = [b, (b + 1) % nb]
+    # a log-weight of ln 2 on one entry counts that block twice
+    lw = np.zeros((1, nb, 3))
+    lw[0, :, 1] = math.log(2.0)
+    got = oracle.attention_lists_rows(q, k, v, idx, cnt, rows, lw=lw)
+    dup = idx.copy()
+    dup[0, :, 2] = dup[0, :, 1]
+    ref = oracle.attention_lists_rows(q, k, v, dup, np.full((1, nb), 3, dtype=np.int32), rows)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+    # a constant log-weight changes nothing
+    const = oracle.attention_lists_rows(q, k, v, idx, cnt, rows, lw=np.full((1, nb, 3), 0.7))
+    plain = oracle.attention_lists_rows(q, k, v, idx, cnt, rows)
+    np.testing.assert_allclose(const, plain, rtol=1e-12, atol=1e-13)

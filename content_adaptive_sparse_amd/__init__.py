@@ -19,13 +19,13 @@ __all__ = [
     "TRA_RADIUS_INF", "TraError", "library", "tra_attention", "tra_probe", "tra_mask",
     "tra_attn", "tra_grid", "tra_maxcnt", "tra_status_string", "tra_version",
     "tra_plan_bytes", "tra_plan", "tra_attn_plan", "tra_token_probe", "tra_token_mask",
-    "tra_token_attention",
+    "tra_token_attention", "tra_sip_mask", "tra_attn_weighted",
     "tra_profile_begin", "tra_profile_end", "KERNEL_KINDS",
 ]
 
 TRA_RADIUS_INF = 2147483647
 KERNEL_KINDS = ("pack_pool", "entropy", "mask", "attn", "fill", "order", "union",
-                "token_entropy", "token_mask")
+                "token_entropy", "token_mask", "sip")
 
 _lib = None
 
@@ -75,6 +75,10 @@ def library() -> ctypes.CDLL:
         lib.tra_token_mask.restype = I
         lib.tra_token_attention.argtypes = [P, P, P, I, I, I, I, I, I, F, F, I, P, P]
         lib.tra_token_attention.restype = I
+        lib.tra_sip_mask.argtypes = [P, P, P, I, I, I, I, I, I, F, P, P, P, P]
+        lib.tra_sip_mask.restype = I
+        lib.tra_attn_weighted.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P, L, P, P]
+        lib.tra_attn_weighted.restype = I
         lib.tra_profile_begin.argtypes = []
         lib.tra_profile_begin.restype = I
         lib.tra_profile_end.argtypes = [P, P, I]
@@ -218,6 +222,22 @@ def tra_token_attention(q, k, v, T, H, W, heads, head_dim, block, tau, gamma, mi
         _ptr(q, _bf16(), "q"), _ptr(k, _bf16(), "k"), _ptr(v, _bf16(), "v"), T, H, W, heads,
         head_dim, block, float(tau), float(gamma), int(min_votes), _ptr(out, _f32(), "out"),
         _stream(stream)), "tra_token_attention")
+
+
+def tra_sip_mask(q, k, u, T, H, W, heads, head_dim, block, m, idx, cnt, lw, stream=None):
+    _check(library().tra_sip_mask(
+        _ptr(q, _bf16(), "q"), _ptr(k, _bf16(), "k"), _ptr(u, _f32(), "u"), T, H, W, heads,
+        head_dim, block, float(m), _ptr(idx, _i32(), "idx"), _ptr(cnt, _i32(), "cnt"),
+        _ptr(lw, _f32(), "lw"), _stream(stream)), "tra_sip_mask")
+
+
+def tra_attn_weighted(q, k, v, T, H, W, heads, head_dim, block, idx, cnt, lw, maxcnt, out,
+                      stream=None):
+    _check(library().tra_attn_weighted(
+        _ptr(q, _bf16(), "q"), _ptr(k, _bf16(), "k"), _ptr(v, _bf16(), "v"), T, H, W, heads,
+        head_dim, block, _ptr(idx, _i32(), "idx"), _ptr(cnt, _i32(), "cnt"),
+        _ptr(lw, _f32(), "lw"), int(maxcnt), _ptr(out, _f32(), "out"), _stream(stream)),
+        "tra_attn_weighted")
 
 
 def tra_profile_begin():

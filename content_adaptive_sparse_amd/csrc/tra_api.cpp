@@ -258,13 +258,13 @@ int tra_mask(const int32_t *radius, int T, int H, int W, int heads, int block, i
 
 // The attention walk of the lists: union of each pair's two lists, then the
 // longest-first order of the pairs.
-static hipError_t plan_walk(const int32_t *idx, const int32_t *cnt, int64_t maxcnt,
-                            const tra::Grid &g, int heads, int32_t *ulist, int32_t *ulen,
-                            int32_t *order, hipStream_t stream) {
+static hipError_t plan_walk(const int32_t *idx, const int32_t *cnt, const float *lw,
+                            int64_t maxcnt, const tra::Grid &g, int heads, int32_t *ulist,
+                            int32_t *ulen, float2 *ubias, int32_t *order, hipStream_t stream) {
     hipError_t e;
     {
         ProfScope p(TRA_KERNEL_UNION, stream);
-        e = tra::launch_union(idx, cnt, maxcnt, g, heads, ulist, ulen, stream);
+        e = tra::launch_union(idx, cnt, lw, maxcnt, g, heads, ulist, ulen, ubias, stream);
     }
     if (e == hipSuccess) {
         ProfScope p(TRA_KERNEL_ORDER, stream);
@@ -273,23 +273,35 @@ static hipError_t plan_walk(const int32_t *idx, const int32_t *cnt, int64_t maxc
     return e;
 }
 
-// Layout of a walk plan in one buffer: work order, walk lengths, walks; each part
-// 256-byte aligned.
+// Layout of a walk plan in one buffer: work order, walk lengths, walks and (for
+// weighted lists) the walks' per-side log2 weights; each part 256-byte aligned.
 struct PlanLayout {
-    size_t o_order, o_ulen, o_ulist, bytes;
+    size_t o_order, o_ulen, o_ulist, o_ubias, bytes;
     int64_t ustride;
+    bool weighted;
 };
 
-static PlanLayout plan_layout(const tra::Grid &g, int heads, int64_t maxcnt) {
+static PlanLayout plan_layout(const tra::Grid &g, int heads, int64_t maxcnt,
+                              bool weighted = false) {
     auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
     PlanLayout L;
     const size_t slots = order_items(g, heads);
     L.ustride = tra::union_stride(maxcnt);
+    L.weighted = weighted;
     L.o_order = 0;
     L.o_ulen = up(slots * sizeof(int32_t));
     L.o_ulist = L.o_ulen + up(slots * sizeof(int32_t));
-    L.bytes = L.o_ulist + up(slots * (size_t)L.ustride * sizeof(int32_t));
+    L.o_ubias = L.o_ulist + up(slots * (size_t)L.ustride * sizeof(int32_t));
+    L.bytes = L.o_ubias + (weighted ? up(slots * (size_t)L.ustride * sizeof(float2)) : 0);
     return L;
+}
+
+static hipError_t plan_walk_into(const int32_t *idx, const int32_t *cnt, const float *lw,
+                                 int64_t maxcnt, const tra::Grid &g, int heads, char *plan,
+                                 const PlanLayout &L, hipStream_t stream) {
+    return plan_walk(idx, cnt, lw, maxcnt, g, heads, (int32_t *)(plan + L.o_ulist),
+                     (int32_t *)(plan + L.o_ulen), L.weighted ? (float2 *)(plan + L.o_ubias) : nullptr,
+                     (int32_t *)(plan + L.o_order), stream);
 }
 
 // Pack k and v, then attention along a walk plan (nullptr: dense mode).
@@ -313,7 +325,8 @@ static int attn_with_plan(const void *q, const void *k, const void *v, const tra
         const int32_t *order = plan ? (const int32_t *)(plan + L.o_order) : nullptr;
         const int32_t *ulen = plan ? (const int32_t *)(plan + L.o_ulen) : nullptr;
         const int32_t *ulist = plan ? (const int32_t *)(plan + L.o_ulist) : nullptr;
-        e = tra::launch_attn(head_dim, (const uint16_t *)q, kt, vt, ulist, ulen,
+        const float2 *ubias = plan && L.weighted ? (const float2 *)(plan + L.o_ubias) : nullptr;
+        e = tra::launch_attn(head_dim, (const uint16_t *)q, kt, vt, ulist, ulen, ubias,
                              plan ? L.ustride : 0, order, g, heads, (float *)out, stream);
     }
     return hip_status(e);
@@ -343,10 +356,8 @@ int tra_plan(const int32_t *idx, const int32_t *cnt, int64_t maxcnt, int T, int 
     if (rc == TRA_OK) rc = check_plan(g, heads, maxcnt);
     if (rc != TRA_OK) return rc;
     if (!idx || !cnt || !plan) return TRA_ERR_INVALID_ARG;
-    const PlanLayout L = plan_layout(g, heads, maxcnt);
-    char *pb = static_cast<char *>(plan);
-    return hip_status(plan_walk(idx, cnt, maxcnt, g, heads, (int32_t *)(pb + L.o_ulist),
-                                (int32_t *)(pb + L.o_ulen), (int32_t *)(pb + L.o_order), stream));
+    return hip_status(plan_walk_into(idx, cnt, nullptr, maxcnt, g, heads, static_cast<char *>(plan),
+                                     plan_layout(g, heads, maxcnt), stream));
 }
 
 int tra_attn_plan(const void *q, const void *k, const void *v, int T, int H, int W, int heads,
@@ -380,11 +391,65 @@ int tra_attn(const void *q, const void *k, const void *v, int T, int H, int W, i
     const size_t o_plan = ws.reserve(L.bytes);
     if ((rc = ws.allocate()) != TRA_OK) return rc;
     char *plan = ws.at<char>(o_plan);
-    const hipError_t e = plan_walk(idx, cnt, maxcnt, g, heads, (int32_t *)(plan + L.o_ulist),
-                                   (int32_t *)(plan + L.o_ulen), (int32_t *)(plan + L.o_order),
-                                   stream);
+    const hipError_t e = plan_walk_into(idx, cnt, nullptr, maxcnt, g, heads, plan, L, stream);
     if (e != hipSuccess) return hip_status(e);
     return attn_with_plan(q, k, v, g, heads, head_dim, plan, L, out, stream);
+}
+
+int tra_attn_weighted(const void *q, const void *k, const void *v, int T, int H, int W, int heads,
+                      int head_dim, int block, const int32_t *idx, const int32_t *cnt,
+                      const float *lw, int64_t maxcnt, void *out, hipStream_t stream) {
+    if (!lw) return tra_attn(q, k, v, T, H, W, heads, head_dim, block, idx, cnt, maxcnt, out, stream);
+    tra::Grid g;
+    int rc = make_grid(T, H, W, block, &g);
+    if (rc == TRA_OK) rc = check_dims(heads, head_dim, g);
+    if (rc != TRA_OK) return rc;
+    if (!q || !k || !v || !out || !idx || !cnt) return TRA_ERR_INVALID_ARG;
+    if ((rc = check_plan(g, heads, maxcnt)) != TRA_OK) return rc;
+    const PlanLayout L = plan_layout(g, heads, maxcnt, true);
+    Scratch ws(stream);
+    const size_t o_plan = ws.reserve(L.bytes);
+    if ((rc = ws.allocate()) != TRA_OK) return rc;
+    char *plan = ws.at<char>(o_plan);
+    const hipError_t e = plan_walk_into(idx, cnt, lw, maxcnt, g, heads, plan, L, stream);
+    if (e != hipSuccess) return hip_status(e);
+    return attn_with_plan(q, k, v, g, heads, head_dim, plan, L, out, stream);
+}
+
+int tra_sip_mask(const void *q, const void *k, const float *u, int T, int H, int W, int heads,
+                 int head_dim, int block, float m, int32_t *idx, int32_t *cnt, float *lw,
+                 hipStream_t stream) {
+    tra::Grid g;
+    int rc = make_grid(T, H, W, block, &g);
+    if (rc == TRA_OK) rc = check_dims(heads, head_dim, g);
+    if (rc != TRA_OK) return rc;
+    if (!q || !k || !u || !idx || !cnt || !lw || !(m >= 0.f) || !isfinite(m))
+        return TRA_ERR_INVALID_ARG;
+    if ((double)heads * g.nb * g.nb > (double)((int64_t)1 << 40)) return TRA_ERR_UNSUPPORTED;
+    const size_t rows = (size_t)heads * g.nb;
+    Scratch ws(stream);
+    const size_t pooled = rows * head_dim * sizeof(float);
+    const size_t o_qp = ws.reserve(pooled), o_kp = ws.reserve(pooled);
+    const size_t o_r = ws.reserve(rows * sizeof(int32_t));
+    const size_t o_lg = ws.reserve(rows * (size_t)g.nb * sizeof(float));
+    if ((rc = ws.allocate()) != TRA_OK) return rc;
+    float *qp = ws.at<float>(o_qp), *kp = ws.at<float>(o_kp), *lg = ws.at<float>(o_lg);
+    int32_t *radius = ws.at<int32_t>(o_r);
+    hipError_t e;
+    {
+        ProfScope p(TRA_KERNEL_PACK_POOL, stream);
+        e = tra::launch_pack_pool(head_dim, true, false, (const uint16_t *)q, (const uint16_t *)k,
+                                  nullptr, g, heads, qp, kp, nullptr, nullptr, stream);
+    }
+    if (e == hipSuccess) {
+        ProfScope p(TRA_KERNEL_ENTROPY, stream);
+        e = tra::launch_entropy(head_dim, qp, kp, g, heads, 0, 0, radius, nullptr, stream, lg);
+    }
+    if (e == hipSuccess) {
+        ProfScope p(TRA_KERNEL_SIP, stream);
+        e = tra::launch_sip(lg, u, g, heads, m, idx, cnt, lw, stream);
+    }
+    return hip_status(e);
 }
 
 static int check_token_params(float tau, float gamma) {
@@ -476,13 +541,11 @@ int tra_token_attention(const void *q, const void *k, const void *v, int T, int 
         ProfScope p(TRA_KERNEL_TOKEN_MASK, stream);
         e = tra::launch_token_mask(r0, g, heads, gamma, min_votes, g.nb, idx, cnt, stream);
     }
-    if (e == hipSuccess)
-        e = plan_walk(idx, cnt, g.nb, g, heads, (int32_t *)(plan + L.o_ulist),
-                      (int32_t *)(plan + L.o_ulen), (int32_t *)(plan + L.o_order), stream);
+    if (e == hipSuccess) e = plan_walk_into(idx, cnt, nullptr, g.nb, g, heads, plan, L, stream);
     if (e == hipSuccess) {
         ProfScope p(TRA_KERNEL_ATTN, stream);
         e = tra::launch_attn(head_dim, (const uint16_t *)q, kt, vt, (const int32_t *)(plan + L.o_ulist),
-                             (const int32_t *)(plan + L.o_ulen), L.ustride,
+                             (const int32_t *)(plan + L.o_ulen), nullptr, L.ustride,
                              (const int32_t *)(plan + L.o_order), g, heads, (float *)out, stream);
     }
     return hip_status(e);
@@ -529,8 +592,8 @@ int tra_attention(const void *q, const void *k, const void *v, int T, int H, int
         }
         if (e == hipSuccess) {
             ProfScope p(TRA_KERNEL_ATTN, stream);
-            e = tra::launch_attn(head_dim, q16, kt, vt, nullptr, nullptr, 0, nullptr, g, heads, o32,
-                                 stream);
+            e = tra::launch_attn(head_dim, q16, kt, vt, nullptr, nullptr, nullptr, 0, nullptr, g,
+                                 heads, o32, stream);
         }
         return hip_status(e);
     }
@@ -550,11 +613,12 @@ int tra_attention(const void *q, const void *k, const void *v, int T, int H, int
     }
     int32_t *order = ws.at<int32_t>(o_order), *ulen = ws.at<int32_t>(o_ulen);
     int32_t *ulist = ws.at<int32_t>(o_ulist);
-    if (e == hipSuccess) e = plan_walk(idx, cnt, maxcnt, g, heads, ulist, ulen, order, stream);
+    if (e == hipSuccess)
+        e = plan_walk(idx, cnt, nullptr, maxcnt, g, heads, ulist, ulen, nullptr, order, stream);
     if (e == hipSuccess) {
         ProfScope p(TRA_KERNEL_ATTN, stream);
-        e = tra::launch_attn(head_dim, q16, kt, vt, ulist, ulen, tra::union_stride(maxcnt), order,
-                             g, heads, o32, stream);
+        e = tra::launch_attn(head_dim, q16, kt, vt, ulist, ulen, nullptr, tra::union_stride(maxcnt),
+                             order, g, heads, o32, stream);
     }
     return hip_status(e);
 }

@@ -33,11 +33,14 @@ constexpr int kAttnThreads = 256;
 // normalisation by l uses the same reference, so the result is unchanged.
 constexpr float kRescaleLog2 = 8.0f;
 
-template <int D>
+// WEIGHTED: every walk entry carries, per side, a log2 weight added to the
+// logits of its keys (inverse inclusion probabilities of sampled blocks).
+template <int D, bool WEIGHTED>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kt,
     const uint16_t *__restrict__ vt, const int32_t *__restrict__ ulist,
-    const int32_t *__restrict__ ulen, int64_t ustride, const int32_t *__restrict__ order, Grid g,
+    const int32_t *__restrict__ ulen, const float2 *__restrict__ ubias, int64_t ustride,
+    const int32_t *__restrict__ order, Grid g,
     int heads, int pairs_per_head, int per_xcd, FastDiv div_nbx, FastDiv div_nby,
     float *__restrict__ out, float scale_log2) {
     constexpr int KS = D / 16;                  // k-steps of Q.K^T
@@ -109,9 +112,17 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
         return;
     }
     int win = 0, win_next = 0, wbase = 0;
+    // this wave's side's weight of every entry, windowed like the entries
+    const float *ubw = WEIGHTED ? reinterpret_cast<const float *>(ubias + item * ustride) + side
+                                : nullptr;
+    float bwin = 0.f, bwin_next = 0.f;
     if (ul) {
         win = lane < n ? ul[lane] : 0;
         win_next = 64 + lane < n ? ul[64 + lane] : 0;
+        if (WEIGHTED) {
+            bwin = lane < n ? ubw[2 * lane] : 0.f;
+            bwin_next = 64 + lane < n ? ubw[2 * (64 + lane)] : 0.f;
+        }
     }
     // Entry i (-1 past the end); called with i = 0, 1, 2, ... in turn.
     auto entry = [&](int i) -> int {
@@ -121,8 +132,17 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
             win = win_next;
             wbase += 64;
             win_next = wbase + 64 + lane < n ? ul[wbase + 64 + lane] : 0;
+            if (WEIGHTED) {
+                bwin = bwin_next;
+                bwin_next = wbase + 64 + lane < n ? ubw[2 * (wbase + 64 + lane)] : 0.f;
+            }
         }
         return __builtin_amdgcn_readlane(win, i - wbase);
+    };
+    // weight of entry i for this wave's side (right after entry(i): same window)
+    auto weight = [&](int i) -> float {
+        if (!WEIGHTED || i >= n) return 0.f;
+        return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bwin), i - wbase));
     };
 
     // Direct global -> LDS copy of one packed tile of block `blk` into `dst`:
@@ -156,7 +176,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
         for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
     float m_ref = -1e30f, l_run = 0.f;
 
-    int e0 = entry(0), e1 = entry(1);  // entries u and u + 1
+    int e0 = entry(0);
+    float w0 = weight(0);
+    int e1 = entry(1);  // entries u and u + 1
+    float w1 = weight(1);
     TRA_ISSUE(kt, kring[0], e0 >> 2);
     if (e1 >= 0) {
         TRA_ISSUE(kt, kring[1], e1 >> 2);
@@ -229,18 +252,19 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
             for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sb[hf][r]);
-            mx = half_swap_max(mx) * scale_log2;
+            mx = half_swap_max(mx) * scale_log2 + w0;
             const bool grow = mx > m_ref + kRescaleLog2;
             const float m_new = grow ? mx : m_ref;
             const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
             m_ref = m_new;
+            const float bias = w0 - m_ref;
             float psum0 = 0.f, psum1 = 0.f;
             const f16x2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    sb[hf][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[hf][r], scale_log2, -m_ref));
+                    sb[hf][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[hf][r], scale_log2, bias));
 #pragma unroll
                 for (int ks2 = 0; ks2 < 2; ++ks2) {
 #pragma unroll
@@ -281,10 +305,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
         __syncthreads();
         constexpr int s = decltype(slot_tag)::value;
         const int e2 = entry(u + 2);
+        const float w2 = weight(u + 2);
         if (e2 >= 0) TRA_ISSUE(kt, kring[s], e2 >> 2);      // entry u + 2
         if (e1 >= 0) TRA_ISSUE(vt, vring[s ^ 1], e1 >> 2);  // entry u + 1
         e0 = e1;
         e1 = e2;
+        w0 = w1;
+        w1 = w2;
         ++u;
         return true;
     };
@@ -310,23 +337,30 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
 }  // namespace
 
 hipError_t launch_attn(int D, const uint16_t *q, const uint16_t *kt, const uint16_t *vt,
-                       const int32_t *ulist, const int32_t *ulen, int64_t ustride,
-                       const int32_t *order, const Grid &g, int heads, float *out,
-                       hipStream_t s) {
+                       const int32_t *ulist, const int32_t *ulen, const float2 *ubias,
+                       int64_t ustride, const int32_t *order, const Grid &g, int heads,
+                       float *out, hipStream_t s) {
     const int pph = pairs_per_head(g);
     const int64_t total = (int64_t)heads * pph;
     const int per_xcd = (int)((total + 7) / 8);
     const dim3 grid((unsigned)(8 * (int64_t)per_xcd)), block(kAttnThreads);
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
     const FastDiv div_nbx = make_fastdiv(g.nbx), div_nby = make_fastdiv(g.nby);
-    if (D == 128)
-        hipLaunchKernelGGL(attn_kernel<128>, grid, block, 0, s, q, kt, vt, ulist, ulen, ustride,
-                           order, g, heads, pph, per_xcd, div_nbx, div_nby, out, scale_log2);
+#define TRA_LAUNCH(DD, WW)                                                                    \
+    hipLaunchKernelGGL((attn_kernel<DD, WW>), grid, block, 0, s, q, kt, vt, ulist, ulen, ubias,  \
+                       ustride, order, g, heads, pph, per_xcd, div_nbx, div_nby, out, scale_log2)
+    const bool weighted = ubias != nullptr && ulist != nullptr;
+    if (D == 128 && weighted)
+        TRA_LAUNCH(128, true);
+    else if (D == 128)
+        TRA_LAUNCH(128, false);
+    else if (D == 64 && weighted)
+        TRA_LAUNCH(64, true);
     else if (D == 64)
-        hipLaunchKernelGGL(attn_kernel<64>, grid, block, 0, s, q, kt, vt, ulist, ulen, ustride,
-                           order, g, heads, pph, per_xcd, div_nbx, div_nby, out, scale_log2);
+        TRA_LAUNCH(64, false);
     else
         return hipErrorInvalidValue;
+#undef TRA_LAUNCH
     return hipGetLastError();
 }
 

@@ -34,8 +34,10 @@ hipError_t launch_pack_pool(int D, bool pool, bool pack, const uint16_t *q, cons
                             const uint16_t *v, const Grid &g, int heads, float *qp, float *kp,
                             uint16_t *kt, uint16_t *vt, hipStream_t s);
 
+// logits (optional): the pooled logit matrix [heads][nb][nb] (scaled by 1/sqrt(D)).
 hipError_t launch_entropy(int D, const float *qp, const float *kp, const Grid &g, int heads,
-                          int r_min, int r_max, int32_t *radius, float *h_norm, hipStream_t s);
+                          int r_min, int r_max, int32_t *radius, float *h_norm, hipStream_t s,
+                          float *logits = nullptr);
 
 hipError_t launch_fill_dense(const Grid &g, int heads, int32_t *radius, float *h_norm,
                              hipStream_t s);
@@ -74,10 +76,18 @@ __host__ __device__ inline void pair_blocks(int p, const Grid &g, int &qa, int &
 }
 
 // Union walk of each work item (see tra_mask.hip): ulist holds, at row stride
-// union_stride(maxcnt), entries (block << 2) | sides, ulen their counts.
+// union_stride(maxcnt), entries (block << 2) | sides, ulen their counts; with
+// per-entry log-weights lw (laid out like idx, or null) ubias holds each
+// entry's (upper, lower) block weight in log2 units.
 int64_t union_stride(int64_t maxcnt);
-hipError_t launch_union(const int32_t *idx, const int32_t *cnt, int64_t maxcnt, const Grid &g,
-                        int heads, int32_t *ulist, int32_t *ulen, hipStream_t s);
+hipError_t launch_union(const int32_t *idx, const int32_t *cnt, const float *lw, int64_t maxcnt,
+                        const Grid &g, int heads, int32_t *ulist, int32_t *ulen, float2 *ubias,
+                        hipStream_t s);
+
+// Sampled lists with log-weights from the pooled logit matrix and uniforms
+// u[heads][nb][nb] (row stride nb for idx and lw).
+hipError_t launch_sip(const float *logits, const float *u, const Grid &g, int heads, float m,
+                      int32_t *idx, int32_t *cnt, float *lw, hipStream_t s);
 
 // XCD-aware, longest-first order of the attention work items by union length:
 // order holds order_slots(g, heads) grid slots (-1: no item).
@@ -90,8 +100,8 @@ hipError_t launch_order(const int32_t *ulen, const Grid &g, int heads, int64_t m
 // ulist == nullptr: the dense mode (every block, both sides; order null, items
 // in XCD-contiguous raster order).
 hipError_t launch_attn(int D, const uint16_t *q, const uint16_t *kt, const uint16_t *vt,
-                       const int32_t *ulist, const int32_t *ulen, int64_t ustride,
-                       const int32_t *order, const Grid &g, int heads, float *out,
-                       hipStream_t s);
+                       const int32_t *ulist, const int32_t *ulen, const float2 *ubias,
+                       int64_t ustride, const int32_t *order, const Grid &g, int heads,
+                       float *out, hipStream_t s);
 
 }  // namespace tra

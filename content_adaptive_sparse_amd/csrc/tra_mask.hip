@@ -109,10 +109,15 @@ __device__ bool list_ascending(const int32_t *l, int n, int nb, int lane) {
     return true;
 }
 
+// With per-entry log-weights lw (natural log, laid out like idx), every walk
+// entry also gets its two blocks' weights in log2 units (ubias; 0 for a side
+// that does not keep the block).
 __global__ __launch_bounds__(64 * kUnionWaves) void union_kernel(
-    const int32_t *__restrict__ idx, const int32_t *__restrict__ cnt, int64_t maxcnt, Grid g,
-    int64_t items, int pairs_per_head, int64_t ustride, int32_t *__restrict__ ulist,
-    int32_t *__restrict__ ulen) {
+    const int32_t *__restrict__ idx, const int32_t *__restrict__ cnt,
+    const float *__restrict__ lw, int64_t maxcnt, Grid g, int64_t items, int pairs_per_head,
+    int64_t ustride, int32_t *__restrict__ ulist, int32_t *__restrict__ ulen,
+    float2 *__restrict__ ubias) {
+    constexpr float kLog2e = 1.4426950408889634f;
     const int64_t item = (int64_t)blockIdx.x * kUnionWaves + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (item >= items) return;
@@ -126,8 +131,11 @@ __global__ __launch_bounds__(64 * kUnionWaves) void union_kernel(
     };
     const int32_t *A = idx + (h * g.nb + qa) * maxcnt;
     const int32_t *B = qb >= 0 ? idx + (h * g.nb + qb) * maxcnt : A;
+    const float *wA = lw ? lw + (h * g.nb + qa) * maxcnt : nullptr;
+    const float *wB = lw ? lw + (h * g.nb + (qb >= 0 ? qb : qa)) * maxcnt : nullptr;
     const int a = len(qa), b = len(qb);
     int32_t *out = ulist + item * ustride;
+    float2 *bout = ubias ? ubias + item * ustride : nullptr;
     int n = 0;
     if (list_ascending(A, a, g.nb, lane) && list_ascending(B, b, g.nb, lane)) {
         int common = 0;
@@ -141,7 +149,11 @@ __global__ __launch_bounds__(64 * kUnionWaves) void union_kernel(
                 in_b = pos < b && B[pos] == x;
             }
             const uint64_t bal = __ballot(in_b);
-            if (i < a) out[i + pos - common - lanes_before(bal)] = (x << 2) | 1 | (in_b ? 2 : 0);
+            if (i < a) {
+                const int64_t o = i + pos - common - lanes_before(bal);
+                out[o] = (x << 2) | 1 | (in_b ? 2 : 0);
+                if (bout) bout[o] = make_float2(wA[i] * kLog2e, in_b ? wB[pos] * kLog2e : 0.f);
+            }
             common += __popcll(bal);
         }
         int common_b = 0;
@@ -155,7 +167,11 @@ __global__ __launch_bounds__(64 * kUnionWaves) void union_kernel(
                 in_a = pos < a && A[pos] == y;
             }
             const uint64_t bal = __ballot(in_a);
-            if (j < b && !in_a) out[j + pos - common_b - lanes_before(bal)] = (y << 2) | 2;
+            if (j < b && !in_a) {
+                const int64_t o = j + pos - common_b - lanes_before(bal);
+                out[o] = (y << 2) | 2;
+                if (bout) bout[o] = make_float2(0.f, wB[j] * kLog2e);
+            }
             common_b += __popcll(bal);
         }
         n = a + b - common;
@@ -163,13 +179,21 @@ __global__ __launch_bounds__(64 * kUnionWaves) void union_kernel(
 #pragma unroll
         for (int side = 0; side < 2; ++side) {
             const int32_t *l = side ? B : A;
+            const float *wl = side ? wB : wA;
             const int m = side ? b : a;
             for (int i0 = 0; i0 < m; i0 += 64) {
                 const int i = i0 + lane;
                 const int x = i < m ? l[i] : -1;
                 const bool keep = i < m && (unsigned)x < (unsigned)g.nb;
                 const uint64_t bal = __ballot(keep);
-                if (keep) out[n + lanes_before(bal)] = (x << 2) | (1 << side);
+                if (keep) {
+                    const int64_t o = n + lanes_before(bal);
+                    out[o] = (x << 2) | (1 << side);
+                    if (bout) {
+                        const float w = wl[i] * kLog2e;
+                        bout[o] = side ? make_float2(0.f, w) : make_float2(w, 0.f);
+                    }
+                }
                 n += __popcll(bal);
             }
         }
@@ -221,17 +245,69 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *__r
         order[kXcds * k + x] = -1;
 }
 
+// Sampling with inclusion-probability weights (AB-Attention speeds up video
+// diffusion transformers up to 2.23x, second paragraph): per (head, query
+// block Q), importance p_K = softmax of the pooled logits over every key
+// block, inclusion pi_K = min(1, m p_K) (pi_Q = 1: the own block is always
+// kept), key block K kept when the caller's uniform u_QK < pi_K, with
+// log-weight -ln pi_K.  One wave64 per row: a max and a sum over the row,
+// then ballot compaction in ascending block order.
+__global__ __launch_bounds__(256) void sip_kernel(const float *__restrict__ logits,
+                                                  const float *__restrict__ u, int64_t rows,
+                                                  int nb, float m, int64_t maxcnt,
+                                                  int32_t *__restrict__ idx,
+                                                  int32_t *__restrict__ cnt,
+                                                  float *__restrict__ lw) {
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const int qb = (int)(row % nb);
+    const float *lr = logits + row * nb;
+    const float *ur = u + row * nb;
+    constexpr float kLog2e = 1.4426950408889634f;
+    float mx = -INFINITY;
+    for (int c = lane; c < nb; c += 64) mx = fmaxf(mx, lr[c]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    float z = 0.f;
+    for (int c = lane; c < nb; c += 64) z += __builtin_amdgcn_exp2f((lr[c] - mx) * kLog2e);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
+    const float mz = m / z;
+    int32_t *out = idx + row * maxcnt;
+    float *wout = lw + row * maxcnt;
+    int64_t count = 0;
+    for (int c0 = 0; c0 < nb; c0 += 64) {
+        const int c = c0 + lane;
+        bool keep = false;
+        float pi = 1.f;
+        if (c < nb) {
+            pi = c == qb ? 1.f : fminf(1.f, mz * __builtin_amdgcn_exp2f((lr[c] - mx) * kLog2e));
+            keep = ur[c] < pi;
+        }
+        const uint64_t bal = __ballot(keep);
+        const int64_t pos = count + lanes_before(bal);
+        if (keep && pos < maxcnt) {
+            out[pos] = c;
+            wout[pos] = -0.69314718055994531f * __builtin_amdgcn_logf(pi);
+        }
+        count += __popcll(bal);
+    }
+    if (lane == 0) cnt[row] = (int32_t)(count < maxcnt ? count : maxcnt);
+}
+
 }  // namespace
 
 int64_t union_stride(int64_t maxcnt) { return (2 * maxcnt + 63) / 64 * 64; }
 
-hipError_t launch_union(const int32_t *idx, const int32_t *cnt, int64_t maxcnt, const Grid &g,
-                        int heads, int32_t *ulist, int32_t *ulen, hipStream_t s) {
+hipError_t launch_union(const int32_t *idx, const int32_t *cnt, const float *lw, int64_t maxcnt,
+                        const Grid &g, int heads, int32_t *ulist, int32_t *ulen, float2 *ubias,
+                        hipStream_t s) {
     const int pph = pairs_per_head(g);
     const int64_t items = (int64_t)heads * pph;
     hipLaunchKernelGGL(union_kernel, dim3((unsigned)((items + kUnionWaves - 1) / kUnionWaves)),
-                       dim3(64 * kUnionWaves), 0, s, idx, cnt, maxcnt, g, items, pph,
-                       union_stride(maxcnt), ulist, ulen);
+                       dim3(64 * kUnionWaves), 0, s, idx, cnt, lw, maxcnt, g, items, pph,
+                       union_stride(maxcnt), ulist, ulen, ubias);
     return hipGetLastError();
 }
 
@@ -243,6 +319,18 @@ hipError_t launch_order(const int32_t *ulen, const Grid &g, int heads, int64_t m
     const size_t lds = (size_t)(maxlen + 1) * sizeof(int32_t);
     hipLaunchKernelGGL(order_kernel, dim3(kXcds), dim3(kOrderThreads), lds, s, ulen, items, maxlen,
                        order);
+    return hipGetLastError();
+}
+
+}  // namespace tra
+
+namespace tra {
+
+hipError_t launch_sip(const float *logits, const float *u, const Grid &g, int heads, float m,
+                      int32_t *idx, int32_t *cnt, float *lw, hipStream_t s) {
+    const int64_t rows = (int64_t)heads * g.nb;
+    hipLaunchKernelGGL(sip_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, logits, u,
+                       rows, g.nb, m, (int64_t)g.nb, idx, cnt, lw);
     return hipGetLastError();
 }
 

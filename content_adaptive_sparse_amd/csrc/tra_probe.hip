@@ -172,7 +172,7 @@ template <int D>
 __global__ __launch_bounds__(256) void entropy_kernel(
     const float *__restrict__ qp, const float *__restrict__ kp, Grid g, int r_min,
     int64_t R, int r_max, float inv_ln_nb, float scale, int32_t *__restrict__ radius,
-    float *__restrict__ h_norm) {
+    float *__restrict__ h_norm, float *__restrict__ logits) {
     constexpr int P = D + 4;
     __shared__ __attribute__((aligned(16))) float Qs[kEntQ][P];
     __shared__ __attribute__((aligned(16))) float Ks[kEntK][P];
@@ -209,6 +209,7 @@ __global__ __launch_bounds__(256) void entropy_kernel(
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) s[i][j] = 0.f;
+#pragma unroll 2
         for (int dd = 0; dd < D; dd += 4) {
             const float4 a0 = *reinterpret_cast<const float4 *>(&Qs[2 * tq][dd]);
             const float4 a1 = *reinterpret_cast<const float4 *>(&Qs[2 * tq + 1][dd]);
@@ -226,6 +227,9 @@ __global__ __launch_bounds__(256) void entropy_kernel(
             for (int j = 0; j < 4; ++j) {
                 s[i][j] *= scale;
                 if (c0 + tk + 16 * j < g.nb) mx = fmaxf(mx, s[i][j]);
+                // the pooled logit matrix [heads][nb][nb], when asked for
+                if (logits && c0 + tk + 16 * j < g.nb && q0 + 2 * tq + i < g.nb)
+                    logits[((size_t)h * g.nb + q0 + 2 * tq + i) * g.nb + c0 + tk + 16 * j] = s[i][j];
             }
             if (mx > st[i].m) {
                 const float a = expf(st[i].m - mx);
@@ -317,17 +321,18 @@ hipError_t launch_pack_pool(int D, bool pool, bool pack, const uint16_t *q, cons
 }
 
 hipError_t launch_entropy(int D, const float *qp, const float *kp, const Grid &g, int heads,
-                          int r_min, int r_max, int32_t *radius, float *h_norm, hipStream_t s) {
+                          int r_min, int r_max, int32_t *radius, float *h_norm, hipStream_t s,
+                          float *logits) {
     const dim3 grid((g.nb + kEntQ - 1) / kEntQ, heads), block(256);
     const int64_t R = (int64_t)r_max - (int64_t)r_min + 1;
     const float inv_ln_nb = g.nb > 1 ? (float)(1.0 / log((double)g.nb)) : 0.f;
     const float scale = (float)(1.0 / sqrt((double)D));
     if (D == 128)
         hipLaunchKernelGGL(entropy_kernel<128>, grid, block, 0, s, qp, kp, g, r_min, R, r_max,
-                           inv_ln_nb, scale, radius, h_norm);
+                           inv_ln_nb, scale, radius, h_norm, logits);
     else if (D == 64)
         hipLaunchKernelGGL(entropy_kernel<64>, grid, block, 0, s, qp, kp, g, r_min, R, r_max,
-                           inv_ln_nb, scale, radius, h_norm);
+                           inv_ln_nb, scale, radius, h_norm, logits);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

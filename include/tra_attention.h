@@ -190,6 +190,36 @@ int tra_token_attention(const void *q, const void *k, const void *v, int T, int 
                         int min_votes, void *out, hipStream_t stream);
 
 /*
+ * Sampling with inclusion-probability weighting (AB-Attention speeds up video
+ * diffusion transformers up to 2.23x, second paragraph: key blocks sampled in
+ * proportion to importance estimates and reweighted by inverse inclusion
+ * probability, so that one pass estimates dense attention), per head and
+ * query block Q:
+ *   p_QK  = softmax over every key block K of Qbar_Q . Kbar_K / sqrt(head_dim)
+ *           (means over real tokens; one query cluster per block);
+ *   pi_QK = min(1, m p_QK), pi_QQ = 1 (the own block is always kept);
+ *   K is kept iff u[h][Q][K] < pi_QK, with log-weight lw = -ln pi_QK.
+ *   tra_sip_mask writes the kept blocks ascending:
+ *     u       device fp32 [heads][nb][nb] uniforms in [0, 1) drawn by the caller
+ *     m       expected number of blocks drawn per query block (>= 0, finite)
+ *     idx, lw device int32 / fp32 [heads][nb][nb] (row stride nb; first cnt written)
+ *     cnt     device int32 [heads][nb]
+ *     p and pi are formed in fp32: draws within rounding of pi may differ from
+ *     exact arithmetic.
+ *   tra_attn_weighted is tra_attn with a log-weight per list entry (laid out
+ *     like idx): every key of the entry's block enters the softmax with its
+ *     logit plus lw, i.e. exp(lw) times in numerator and denominator -- the
+ *     self-normalised inverse-inclusion estimate of dense attention when the
+ *     lists come from tra_sip_mask.  lw = NULL is tra_attn.
+ */
+int tra_sip_mask(const void *q, const void *k, const float *u, int T, int H, int W, int heads,
+                 int head_dim, int block, float m, int32_t *idx, int32_t *cnt, float *lw,
+                 hipStream_t stream);
+int tra_attn_weighted(const void *q, const void *k, const void *v, int T, int H, int W, int heads,
+                      int head_dim, int block, const int32_t *idx, const int32_t *cnt,
+                      const float *lw, int64_t maxcnt, void *out, hipStream_t stream);
+
+/*
  * Plan / execute split with cross-step reuse (Token Radius Attention ...,
  * "The TRA Pipeline: Cross-Step Reuse": the sparsity decided in a warm-up step
  * is reused by the later denoising steps).  tra_plan turns key-block lists into
@@ -234,7 +264,8 @@ enum tra_kernel_kind {
     TRA_KERNEL_UNION = 6,     /* union walk of each pair of query blocks' lists */
     TRA_KERNEL_TOKEN_ENTROPY = 7, /* per-token entropy and base radius (warm-up) */
     TRA_KERNEL_TOKEN_MASK = 8,    /* token-disk voting lists */
-    TRA_KERNEL_KINDS = 9
+    TRA_KERNEL_SIP = 9,           /* sampled lists with inverse-inclusion weights */
+    TRA_KERNEL_KINDS = 10
 };
 int tra_profile_begin(void);
 int tra_profile_end(double *ms, int *launches, int n);

@@ -215,7 +215,7 @@ def main():
 
     # ---- cross-step reuse: probe, mask and walk plan once (the warm-up step);
     # every later step packs k, v and runs the attention along the stored plan ----
-    reuse, routing = None, None
+    reuse, routing, route_lists = None, None, None
     if not args.no_sweep:
         idx = torch.empty(heads, nb, maxcnt, dtype=torch.int32, device="cuda")
         tra.tra_mask(radius, T, H, W, heads, 64, c.r_max, idx, cnt)
@@ -253,7 +253,8 @@ def main():
                    "tflops": round(flops_pair * p / (kk["attn"] * 1e-3) / 1e12, 1),
                    "speedup_vs_dense_attn": round(kd_["attn"] / kk["attn"], 2)}
         log(f"[bench] binary routing {routing}")
-        del ix, cn, rd
+        route_lists = (ix, cn)
+        del rd
 
     # ---- token-level radius policy: entropy warm-up, voting mask, attention on
     # the voted lists (first step), then steps reusing those lists ----
@@ -291,6 +292,50 @@ def main():
                  "reuse_speedup_vs_dense_layer": round(ms_dense / ms_step, 3)}
         log(f"[bench] token policy {token}")
         del ix, cn, plan, ent, r0
+
+    # ---- sampling with inclusion-probability weights (seeded device uniforms),
+    # and how far each scheme's output is from dense attention ----
+    sip, quality = [], None
+    if not args.no_sweep:
+        out_dense = torch.empty_like(out)
+        tra.tra_attention(qd, kd, vd, T, H, W, heads, d, 64, INF, INF, out_dense)
+
+        def l1_vs_dense():
+            torch.cuda.synchronize()
+            return round(float((out - out_dense).abs().sum() / out_dense.abs().sum()), 5)
+
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(0)
+        u = torch.rand(heads, nb, nb, device="cuda", generator=gen)
+        ix = torch.empty(heads, nb, nb, dtype=torch.int32, device="cuda")
+        cn = torch.empty(heads, nb, dtype=torch.int32, device="cuda")
+        lw = torch.empty(heads, nb, nb, dtype=torch.float32, device="cuda")
+        for m in (64.0, 256.0, 1024.0):
+            ks = profiled(lambda: tra.tra_sip_mask(qd, kd, u, T, H, W, heads, d, 64, m, ix, cn, lw), 3)
+            torch.cuda.synchronize()
+            p = int(cn.sum().item())
+            kw = profiled(lambda: tra.tra_attn_weighted(qd, kd, vd, T, H, W, heads, d, 64, ix, cn, lw,
+                                                        nb, out), 5)
+            sip.append({"m": m, "density": round(p / (heads * nb * nb), 4),
+                        "sip_mask_ms": round(ks["sip"] + ks["entropy"] + ks["pack_pool"], 4),
+                        "attn_ms": round(kw["attn"], 4),
+                        "tflops": round(flops_pair * p / (kw["attn"] * 1e-3) / 1e12, 1),
+                        "l1_vs_dense": l1_vs_dense()})
+            log(f"[bench] sip {sip[-1]}")
+        del ix, cn, lw, u
+        quality = {}
+        layer(c.r_min, c.r_max)
+        quality["probe_radii"] = {"density": round(density, 4), "l1_vs_dense": l1_vs_dense()}
+        if token is not None:
+            tra.tra_token_attention(qd, kd, vd, T, H, W, heads, d, 64, token["tau"], token["gamma"],
+                                    token["min_votes"], out)
+            quality["token_policy"] = {"density": token["density"], "l1_vs_dense": l1_vs_dense()}
+        if routing is not None:
+            tra.tra_attn(qd, kd, vd, T, H, W, heads, d, 64, route_lists[0], route_lists[1], nb, out)
+            quality["binary_routing"] = {"density": routing["density"], "l1_vs_dense": l1_vs_dense()}
+        quality["sip"] = [{"density": e["density"], "l1_vs_dense": e["l1_vs_dense"]} for e in sip]
+        log(f"[bench] output error vs dense attention {quality}")
+        del out_dense, route_lists
 
     # HBM bandwidth of the probe/pack kernel (algorithmic bytes: read q, k, v,
     # write the packed k and v^T tiles and the pooled means)
@@ -345,6 +390,8 @@ def main():
             "cross_step_reuse": reuse,
             "binary_routing": routing,
             "token_policy": token,
+            "sip_sweep": sip,
+            "l1_vs_dense_by_scheme": quality,
             "wall_ms_per_step": round(ms_wall, 4),
             "pv_dtype": "fp16",
         },

@@ -343,6 +343,27 @@ def test_binary_routing():
     assert_close(out.reshape(-1, d)[rows], ref, "binary routing attention")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mixed", [False, True], ids=["negative", "mixed"])
+def test_negative_logit_rows_on_edge_tiles(d, mixed):
+    # Rows whose every logit is far below zero, on grids with ragged tiles.
+    # A padded key must never stand in for such a row's max: that would push
+    # every probability of the row below the fp16 range.
+    for T, H, W, heads in ((3, 20, 28, 2), (2, 13, 9, 3), (2, 30, 52, 1)):
+        shp = (heads, T, H, W, d)
+        print(f"[case] negative logits {shp} mixed={mixed}", flush=True)
+        q, k, v = ti.aligned_qkv(T, H, W, heads, d, seed=13, mixed_signs=mixed)
+        qd, kd, vd = dev16(q), dev16(k), dev16(v)
+        nb = tra.tra_grid(T, H, W)[2]
+        radii = np.random.default_rng(4).integers(0, 3, size=(heads, nb)).astype(np.int32)
+        idx, cnt, maxcnt = gpu_mask(radii, shp, 2)
+        out = gpu_attn(qd, kd, vd, shp, idx, cnt, maxcnt).cpu().numpy()
+        assert_close(out, oracle.attention(q, k, v, radii), f"negative logits {shp}")
+        dense = gpu_attn(qd, kd, vd, shp).cpu().numpy()
+        assert_close(dense, oracle.attention(q, k, v, oracle.dense_radii(heads, nb)),
+                     f"negative logits dense {shp}")
+
+
 def test_mask_clamps_radius_to_r_max():
     T, H, W, heads = 6, 24, 40, 1
     shp = (heads, T, H, W, 64)

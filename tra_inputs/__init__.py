@@ -200,6 +200,25 @@ def make_config_inputs(cfg_id: int, seed: int = 0, heads_only=None):
                        sigma=c.sigma, head_scale=c.head_scale, heads_only=heads_only)
 
 
+def aligned_qkv(T: int, H: int, W: int, heads: int, d: int, *, seed: int = 0,
+                amp: float = 20.0, noise: float = 0.3, mixed_signs: bool = False):
+    """q and k along one shared unit direction u, as bf16 bit patterns.
+
+    k = amp u + noise e_k, and q = -amp u + noise e_q (every logit of every row
+    strongly negative), or with mixed_signs each query token's sign drawn at
+    random (rows of both signs side by side).  v ~ N(0, 1).
+    """
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(98,))))
+    shape = (heads, T, H, W, d)
+    u = rng.standard_normal((heads, 1, 1, 1, d))
+    u /= np.linalg.norm(u, axis=-1, keepdims=True)
+    sign = (rng.integers(0, 2, size=shape[:-1] + (1,)) * 2 - 1) if mixed_signs else -1.0
+    q = sign * amp * u + noise * rng.standard_normal(shape)
+    k = amp * u + noise * rng.standard_normal(shape)
+    v = rng.standard_normal(shape)
+    return tuple(bf16_from_f32(a.astype(np.float32)) for a in (q, k, v))
+
+
 def random_qkv(T: int, H: int, W: int, heads: int, d: int, *, seed: int = 0,
                scale: float = 1.0):
     """Plain i.i.d. N(0, scale^2) q, k, v as bf16 bit patterns (property tests)."""

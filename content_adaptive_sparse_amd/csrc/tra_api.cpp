@@ -134,7 +134,8 @@ class Scratch {
 int hip_status(hipError_t e) { return e == hipSuccess ? TRA_OK : TRA_ERR_HIP; }
 
 // Work items of the attention kernel: pairs of neighbouring query blocks.
-size_t order_items(const tra::Grid &g, int heads) { return (size_t)tra::order_slots(g, heads); }
+size_t walk_rows(const tra::Grid &g, int heads) { return (size_t)tra::walk_items(g, heads); }
+size_t order_len(const tra::Grid &g, int heads) { return (size_t)tra::order_slots(g, heads); }
 
 // ---- optional per-kernel event timing ----
 struct ProfRecord {
@@ -285,14 +286,14 @@ static PlanLayout plan_layout(const tra::Grid &g, int heads, int64_t maxcnt,
                               bool weighted = false) {
     auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
     PlanLayout L;
-    const size_t slots = order_items(g, heads);
+    const size_t rows = walk_rows(g, heads);
     L.ustride = tra::union_stride(maxcnt);
     L.weighted = weighted;
     L.o_order = 0;
-    L.o_ulen = up(slots * sizeof(int32_t));
-    L.o_ulist = L.o_ulen + up(slots * sizeof(int32_t));
-    L.o_ubias = L.o_ulist + up(slots * (size_t)L.ustride * sizeof(int32_t));
-    L.bytes = L.o_ubias + (weighted ? up(slots * (size_t)L.ustride * sizeof(float2)) : 0);
+    L.o_ulen = up(order_len(g, heads) * sizeof(int32_t));
+    L.o_ulist = L.o_ulen + up(rows * sizeof(int32_t));
+    L.o_ubias = L.o_ulist + up(rows * (size_t)L.ustride * sizeof(int32_t));
+    L.bytes = L.o_ubias + (weighted ? up(rows * (size_t)L.ustride * sizeof(float2)) : 0);
     return L;
 }
 
@@ -335,7 +336,7 @@ static int attn_with_plan(const void *q, const void *k, const void *v, const tra
 // Walk plans above 2^44 bytes are refused (they could not be allocated anyway).
 static int check_plan(const tra::Grid &g, int heads, int64_t maxcnt) {
     if (maxcnt < 1 || maxcnt > (int64_t)1 << 30) return TRA_ERR_INVALID_ARG;
-    const double bytes = (double)order_items(g, heads) * (double)tra::union_stride(maxcnt) * 4.0;
+    const double bytes = (double)walk_rows(g, heads) * (double)tra::union_stride(maxcnt) * 4.0;
     return bytes > (double)((int64_t)1 << 44) ? TRA_ERR_UNSUPPORTED : TRA_OK;
 }
 
@@ -574,9 +575,9 @@ int tra_attention(const void *q, const void *k, const void *v, int T, int H, int
         o_r = ws.reserve(rows * sizeof(int32_t));
         o_cnt = ws.reserve(rows * sizeof(int32_t));
         o_idx = ws.reserve(rows * (size_t)maxcnt * sizeof(int32_t));
-        o_order = ws.reserve(order_items(g, heads) * sizeof(int32_t));
-        o_ulen = ws.reserve(order_items(g, heads) * sizeof(int32_t));
-        o_ulist = ws.reserve(order_items(g, heads) * (size_t)tra::union_stride(maxcnt) * sizeof(int32_t));
+        o_order = ws.reserve(order_len(g, heads) * sizeof(int32_t));
+        o_ulen = ws.reserve(walk_rows(g, heads) * sizeof(int32_t));
+        o_ulist = ws.reserve(walk_rows(g, heads) * (size_t)tra::union_stride(maxcnt) * sizeof(int32_t));
     }
     if ((rc = ws.allocate()) != TRA_OK) return rc;
     uint16_t *kt = ws.at<uint16_t>(o_kt), *vt = ws.at<uint16_t>(o_vt);

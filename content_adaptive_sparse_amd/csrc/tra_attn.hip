@@ -343,7 +343,9 @@ hipError_t launch_attn(int D, const uint16_t *q, const uint16_t *kt, const uint1
     const int pph = pairs_per_head(g);
     const int64_t total = (int64_t)heads * pph;
     const int per_xcd = (int)((total + 7) / 8);
-    const dim3 grid((unsigned)(8 * (int64_t)per_xcd)), block(kAttnThreads);
+    // one workgroup per slot of the work order, or per item in XCD ranges
+    const dim3 grid((unsigned)(order ? order_slots(g, heads) : 8 * (int64_t)per_xcd)),
+        block(kAttnThreads);
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
     const FastDiv div_nbx = make_fastdiv(g.nbx), div_nby = make_fastdiv(g.nby);
 #define TRA_LAUNCH(DD, WW)                                                                    \

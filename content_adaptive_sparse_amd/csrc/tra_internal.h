@@ -89,11 +89,19 @@ hipError_t launch_union(const int32_t *idx, const int32_t *cnt, const float *lw,
 hipError_t launch_sip(const float *logits, const float *u, const Grid &g, int heads, float m,
                       int32_t *idx, int32_t *cnt, float *lw, hipStream_t s);
 
-// XCD-aware, longest-first order of the attention work items by union length:
-// order holds order_slots(g, heads) grid slots (-1: no item).
-inline int64_t order_slots(const Grid &g, int heads) {
+// Per-item arrays of a walk plan (lengths, walks) hold walk_items(g, heads) rows.
+inline int64_t walk_items(const Grid &g, int heads) {
     return ((int64_t)heads * pairs_per_head(g) + 7) / 8 * 8;
 }
+// XCD-aware, longest-first order of the attention work items: eight contiguous
+// ranges of equal work, each of at most order_range_cap items (twice the
+// average count); order holds order_slots(g, heads) = 8 x cap grid slots (-1:
+// no item), and the attention launch has one workgroup per slot (an empty
+// slot's workgroup exits at once; empty slots come last on their XCD).
+inline int64_t order_range_cap(const Grid &g, int heads) {
+    return 2 * (((int64_t)heads * pairs_per_head(g) + 7) / 8);
+}
+inline int64_t order_slots(const Grid &g, int heads) { return 8 * order_range_cap(g, heads); }
 hipError_t launch_order(const int32_t *ulen, const Grid &g, int heads, int64_t maxcnt,
                         int32_t *order, hipStream_t s);
 

@@ -202,30 +202,79 @@ __global__ __launch_bounds__(64 * kUnionWaves) void union_kernel(
 }
 
 // Work order for the attention kernel.  Workgroup ids are dealt to the eight
-// XCDs round robin (id % 8), each XCD with its own L2, so XCD x is given the
-// contiguous raster range x of the items (neighbouring query blocks of the
-// same head share most key tiles) and takes it longest first, so that long
-// items do not start last and leave a tail: the k-th longest item of range x
-// goes to grid slot 8 k + x, slots past a short range hold -1.  One workgroup
-// per XCD: histogram of lengths in LDS, a descending prefix scan, a scatter
-// (the order among equal lengths is arbitrary; results do not depend on it).
+// XCDs round robin (id % 8), each XCD with its own L2, so XCD x is given a
+// contiguous raster range of the items (neighbouring query blocks of the same
+// head share most key tiles).  The ranges are cut at equal shares of the total
+// work (walk length plus a fixed per-item cost), not at equal item counts: the
+// whole launch waits for its busiest XCD.  A range holds at most `cap` items
+// (the cut moves when a range would exceed it).  Each range is taken longest
+// first, so that long items do not start last and leave a tail: the k-th
+// longest item of range x goes to grid slot 8 k + x, and slots past a range's
+// end hold -1.  One workgroup per XCD, each finding all eight cuts the same
+// way: per-thread chunk sums, a block scan, a count of the items starting
+// below each share; then a histogram of its range's lengths in LDS, a
+// descending prefix scan and a scatter (the order among equal lengths is
+// arbitrary; results do not depend on it).
 constexpr int kOrderThreads = 1024;
 constexpr int kOrderMaxBin = 8191;
 constexpr int kXcds = 8;
+constexpr int kItemCost = 4;  // prologue and epilogue of an item, in walk steps
 
 __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *__restrict__ ulen,
-                                                              int64_t items, int maxlen,
+                                                              int64_t items, int64_t cap,
+                                                              int maxlen,
                                                               int32_t *__restrict__ order) {
     extern __shared__ int32_t bins[];  // maxlen + 1 bins
+    __shared__ int64_t part[kOrderThreads];
+    __shared__ int64_t below[kXcds];  // items starting below share x / 8 of the work
+    __shared__ int64_t total_work;
     const int tid = threadIdx.x, x = blockIdx.x;
-    const int64_t per = (items + kXcds - 1) / kXcds;
-    const int64_t lo = x * per, hi = min(items, lo + per);
-    for (int i = tid; i <= maxlen; i += kOrderThreads) bins[i] = 0;
-    __syncthreads();
     auto length_of = [&](int64_t it) -> int {
         const int len = ulen[it];
         return len < 0 ? 0 : (len > maxlen ? maxlen : len);
     };
+    // chunk sums and their exclusive block scan
+    const int64_t chunk = (items + kOrderThreads - 1) / kOrderThreads;
+    const int64_t c0 = min(items, tid * chunk), c1 = min(items, c0 + chunk);
+    int64_t mine = 0;
+    for (int64_t it = c0; it < c1; ++it) mine += length_of(it) + kItemCost;
+    part[tid] = mine;
+    if (tid < kXcds) below[tid] = 0;
+    __syncthreads();
+    if (tid == 0) {
+        int64_t run = 0;
+        for (int i = 0; i < kOrderThreads; ++i) {
+            const int64_t v = part[i];
+            part[i] = run;
+            run += v;
+        }
+        total_work = run;
+    }
+    __syncthreads();
+    const int64_t total = total_work;
+    // count, for every share, the items of this chunk starting below it
+    {
+        int64_t start = part[tid];
+        int64_t cnt[kXcds] = {};
+        for (int64_t it = c0; it < c1; ++it) {
+#pragma unroll
+            for (int s = 1; s < kXcds; ++s) cnt[s] += start * kXcds < s * total ? 1 : 0;
+            start += length_of(it) + kItemCost;
+        }
+#pragma unroll
+        for (int s = 1; s < kXcds; ++s)
+            if (cnt[s]) atomicAdd((unsigned long long *)&below[s], (unsigned long long)cnt[s]);
+    }
+    for (int i = tid; i <= maxlen; i += kOrderThreads) bins[i] = 0;
+    __syncthreads();
+    // this XCD's range, cut at the shares within the cap
+    int64_t lo = 0, hi = 0;
+    for (int r = 0; r <= x; ++r) {
+        lo = hi;
+        hi = r == kXcds - 1 ? items : below[r + 1];
+        hi = max(hi, items - cap * (kXcds - 1 - r));  // the rest must fit the later ranges
+        hi = min(max(hi, lo), min(items, lo + cap));
+    }
     for (int64_t it = lo + tid; it < hi; it += kOrderThreads) atomicAdd(&bins[length_of(it)], 1);
     __syncthreads();
     if (tid == 0) {  // descending exclusive scan: longest lengths first
@@ -241,8 +290,7 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *__r
         const int64_t k = atomicAdd(&bins[length_of(it)], 1);
         order[kXcds * k + x] = (int32_t)it;
     }
-    for (int64_t k = (hi > lo ? hi - lo : 0) + tid; k < per; k += kOrderThreads)
-        order[kXcds * k + x] = -1;
+    for (int64_t k = (hi - lo) + tid; k < cap; k += kOrderThreads) order[kXcds * k + x] = -1;
 }
 
 // Sampling with inclusion-probability weights (AB-Attention speeds up video
@@ -317,8 +365,8 @@ hipError_t launch_order(const int32_t *ulen, const Grid &g, int heads, int64_t m
     // lengths above kOrderMaxBin share the top bin (they still start first)
     const int maxlen = (int)(2 * maxcnt < kOrderMaxBin ? 2 * maxcnt : kOrderMaxBin);
     const size_t lds = (size_t)(maxlen + 1) * sizeof(int32_t);
-    hipLaunchKernelGGL(order_kernel, dim3(kXcds), dim3(kOrderThreads), lds, s, ulen, items, maxlen,
-                       order);
+    hipLaunchKernelGGL(order_kernel, dim3(kXcds), dim3(kOrderThreads), lds, s, ulen, items,
+                       order_range_cap(g, heads), maxlen, order);
     return hipGetLastError();
 }
 

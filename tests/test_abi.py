@@ -116,8 +116,9 @@ def test_plan_bytes_closed_form(lib):
         nby, nbx = -(-H // 8), -(-W // 8)
         items = heads * T * ((nby + 1) // 2) * nbx
         slots = -(-items // 8) * 8
+        order = 8 * 2 * -(-items // 8)  # eight ranges of at most twice the mean count
         stride = -(-(2 * maxcnt) // 64) * 64
-        want = up(4 * slots) + up(4 * slots) + up(4 * slots * stride)
+        want = up(4 * order) + up(4 * slots) + up(4 * slots * stride)
         assert tra.tra_plan_bytes(T, H, W, heads, 64, maxcnt) == want
 
 

@@ -321,6 +321,56 @@ def test_plan_reuse_across_steps():
         assert_close(out.cpu().numpy().reshape(-1, d)[rows], ref, f"plan reuse step {step}")
 
 
+def test_work_order_ranges():
+    # The work order deals the walk items to eight XCD ranges: contiguous raster
+    # ranges cut at equal shares of the total work (walk length + 4 per item),
+    # each of at most cap = 2 ceil(items / 8) items, taken longest first into
+    # grid slots 8 k + x, -1 past a range's end.  Every item appears once.
+    T, H, W, heads = 6, 30, 52, 3
+    shp = (heads, T, H, W, 128)
+    print(f"[case] work order {shp}", flush=True)
+    nb = tra.tra_grid(T, H, W)[2]
+    rng = np.random.default_rng(17)
+    radii = rng.integers(2, 4, size=(heads, nb)).astype(np.int32)
+    radii[:, : nb // 3] = 1  # a cheap third: equal counts would not balance the work
+    idx, cnt, maxcnt = gpu_mask(radii, shp, 3)
+    plan = torch.zeros(tra.tra_plan_bytes(T, H, W, heads, 64, maxcnt), dtype=torch.uint8,
+                       device="cuda")
+    tra.tra_plan(idx, cnt, maxcnt, T, H, W, heads, 64, plan)
+    torch.cuda.synchronize()
+    raw = plan.cpu().numpy().view(np.int32)
+    nby, nbx = -(-H // 8), -(-W // 8)
+    items = heads * T * ((nby + 1) // 2) * nbx
+    cap = 2 * -(-items // 8)
+    order = raw[: 8 * cap]
+    o_ulen = -(-(4 * 8 * cap) // 256) * 256 // 4  # the walk lengths follow, 256-byte aligned
+    ulen = raw[o_ulen: o_ulen + items]
+    assert np.array_equal(np.sort(order[order >= 0]), np.arange(items)), "not a permutation"
+    cost = np.clip(ulen, 0, min(2 * maxcnt, 8191)).astype(np.int64) + 4
+    start = np.concatenate([[0], np.cumsum(cost)[:-1]])
+    total = int(cost.sum())
+    below = [0] + [int(np.sum(8 * start < s * total)) for s in range(1, 8)]
+    lo = hi = 0
+    works = []
+    clamped = False
+    for x in range(8):
+        lo = hi
+        cut = items if x == 7 else below[x + 1]
+        hi = max(cut, items - cap * (7 - x))
+        hi = min(max(hi, lo), min(items, lo + cap))
+        clamped |= hi != cut
+        col = order[x::8]
+        n = hi - lo
+        assert np.array_equal(np.sort(col[:n]), np.arange(lo, hi)), f"range {x}"
+        assert (col[n:] == -1).all(), f"range {x}: slots past the end"
+        assert (np.diff(ulen[col[:n]]) <= 0).all(), f"range {x}: not longest first"
+        works.append(int(cost[lo:hi].sum()))
+    print(f"[order] items {items} cap {cap} range work {works} mean {total / 8:.0f} "
+          f"clamped {clamped}", flush=True)
+    assert not clamped  # this workload fits the cap, so the cuts are the equal shares
+    assert max(works) <= total / 8 + cost.max()
+
+
 def test_binary_routing():
     # HetA-style routing: every block either local (radius 1) or dense (radius
     # infinite) from a supplied difficulty map; the mask with r_max infinite

@@ -146,18 +146,25 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     };
 
     // Direct global -> LDS copy of one packed tile of block `blk` into `dst`:
-    // each wave moves PPW 1 KB pieces; lane l lands 16 bytes at piece base + 16 l.
+    // each wave moves PPW 1 KB pieces; lane l lands 16 bytes at piece base +
+    // 16 l.  One global address and one LDS base (M0, wave-uniform) serve the
+    // wave's pieces: a piece's 1 KB step is the instruction's immediate
+    // offset, which applies to both the global and the LDS address.
+    static_assert(PPW == 2 || PPW == 4, "pieces per wave");
     const size_t head_tiles = (size_t)h * g.nb;
-    const int wave_piece_bytes = wave * PPW * 1024;
-    const int wave_piece_elems = wave * PPW * 512;
-    const int lane16 = lane * 16;
+    const int wave_lds_bytes = __builtin_amdgcn_readfirstlane(wave * PPW * 1024);
+    const uint32_t lane_bytes = (uint32_t)(wave * PPW * 1024 + lane * 16);
 #define TRA_ISSUE(src, dst, blk)                                                              \
     do {                                                                                      \
-        const char *s_ = reinterpret_cast<const char *>(src + (head_tiles + (blk)) * 64 * D) + \
-                         wave_piece_bytes + lane16;                                           \
-        _Pragma("unroll") for (int i_ = 0; i_ < PPW; ++i_)                                    \
-            __builtin_amdgcn_global_load_lds((const global_void_t *)(s_ + i_ * 1024),         \
-                                             (lds_void_t *)&(dst)[wave_piece_elems + i_ * 512], 16, 0, 0); \
+        const global_void_t *g_ = (const global_void_t *)(                                    \
+            reinterpret_cast<const char *>(src + (head_tiles + (blk)) * 64 * D) + lane_bytes); \
+        lds_void_t *l_ = (lds_void_t *)(reinterpret_cast<char *>(dst) + wave_lds_bytes);      \
+        __builtin_amdgcn_global_load_lds(g_, l_, 16, 0, 0);                                   \
+        __builtin_amdgcn_global_load_lds(g_, l_, 16, 1024, 0);                                \
+        if constexpr (PPW == 4) {                                                             \
+            __builtin_amdgcn_global_load_lds(g_, l_, 16, 2048, 0);                            \
+            __builtin_amdgcn_global_load_lds(g_, l_, 16, 3072, 0);                            \
+        }                                                                                     \
     } while (0)
 
     // Every matrix-core operand of a packed tile is a 1 KB piece in which this

@@ -220,14 +220,42 @@ constexpr int kOrderMaxBin = 8191;
 constexpr int kXcds = 8;
 constexpr int kItemCost = 4;  // prologue and epilogue of an item, in walk steps
 
+// Exclusive prefix sum of one value per thread over the block (1024 threads):
+// shuffles within each wave, then the 16 wave totals.  Every thread gets its
+// exclusive prefix; *total receives the block total.
+__device__ int64_t block_exclusive_scan(int64_t v, int64_t *wave_sums, int64_t *total) {
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    int64_t x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int64_t y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) wave_sums[wid] = x;
+    __syncthreads();
+    if (tid == 0) {
+        int64_t run = 0;
+        for (int w = 0; w < kOrderThreads / 64; ++w) {
+            const int64_t t = wave_sums[w];
+            wave_sums[w] = run;
+            run += t;
+        }
+        *total = run;
+    }
+    __syncthreads();
+    const int64_t r = wave_sums[wid] + x - v;
+    __syncthreads();  // wave_sums may be reused by the next scan
+    return r;
+}
+
 __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *__restrict__ ulen,
                                                               int64_t items, int64_t cap,
                                                               int maxlen,
                                                               int32_t *__restrict__ order) {
     extern __shared__ int32_t bins[];  // maxlen + 1 bins
-    __shared__ int64_t part[kOrderThreads];
+    __shared__ int64_t wave_sums[kOrderThreads / 64];
     __shared__ int64_t below[kXcds];  // items starting below share x / 8 of the work
-    __shared__ int64_t total_work;
+    __shared__ int64_t total_work, total_bins;
     const int tid = threadIdx.x, x = blockIdx.x;
     auto length_of = [&](int64_t it) -> int {
         const int len = ulen[it];
@@ -238,23 +266,11 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *__r
     const int64_t c0 = min(items, tid * chunk), c1 = min(items, c0 + chunk);
     int64_t mine = 0;
     for (int64_t it = c0; it < c1; ++it) mine += length_of(it) + kItemCost;
-    part[tid] = mine;
     if (tid < kXcds) below[tid] = 0;
-    __syncthreads();
-    if (tid == 0) {
-        int64_t run = 0;
-        for (int i = 0; i < kOrderThreads; ++i) {
-            const int64_t v = part[i];
-            part[i] = run;
-            run += v;
-        }
-        total_work = run;
-    }
-    __syncthreads();
+    int64_t start = block_exclusive_scan(mine, wave_sums, &total_work);
     const int64_t total = total_work;
     // count, for every share, the items of this chunk starting below it
     {
-        int64_t start = part[tid];
         int64_t cnt[kXcds] = {};
         for (int64_t it = c0; it < c1; ++it) {
 #pragma unroll
@@ -277,11 +293,18 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *__r
     }
     for (int64_t it = lo + tid; it < hi; it += kOrderThreads) atomicAdd(&bins[length_of(it)], 1);
     __syncthreads();
-    if (tid == 0) {  // descending exclusive scan: longest lengths first
-        int run = 0;
-        for (int len = maxlen; len >= 0; --len) {
-            const int c = bins[len];
-            bins[len] = run;
+    // descending exclusive scan of the bins (longest lengths first): thread t
+    // owns a run of consecutive bins counted from the top
+    {
+        const int nbins = maxlen + 1;
+        const int per = (nbins + kOrderThreads - 1) / kOrderThreads;
+        const int b0 = tid * per, b1 = min(nbins, b0 + per);  // positions from the top
+        int64_t sum = 0;
+        for (int b = b0; b < b1; ++b) sum += bins[maxlen - b];
+        int64_t run = block_exclusive_scan(sum, wave_sums, &total_bins);
+        for (int b = b0; b < b1; ++b) {
+            const int c = bins[maxlen - b];
+            bins[maxlen - b] = (int)run;
             run += c;
         }
     }

@@ -69,17 +69,24 @@ __global__ __launch_bounds__(kEntThreads, 2) void token_entropy_kernel(
     for (int ks = 0; ks < KS; ++ks)
         qreg[ks] = *reinterpret_cast<const bf16x8_t *>(q + (head_tok + qtok) * D + 16 * ks + 8 * hl);
 
+    // Copy of key tile kb into a slot: each wave moves PPW 1 KB pieces with one
+    // global address and one wave-uniform LDS base, the pieces' 1 KB step in the
+    // instruction's immediate offset (it moves the global and the LDS address).
+    static_assert(PPW == 2 || PPW == 4, "pieces per wave");
     const size_t head_tiles = (size_t)h * g.nb;
-    const int wave_piece_bytes = wave * PPW * 1024, wave_piece_elems = wave * PPW * 512;
-    const int lane16 = lane * 16, lane8 = lane * 8;
+    const int wave_lds_bytes = __builtin_amdgcn_readfirstlane(wave * PPW * 1024);
+    const uint32_t lane_bytes = (uint32_t)(wave * PPW * 1024 + lane * 16);
+    const int lane8 = lane * 8;
     auto issue = [&](int kb, int slot) {
-        const char *s_ = reinterpret_cast<const char *>(kt + (head_tiles + kb) * 64 * D) +
-                         wave_piece_bytes + lane16;
-#pragma unroll
-        for (int i = 0; i < PPW; ++i)
-            __builtin_amdgcn_global_load_lds((const global_void_t *)(s_ + i * 1024),
-                                             (lds_void_t *)&kring[slot][wave_piece_elems + i * 512],
-                                             16, 0, 0);
+        const global_void_t *g_ = (const global_void_t *)(
+            reinterpret_cast<const char *>(kt + (head_tiles + kb) * 64 * D) + lane_bytes);
+        lds_void_t *l_ = (lds_void_t *)(reinterpret_cast<char *>(kring[slot]) + wave_lds_bytes);
+        __builtin_amdgcn_global_load_lds(g_, l_, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(g_, l_, 16, 1024, 0);
+        if constexpr (PPW == 4) {
+            __builtin_amdgcn_global_load_lds(g_, l_, 16, 2048, 0);
+            __builtin_amdgcn_global_load_lds(g_, l_, 16, 3072, 0);
+        }
     };
 
     issue(0, 0);

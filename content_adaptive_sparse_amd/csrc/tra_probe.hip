@@ -195,15 +195,30 @@ __global__ __launch_bounds__(256) void entropy_kernel(
 #pragma unroll
     for (int i = 0; i < 2; ++i) st[i] = EntState{-1e30f, 0.f, 0.f};
 
+    // Key chunks are double-buffered through registers: the next chunk's loads
+    // are in flight while the current one is computed from LDS.
+    constexpr int KCH = kEntK * D / 4 / 256;  // float4 per thread and chunk
+    static_assert(KCH * 256 * 4 == kEntK * D, "chunk split");
+    float4 stage[KCH];
+    auto load_chunk = [&](int c0) {
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            const int e = tid + 256 * i;
+            const int r = e / (D / 4), c4 = e % (D / 4);
+            stage[i] = c0 + r < g.nb ? reinterpret_cast<const float4 *>(kh + (size_t)(c0 + r) * D)[c4]
+                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    load_chunk(0);
     for (int c0 = 0; c0 < g.nb; c0 += kEntK) {
         __syncthreads();
-        for (int e = tid; e < kEntK * D / 4; e += 256) {
-            const int r = e / (D / 4), c4 = e % (D / 4);
-            float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (c0 + r < g.nb) val = reinterpret_cast<const float4 *>(kh + (size_t)(c0 + r) * D)[c4];
-            *reinterpret_cast<float4 *>(&Ks[r][4 * c4]) = val;
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            const int e = tid + 256 * i;
+            *reinterpret_cast<float4 *>(&Ks[e / (D / 4)][4 * (e % (D / 4))]) = stage[i];
         }
         __syncthreads();
+        if (c0 + kEntK < g.nb) load_chunk(c0 + kEntK);
         float s[2][4];
 #pragma unroll
         for (int i = 0; i < 2; ++i)

@@ -89,7 +89,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=1, help="workload id (tra_inputs.CONFIGS)")
+    ap.add_argument("--workload", default="wan13b_81f",
+                    help="workload slug (tra_inputs.WORKLOADS): tiny, wan13b_81f, wan13b_241f, "
+                         "wan14b_81f, hunyuan_129f")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU oracle sample budget (0 skips it)")
     ap.add_argument("--no-sweep", action="store_true")
@@ -109,11 +111,15 @@ def main():
     import content_adaptive_sparse_amd as tra
     import tra_inputs as ti
 
-    c = ti.CONFIGS[args.config]
+    wid = {w.slug: i for i, w in ti.WORKLOADS.items()}.get(args.workload)
+    if wid is None:
+        print(f"unknown workload {args.workload!r}", file=sys.stderr)
+        sys.exit(2)
+    c = ti.WORKLOADS[wid]
     T, H, W, heads, d = c.T, c.H, c.W, c.heads, c.d
     nby, nbx, nb = tra.tra_grid(T, H, W)
     log(f"[bench] workload {c.name}; generating inputs", )
-    q, k, v = ti.make_config_inputs(args.config)
+    q, k, v = ti.make_workload_inputs(wid)
 
     def dev(x):
         return torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
@@ -344,7 +350,7 @@ def main():
     mask_bytes = 4 * (heads * nb + pairs)
     mask_gbs = mask_bytes / (kern["mask"] * 1e-3) / 1e9 if kern["mask"] > 0 else None
 
-    workload_key = f"config{args.config}"
+    workload_key = c.slug
     traffic = measured_traffic(workload_key)
     res = {
         "metric": METRIC,

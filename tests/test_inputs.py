@@ -21,19 +21,19 @@ def test_bf16_rounding_matches_torch():
 
 
 def test_generator_deterministic_and_per_head():
-    q, k, v = ti.make_inputs(3, 9, 10, 3, 32, seed=0, cfg=7)
-    q2, k2, v2 = ti.make_inputs(3, 9, 10, 3, 32, seed=0, cfg=7)
+    q, k, v = ti.make_inputs(3, 9, 10, 3, 32, seed=0, family=7)
+    q2, k2, v2 = ti.make_inputs(3, 9, 10, 3, 32, seed=0, family=7)
     assert q.shape == (3, 3, 9, 10, 32) and q.dtype == np.uint16
     assert np.array_equal(q, q2) and np.array_equal(k, k2) and np.array_equal(v, v2)
-    qh, kh, vh = ti.make_inputs(3, 9, 10, 3, 32, seed=0, cfg=7, heads_only=[2])
+    qh, kh, vh = ti.make_inputs(3, 9, 10, 3, 32, seed=0, family=7, heads_only=[2])
     assert np.array_equal(qh[0], q[2]) and np.array_equal(kh[0], k[2]) and np.array_equal(vh[0], v[2])
-    q3, _, _ = ti.make_inputs(3, 9, 10, 3, 32, seed=1, cfg=7)
+    q3, _, _ = ti.make_inputs(3, 9, 10, 3, 32, seed=1, family=7)
     assert not np.array_equal(q, q3)
 
 
 @pytest.mark.parametrize("kind", ["smooth", "frames20", "bimodal80"])
 def test_sigma_maps(kind):
-    s = ti.sigma_map(10, 12, 14, kind, seed=0, cfg=1)
+    s = ti.sigma_map(10, 12, 14, kind, seed=0, family=1)
     assert s.shape == (10, 12, 14)
     assert s.min() >= 0.1 - 1e-12 and s.max() <= 1.0 + 1e-12
     if kind == "frames20":
@@ -45,7 +45,7 @@ def test_sigma_maps(kind):
 
 
 def test_config_table():
-    c = ti.CONFIGS[1]
+    c = ti.WORKLOADS[ti.WAN13B_81F]
     assert (c.T, c.H, c.W, c.heads, c.d, c.r_min, c.r_max) == (21, 30, 52, 12, 128, 1, 8)
     assert c.N == 32760
-    assert ti.CONFIGS[4].N == 118800
+    assert ti.WORKLOADS[ti.HUNYUAN_129F].N == 118800

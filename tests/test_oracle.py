@@ -103,7 +103,7 @@ def test_radius_quantiser_closed_form():
 
 def test_probe_entropy_matches_scipy():
     T, H, W, heads, d = 4, 12, 20, 2, 32
-    q, k, _ = ti.make_inputs(T, H, W, heads, d, seed=0, cfg=11)
+    q, k, _ = ti.make_inputs(T, H, W, heads, d, seed=0, family=11)
     hn, r = oracle.probe(q, k, 1, 8)
     ids, coords = tile_membership(T, H, W)
     nb = len(coords)
@@ -271,7 +271,7 @@ def test_attention_radius0_is_per_tile_attention():
 def test_attention_random_radii_vs_masked_sdpa(seed):
     rng = np.random.default_rng(100 + seed)
     T, H, W, heads, d = 5, 14, 18, 2, 16
-    q, k, v = ti.make_inputs(T, H, W, heads, d, seed=seed, cfg=12)
+    q, k, v = ti.make_inputs(T, H, W, heads, d, seed=seed, family=12)
     nb = oracle.grid_blocks(T, H, W)[2]
     radii = rng.integers(0, 3, size=(heads, nb)).astype(np.int32)
     got = oracle.attention(q, k, v, radii)

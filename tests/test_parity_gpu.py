@@ -147,7 +147,7 @@ def test_small_grid_staged_path(shape):
     heads, T, H, W, d = shape[3], shape[0], shape[1], shape[2], shape[4]
     shp = (heads, T, H, W, d)
     print(f"[case] staged {shp}", flush=True)
-    q, k, v = ti.make_inputs(T, H, W, heads, d, seed=1, cfg=21)
+    q, k, v = ti.make_inputs(T, H, W, heads, d, seed=1, family=21)
     qd, kd, vd = dev16(q), dev16(k), dev16(v)
     r_min, r_max = 0, 2
     hn_g, r_g = gpu_probe(qd, kd, shp, r_min, r_max)
@@ -191,17 +191,17 @@ def test_random_radii_and_dense(d):
     assert np.array_equal(wide, dense)
 
 
-def test_config0_end_to_end():
-    c = ti.CONFIGS[0]
+def test_tiny_workload_end_to_end():
+    c = ti.WORKLOADS[ti.TINY]
     shp = (c.heads, c.T, c.H, c.W, c.d)
-    print(f"[case] config0 {shp}", flush=True)
-    q, k, v = ti.make_config_inputs(0)
+    print(f"[case] tiny workload {shp}", flush=True)
+    q, k, v = ti.make_workload_inputs(ti.TINY)
     qd, kd, vd = dev16(q), dev16(k), dev16(v)
     hn_g, r_g = gpu_probe(qd, kd, shp, c.r_min, c.r_max)
     hn_o, r_o = oracle.probe(q, k, c.r_min, c.r_max)
-    check_radii(hn_g, r_g, hn_o, r_o, c.r_min, c.r_max, "config0 probe")
+    check_radii(hn_g, r_g, hn_o, r_o, c.r_min, c.r_max, "tiny workload probe")
     out = gpu_attention(qd, kd, vd, shp, c.r_min, c.r_max).cpu().numpy()
-    assert_close(out, oracle.attention(q, k, v, r_g), "config0 attention")
+    assert_close(out, oracle.attention(q, k, v, r_g), "tiny workload attention")
 
 
 # --------------------------------------------------------------- edge cases --
@@ -302,14 +302,14 @@ def test_plan_reuse_across_steps():
     shp = (heads, T, H, W, d)
     print(f"[case] plan reuse {shp}", flush=True)
     r_min, r_max = 0, 3
-    q0, k0, _ = ti.make_inputs(T, H, W, heads, d, seed=3, cfg=31)
+    q0, k0, _ = ti.make_inputs(T, H, W, heads, d, seed=3, family=31)
     hn, radii = gpu_probe(dev16(q0), dev16(k0), shp, r_min, r_max)
     idx, cnt, maxcnt = gpu_mask(radii, shp, r_max)
     plan = torch.empty(tra.tra_plan_bytes(T, H, W, heads, 64, maxcnt), dtype=torch.uint8,
                        device="cuda")
     tra.tra_plan(idx, cnt, maxcnt, T, H, W, heads, 64, plan)
     for step in range(2):
-        q, k, v = ti.make_inputs(T, H, W, heads, d, seed=40 + step, cfg=31)
+        q, k, v = ti.make_inputs(T, H, W, heads, d, seed=40 + step, family=31)
         qd, kd, vd = dev16(q), dev16(k), dev16(v)
         out = torch.full(shp, float("nan"), dtype=torch.float32, device="cuda")
         tra.tra_attn_plan(qd, kd, vd, T, H, W, heads, d, 64, plan, maxcnt, out)
@@ -378,7 +378,7 @@ def test_binary_routing():
     T, H, W, heads, d = 6, 32, 48, 2, 128
     shp = (heads, T, H, W, d)
     print(f"[case] binary routing {shp}", flush=True)
-    q, k, v = ti.make_inputs(T, H, W, heads, d, seed=5, cfg=32)
+    q, k, v = ti.make_inputs(T, H, W, heads, d, seed=5, family=32)
     nb = tra.tra_grid(T, H, W)[2]
     rng = np.random.default_rng(17)
     radii = np.where(rng.random((heads, nb)) < 0.2, INF, 1).astype(np.int32)
@@ -426,7 +426,7 @@ def test_mask_clamps_radius_to_r_max():
 def test_deterministic():
     T, H, W, heads, d = 3, 30, 52, 2, 128
     shp = (heads, T, H, W, d)
-    q, k, v = ti.make_inputs(T, H, W, heads, d, seed=2, cfg=22)
+    q, k, v = ti.make_inputs(T, H, W, heads, d, seed=2, family=22)
     qd, kd, vd = dev16(q), dev16(k), dev16(v)
     a = gpu_attention(qd, kd, vd, shp, 1, 3).cpu().numpy()
     b = gpu_attention(qd, kd, vd, shp, 1, 3).cpu().numpy()
@@ -438,46 +438,47 @@ def test_deterministic():
 _CACHE = {}
 
 
-def config_inputs(cfg):
-    if cfg not in _CACHE:
+def workload_inputs(wid):
+    if wid not in _CACHE:
         _CACHE.clear()
-        _CACHE[cfg] = ti.make_config_inputs(cfg)
-    return _CACHE[cfg]
+        _CACHE[wid] = ti.make_workload_inputs(wid)
+    return _CACHE[wid]
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
-def test_full_config(cfg):
-    c = ti.CONFIGS[cfg]
+@pytest.mark.parametrize("wid", [ti.WAN13B_81F, ti.WAN13B_241F, ti.WAN14B_81F, ti.HUNYUAN_129F],
+                         ids=lambda w: ti.WORKLOADS[w].slug)
+def test_full_workload(wid):
+    c = ti.WORKLOADS[wid]
     shp = (c.heads, c.T, c.H, c.W, c.d)
-    print(f"[case] config{cfg} {shp} r=[{c.r_min},{c.r_max}]", flush=True)
-    q, k, v = config_inputs(cfg)
+    print(f"[case] {c.slug} {shp} r=[{c.r_min},{c.r_max}]", flush=True)
+    q, k, v = workload_inputs(wid)
     qd, kd, vd = dev16(q), dev16(k), dev16(v)
     hn_g, r_g = gpu_probe(qd, kd, shp, c.r_min, c.r_max)
     hn_o, r_o = oracle.probe(q, k, c.r_min, c.r_max)
-    check_radii(hn_g, r_g, hn_o, r_o, c.r_min, c.r_max, f"config{cfg} probe")
+    check_radii(hn_g, r_g, hn_o, r_o, c.r_min, c.r_max, f"{c.slug} probe")
     idx, cnt, maxcnt = gpu_mask(r_g, shp, c.r_max)
-    check_lists(idx, cnt, r_g, shp, maxcnt, f"config{cfg} mask")
+    check_lists(idx, cnt, r_g, shp, maxcnt, f"{c.slug} mask")
     nb = tra.tra_grid(c.T, c.H, c.W)[2]
     density = cnt.sum().item() / (c.heads * nb * nb)
-    print(f"[parity] config{cfg}: block density {density:.4f}", flush=True)
+    print(f"[parity] {c.slug}: block density {density:.4f}", flush=True)
     del idx, cnt
     out = gpu_attention(qd, kd, vd, shp, c.r_min, c.r_max)
-    rows = sample_rows(shp, 96, seed=cfg)
+    rows = sample_rows(shp, 96, seed=wid)
     got = out.view(-1, c.d)[torch.from_numpy(rows).cuda()].cpu().numpy()
     del out
     ref = oracle.attention_rows(q, k, v, r_g, rows)
-    assert_close(got, ref, f"config{cfg} attention (sampled rows)")
+    assert_close(got, ref, f"{c.slug} attention (sampled rows)")
 
 
-def test_full_config1_dense_mode():
-    c = ti.CONFIGS[1]
+def test_wan13b_81f_dense_mode():
+    c = ti.WORKLOADS[ti.WAN13B_81F]
     shp = (c.heads, c.T, c.H, c.W, c.d)
-    print(f"[case] config1 dense {shp}", flush=True)
-    q, k, v = config_inputs(1)
+    print(f"[case] {c.slug} dense {shp}", flush=True)
+    q, k, v = workload_inputs(ti.WAN13B_81F)
     qd, kd, vd = dev16(q), dev16(k), dev16(v)
     out = gpu_attention(qd, kd, vd, shp, INF, INF)
     rows = sample_rows(shp, 48, seed=11)
     got = out.view(-1, c.d)[torch.from_numpy(rows).cuda()].cpu().numpy()
     nb = tra.tra_grid(c.T, c.H, c.W)[2]
     ref = oracle.attention_rows(q, k, v, oracle.dense_radii(c.heads, nb), rows)
-    assert_close(got, ref, "config1 dense (sampled rows)")
+    assert_close(got, ref, f"{c.slug} dense (sampled rows)")

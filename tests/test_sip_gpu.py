@@ -79,7 +79,7 @@ def test_sip_small_grids(case):
     T, H, W, heads, d, m = case
     shape = (heads, T, H, W, d)
     print(f"[case] sip {case}", flush=True)
-    q, k, v = ti.make_inputs(T, H, W, heads, d, seed=T * 7 + W, cfg=51)
+    q, k, v = ti.make_inputs(T, H, W, heads, d, seed=T * 7 + W, family=51)
     nb = tra.tra_grid(T, H, W)[2]
     u = np.random.default_rng(T + H).random((heads, nb, nb))
     idx, cnt, lw = gpu_sip(q, k, u, shape, m)
@@ -97,7 +97,7 @@ def test_sip_small_grids(case):
 def test_weighted_attention_with_zero_weights_is_tra_attn():
     T, H, W, heads, d = 3, 24, 40, 2, 128
     shape = (heads, T, H, W, d)
-    q, k, v = ti.make_inputs(T, H, W, heads, d, seed=12, cfg=52)
+    q, k, v = ti.make_inputs(T, H, W, heads, d, seed=12, family=52)
     nb = tra.tra_grid(T, H, W)[2]
     u = np.random.default_rng(9).random((heads, nb, nb))
     idx, cnt, _ = gpu_sip(q, k, u, shape, 4.0)
@@ -112,11 +112,11 @@ def test_weighted_attention_with_zero_weights_is_tra_attn():
 
 
 def test_sip_wan_layer_sampled():
-    c = ti.CONFIGS[1]
+    c = ti.WORKLOADS[ti.WAN13B_81F]
     shape = (c.heads, c.T, c.H, c.W, c.d)
     m = 64.0
     print(f"[case] sip {c.name}, m = {m}", flush=True)
-    q, k, v = ti.make_config_inputs(1)
+    q, k, v = ti.make_workload_inputs(ti.WAN13B_81F)
     nb = tra.tra_grid(c.T, c.H, c.W)[2]
     u = np.random.default_rng(3).random((c.heads, nb, nb)).astype(np.float32)
     idx, cnt, lw = gpu_sip(q, k, u, shape, m)

@@ -98,7 +98,7 @@ def test_token_policy_small_grids(case):
     T, H, W, heads, d, tau, gamma, mv = case
     shape = (heads, T, H, W, d)
     print(f"[case] token policy {case}", flush=True)
-    q, k, v = ti.make_inputs(T, H, W, heads, d, seed=T + H, cfg=41)
+    q, k, v = ti.make_inputs(T, H, W, heads, d, seed=T + H, family=41)
     ent_g, r0_g = gpu_token_probe(q, k, shape, tau, gamma)
     check_entropy(ent_g, r0_g, oracle.token_entropy(q, k), tau, gamma, f"token probe {case[:5]}")
     idx, cnt = gpu_token_mask(r0_g, shape, gamma, mv)
@@ -120,11 +120,11 @@ def test_token_policy_small_grids(case):
 
 
 def test_token_policy_wan_layer_sampled():
-    c = ti.CONFIGS[1]
+    c = ti.WORKLOADS[ti.WAN13B_81F]
     shape = (c.heads, c.T, c.H, c.W, c.d)
     tau, gamma, mv = 1.0, 0.5, 1
     print(f"[case] token policy {c.name}", flush=True)
-    q, k, v = ti.make_config_inputs(1)
+    q, k, v = ti.make_workload_inputs(ti.WAN13B_81F)
     ent_g, r0_g = gpu_token_probe(q, k, shape, tau, gamma)
     N = c.T * c.H * c.W
     rng = np.random.default_rng(7)

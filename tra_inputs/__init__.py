@@ -40,14 +40,20 @@ import math
 import numpy as np
 
 __all__ = [
-    "GridConfig",
-    "CONFIGS",
+    "Workload",
+    "WORKLOADS",
+    "TINY",
+    "WAN13B_81F",
+    "WAN13B_241F",
+    "WAN14B_81F",
+    "HUNYUAN_129F",
     "ELL_S",
     "ELL_T",
     "bf16_from_f32",
     "bf16_to_f32",
     "make_inputs",
-    "make_config_inputs",
+    "make_workload_inputs",
+    "aligned_qkv",
     "random_qkv",
     "sigma_map",
 ]
@@ -63,10 +69,11 @@ _S_FEAT, _S_QN, _S_KN, _S_V, _S_SIGMA, _S_SCALE = 0, 1, 2, 3, 4, 5
 
 
 @dataclasses.dataclass(frozen=True)
-class GridConfig:
+class Workload:
     """One benchmark/parity workload: grid, heads, head_dim and radius range."""
 
     name: str
+    slug: str
     T: int
     H: int
     W: int
@@ -83,16 +90,19 @@ class GridConfig:
         return self.T * self.H * self.W
 
 
-CONFIGS = {
-    0: GridConfig("tiny T8xH8xW8, 1 head, d64", 8, 8, 8, 1, 64, 0, 3),
-    1: GridConfig("Wan2.1-1.3B 480x832 81 frames (T21xH30xW52), 12 heads, d128",
-                  21, 30, 52, 12, 128, 1, 8),
-    2: GridConfig("Wan2.1-1.3B 241 frames (T61xH30xW52), 12 heads, d128",
-                  61, 30, 52, 12, 128, 1, 12, sigma="frames20"),
-    3: GridConfig("Wan2.1-14B 720x1280 81 frames (T21xH45xW80), 40 heads, d128",
-                  21, 45, 80, 40, 128, 1, 10, head_scale=(0.5, 4.0)),
-    4: GridConfig("HunyuanVideo 720x1280 129 frames (T33xH45xW80), 24 heads, d128",
-                  33, 45, 80, 24, 128, 0, 16, sigma="bimodal80"),
+# Workload ids; an id is also the family of its inputs' random streams.
+TINY, WAN13B_81F, WAN13B_241F, WAN14B_81F, HUNYUAN_129F = range(5)
+
+WORKLOADS = {
+    TINY: Workload("tiny T8xH8xW8, 1 head, d64", "tiny", 8, 8, 8, 1, 64, 0, 3),
+    WAN13B_81F: Workload("Wan2.1-1.3B 480x832 81 frames (T21xH30xW52), 12 heads, d128",
+                         "wan13b_81f", 21, 30, 52, 12, 128, 1, 8),
+    WAN13B_241F: Workload("Wan2.1-1.3B 241 frames (T61xH30xW52), 12 heads, d128",
+                          "wan13b_241f", 61, 30, 52, 12, 128, 1, 12, sigma="frames20"),
+    WAN14B_81F: Workload("Wan2.1-14B 720x1280 81 frames (T21xH45xW80), 40 heads, d128",
+                         "wan14b_81f", 21, 45, 80, 40, 128, 1, 10, head_scale=(0.5, 4.0)),
+    HUNYUAN_129F: Workload("HunyuanVideo 720x1280 129 frames (T33xH45xW80), 24 heads, d128",
+                           "hunyuan_129f", 33, 45, 80, 24, 128, 0, 16, sigma="bimodal80"),
 }
 
 
@@ -112,8 +122,8 @@ def bf16_to_f32(h) -> np.ndarray:
     return (h.astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def _rng(seed: int, cfg: int, head: int, stream: int) -> np.random.Generator:
-    ss = np.random.SeedSequence(seed, spawn_key=(cfg, head, stream))
+def _rng(seed: int, family: int, head: int, stream: int) -> np.random.Generator:
+    ss = np.random.SeedSequence(seed, spawn_key=(family, head, stream))
     return np.random.Generator(np.random.PCG64(ss))
 
 
@@ -136,9 +146,9 @@ def _smooth_field(T: int, H: int, W: int, rng: np.random.Generator) -> np.ndarra
     return u.reshape(T, H, W)
 
 
-def sigma_map(T: int, H: int, W: int, kind: str, seed: int = 0, cfg: int = 0) -> np.ndarray:
+def sigma_map(T: int, H: int, W: int, kind: str, seed: int = 0, family: int = 0) -> np.ndarray:
     """Per-token noise level sigma(t, y, x) in [0.1, 1.0], shape (T, H, W)."""
-    rng = _rng(seed, cfg, 0, _S_SIGMA)
+    rng = _rng(seed, family, 0, _S_SIGMA)
     if kind == "smooth":
         return 0.1 + 0.9 * _smooth_field(T, H, W, rng)
     if kind == "frames20":
@@ -157,7 +167,7 @@ def sigma_map(T: int, H: int, W: int, kind: str, seed: int = 0, cfg: int = 0) ->
 
 
 def make_inputs(T: int, H: int, W: int, heads: int, d: int, *, seed: int = 0,
-                cfg: int = 0, sigma: str = "smooth", head_scale=None,
+                family: int = 0, sigma: str = "smooth", head_scale=None,
                 ell_s: float = ELL_S, ell_t: float = ELL_T, heads_only=None):
     """Fourier-feature q/k plus N(0,1) v as bf16 bit patterns ``[heads][T][H][W][d]``.
 
@@ -165,9 +175,9 @@ def make_inputs(T: int, H: int, W: int, heads: int, d: int, *, seed: int = 0,
     order; each head's values are identical to the full generation's.
     """
     pos = _positions(T, H, W)
-    sig = sigma_map(T, H, W, sigma, seed, cfg).reshape(-1, 1).astype(np.float32)
+    sig = sigma_map(T, H, W, sigma, seed, family).reshape(-1, 1).astype(np.float32)
     if head_scale is not None:
-        s_all = _rng(seed, cfg, 0, _S_SCALE).uniform(head_scale[0], head_scale[1], size=heads)
+        s_all = _rng(seed, family, 0, _S_SCALE).uniform(head_scale[0], head_scale[1], size=heads)
     else:
         s_all = np.ones(heads)
     hlist = list(range(heads)) if heads_only is None else list(heads_only)
@@ -177,26 +187,26 @@ def make_inputs(T: int, H: int, W: int, heads: int, d: int, *, seed: int = 0,
     v = np.empty_like(q)
     inv_ell = np.array([1.0 / ell_t, 1.0 / ell_s, 1.0 / ell_s])
     for slot, h in enumerate(hlist):
-        rf = _rng(seed, cfg, h, _S_FEAT)
+        rf = _rng(seed, family, h, _S_FEAT)
         g = rf.standard_normal((16, 3))
         b = rf.uniform(0.0, 2.0 * math.pi, size=16)
         P = rf.standard_normal((16, d)) / 4.0  # N(0, 1/16)
         omega = s_all[h] * g * inv_ell
         phi_raw = math.sqrt(2.0) * np.cos(pos @ omega.T + b)
         phi = (phi_raw @ P).astype(np.float32)
-        eq = _rng(seed, cfg, h, _S_QN).standard_normal((N, d), dtype=np.float32)
-        ek = _rng(seed, cfg, h, _S_KN).standard_normal((N, d), dtype=np.float32)
-        ev = _rng(seed, cfg, h, _S_V).standard_normal((N, d), dtype=np.float32)
+        eq = _rng(seed, family, h, _S_QN).standard_normal((N, d), dtype=np.float32)
+        ek = _rng(seed, family, h, _S_KN).standard_normal((N, d), dtype=np.float32)
+        ev = _rng(seed, family, h, _S_V).standard_normal((N, d), dtype=np.float32)
         q[slot] = bf16_from_f32(phi + sig * eq).reshape(T, H, W, d)
         k[slot] = bf16_from_f32(phi + sig * ek).reshape(T, H, W, d)
         v[slot] = bf16_from_f32(ev).reshape(T, H, W, d)
     return q, k, v
 
 
-def make_config_inputs(cfg_id: int, seed: int = 0, heads_only=None):
-    """q, k, v for one of the named workloads in ``CONFIGS``."""
-    c = CONFIGS[cfg_id]
-    return make_inputs(c.T, c.H, c.W, c.heads, c.d, seed=seed, cfg=cfg_id,
+def make_workload_inputs(wid: int, seed: int = 0, heads_only=None):
+    """q, k, v for one of the named workloads in ``WORKLOADS``."""
+    c = WORKLOADS[wid]
+    return make_inputs(c.T, c.H, c.W, c.heads, c.d, seed=seed, family=wid,
                        sigma=c.sigma, head_scale=c.head_scale, heads_only=heads_only)
 
 

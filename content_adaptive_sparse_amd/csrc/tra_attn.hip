@@ -61,8 +61,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     // Work item: a pair of vertically adjacent query blocks of one head.
     // Consecutive workgroup ids land on different XCDs; every XCD is given a
     // contiguous range of items so its L2 sees neighbouring query blocks.  With
-    // a work order (lists of unequal length) each range is taken longest first;
-    // without one (dense mode: equal work) in raster order.
+    // a work order (lists of unequal length) the ranges hold equal shares of
+    // the total work and each is taken longest first; without one (dense mode:
+    // equal work) the ranges hold equal item counts in raster order.
     const int64_t total = (int64_t)heads * pairs_per_head;
     int64_t item;
     if (order) {

@@ -260,7 +260,7 @@ enum tra_kernel_kind {
     TRA_KERNEL_MASK = 2,      /* radius -> key-block lists */
     TRA_KERNEL_ATTN = 3,      /* block-sparse attention */
     TRA_KERNEL_FILL = 4,      /* dense-mode radius fill */
-    TRA_KERNEL_ORDER = 5,     /* longest-first order of the attention work items */
+    TRA_KERNEL_ORDER = 5,     /* work order: equal-work XCD ranges, longest first */
     TRA_KERNEL_UNION = 6,     /* union walk of each pair of query blocks' lists */
     TRA_KERNEL_TOKEN_ENTROPY = 7, /* per-token entropy and base radius (warm-up) */
     TRA_KERNEL_TOKEN_MASK = 8,    /* token-disk voting lists */

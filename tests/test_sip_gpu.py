@@ -94,6 +94,28 @@ def test_sip_small_grids(case):
     assert_close(out.cpu().numpy().reshape(-1, d), ref, f"sip attention {case[:5]}")
 
 
+@pytest.mark.parametrize("mixed", [False, True], ids=["negative", "mixed"])
+def test_sip_negative_logit_rows(mixed):
+    # Sampling and weighted attention where every logit of a row is far below
+    # zero (or rows of both signs side by side), on a ragged grid.
+    T, H, W, heads, d, m = 3, 20, 28, 2, 128, 3.0
+    shape = (heads, T, H, W, d)
+    print(f"[case] sip, negative logits {shape} mixed={mixed}", flush=True)
+    q, k, v = ti.aligned_qkv(T, H, W, heads, d, seed=19, mixed_signs=mixed)
+    nb = tra.tra_grid(T, H, W)[2]
+    u = np.random.default_rng(5).random((heads, nb, nb))
+    idx, cnt, lw = gpu_sip(q, k, u, shape, m)
+    check_sip(q, k, u, m, idx, cnt, lw, f"sip lists, negative logits {shape}")
+    out = torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
+    tra.tra_attn_weighted(dev16(q), dev16(k), dev16(v), T, H, W, heads, d, 64,
+                          torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(),
+                          torch.from_numpy(lw).cuda(), nb, out)
+    torch.cuda.synchronize()
+    rows = np.arange(heads * T * H * W)
+    ref = oracle.attention_lists_rows(q, k, v, idx, cnt, rows, lw=lw.astype(np.float64))
+    assert_close(out.cpu().numpy().reshape(-1, d), ref, f"sip attention, negative logits {shape}")
+
+
 def test_weighted_attention_with_zero_weights_is_tra_attn():
     T, H, W, heads, d = 3, 24, 40, 2, 128
     shape = (heads, T, H, W, d)

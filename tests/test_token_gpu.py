@@ -119,6 +119,20 @@ def test_token_policy_small_grids(case):
     assert_close(out.cpu().numpy().reshape(-1, d), ref, f"token attention {case[:5]}")
 
 
+@pytest.mark.parametrize("mixed", [False, True], ids=["negative", "mixed"])
+def test_token_entropy_negative_logit_rows(mixed):
+    # Rows whose every logit is far below zero (and, mixed, rows of both signs
+    # side by side) on ragged grids: a padded key must never stand in for a
+    # row's max, and the base-2 online state must not lose the row.
+    for T, H, W, heads, d in ((3, 20, 28, 2, 128), (2, 13, 9, 1, 64)):
+        shape = (heads, T, H, W, d)
+        print(f"[case] token entropy, negative logits {shape} mixed={mixed}", flush=True)
+        q, k, _ = ti.aligned_qkv(T, H, W, heads, d, seed=17, mixed_signs=mixed)
+        ent_g, r0_g = gpu_token_probe(q, k, shape, 1.0, 0.5)
+        check_entropy(ent_g, r0_g, oracle.token_entropy(q, k), 1.0, 0.5,
+                      f"token probe, negative logits {shape}")
+
+
 def test_token_policy_wan_layer_sampled():
     c = ti.WORKLOADS[ti.WAN13B_81F]
     shape = (c.heads, c.T, c.H, c.W, c.d)

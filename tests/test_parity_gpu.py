@@ -139,6 +139,8 @@ SMALL = [
     (1, 5, 7, 1, 64),      # one partial tile: nb = 1
     (1, 1, 1, 2, 128),     # a single token
     (5, 8, 8, 1, 128),     # one tile per frame
+    (2, 8, 200, 1, 128),   # one tile row of 25 tiles: no pair has its lower block
+    (2, 70, 6, 2, 64),     # one ragged tile column of 9 tiles: the last pair is single
 ]
 
 

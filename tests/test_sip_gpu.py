@@ -71,6 +71,8 @@ SMALL = [
     (2, 13, 9, 1, 64, 1.5),
     (4, 16, 24, 2, 128, 0.5),
     (5, 8, 8, 1, 128, 1e9),
+    (2, 8, 200, 1, 128, 4.0),   # one tile row: no pair has its lower block
+    (2, 70, 6, 2, 64, 2.0),     # one ragged tile column of 9 tiles
 ]
 
 

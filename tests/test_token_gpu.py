@@ -90,6 +90,8 @@ SMALL = [
     (4, 16, 24, 2, 128, 0.3, 1.0, 8),
     (1, 5, 7, 1, 64, 1.0, 0.5, 1),
     (5, 8, 8, 1, 128, 2.0, 0.2, 64),
+    (2, 8, 200, 1, 128, 1.0, 0.5, 1),   # one tile row: no pair has its lower block
+    (2, 70, 6, 1, 64, 1.0, 0.3, 1),     # one ragged tile column of 9 tiles
 ]
 
 

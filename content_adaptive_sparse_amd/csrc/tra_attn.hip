@@ -84,16 +84,21 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     const int side = wave >> 1;          // which block of the pair this wave computes
     const int qb = blk[side];            // -1: absent (odd tile-row count)
 
-    // This lane's query token (clamped into the grid for the missing cells of
-    // an edge tile, and for an absent block; such rows are never stored).
+    // This lane's query token.  The real queries of a block are numbered
+    // first (row-major over the tile's real rows and columns), so an edge tile
+    // with at most 32 of them leaves its second wave without work.  Lanes past
+    // the real queries (and an absent block) take a clamped token and never
+    // store.
     const int plane = g.nby * g.nbx;
     const int qbc = qb >= 0 ? qb : blk[0];
     const int t = qbc / plane, by = (qbc / g.nbx) % g.nby, bx = qbc % g.nbx;
-    const int qi = 32 * (wave & 1) + l32;
-    const int qy = kTileSide * by + (qi >> 3), qx = kTileSide * bx + (qi & 7);
-    const bool qreal = qb >= 0 && qy < g.H && qx < g.W;
-    const size_t qtok = (size_t)h * g.T * g.H * g.W +
-                        ((size_t)t * g.H + min(qy, g.H - 1)) * g.W + min(qx, g.W - 1);
+    const int qny = min(kTileSide, g.H - kTileSide * by), qnx = min(kTileSide, g.W - kTileSide * bx);
+    const int nq = qb >= 0 ? qny * qnx : 0;
+    const bool live = 32 * (wave & 1) < nq;  // this wave has real queries
+    const int qi = min(32 * (wave & 1) + l32, qny * qnx - 1);
+    const bool qreal = 32 * (wave & 1) + l32 < nq;
+    const int qy = kTileSide * by + qi / qnx, qx = kTileSide * bx + qi % qnx;
+    const size_t qtok = (size_t)h * g.T * g.H * g.W + ((size_t)t * g.H + qy) * g.W + qx;
     float *o = out + qtok * D;
 
     // The item's union walk: n entries (block << 2) | sides (bit 0: the upper
@@ -299,7 +304,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     // pipeline (e0 == -1).
     int u = 0;
     auto step = [&](auto slot_tag) -> bool {
-        const bool mine = e0 >= 0 && ((e0 >> side) & 1);
+        const bool mine = live && e0 >= 0 && ((e0 >> side) & 1);
         if (mine) {
             if (prev_mine) work(slot_tag, T1{}, T1{});
             else work(slot_tag, T1{}, T0{});

@@ -58,10 +58,16 @@ __global__ __launch_bounds__(kEntThreads, 2) void token_entropy_kernel(
     const int plane = g.nby * g.nbx;
     const int qbc = qb >= 0 ? qb : blk[0];
     const int t = qbc / plane, by = (qbc / g.nbx) % g.nby, bx = qbc % g.nbx;
-    const int qi = 32 * (wave & 1) + l32;
-    const int qy = kTileSide * by + (qi >> 3), qx = kTileSide * bx + (qi & 7);
-    const bool qreal = qb >= 0 && qy < g.H && qx < g.W;
-    const size_t qtok = ((size_t)t * g.H + min(qy, g.H - 1)) * g.W + min(qx, g.W - 1);
+    // The block's real queries are numbered first (row-major over the tile's
+    // real rows and columns): a tile with at most 32 leaves its second wave
+    // without queries, and that wave only helps with the copies.
+    const int qny = min(kTileSide, g.H - kTileSide * by), qnx = min(kTileSide, g.W - kTileSide * bx);
+    const int nq = qb >= 0 ? qny * qnx : 0;
+    const bool live = 32 * (wave & 1) < nq;
+    const int qi = min(32 * (wave & 1) + l32, qny * qnx - 1);
+    const bool qreal = 32 * (wave & 1) + l32 < nq;
+    const int qy = kTileSide * by + qi / qnx, qx = kTileSide * bx + qi % qnx;
+    const size_t qtok = ((size_t)t * g.H + qy) * g.W + qx;
     const size_t head_tok = (size_t)h * g.T * g.H * g.W;
 
     bf16x8_t qreg[KS];
@@ -100,54 +106,56 @@ __global__ __launch_bounds__(kEntThreads, 2) void token_entropy_kernel(
 
     float m_ref = -1e30f, Z = 0.f, A = 0.f;
     for (int kb = 0; kb < g.nb; ++kb) {
-        const uint16_t *Kt = kring[kb & 1];
-        f32x16_t sb[2];
+        if (live) {  // a wave without real queries only copies
+            const uint16_t *Kt = kring[kb & 1];
+            f32x16_t sb[2];
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
+            for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sb[hf][r] = 0.f;
+                for (int r = 0; r < 16; ++r) sb[hf][r] = 0.f;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8_t ka = lds_load16<bf16x8_t>(Kt + (hf * KS + ks) * 512 + lane8);
-                sb[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], sb[hf], 0, 0, 0);
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf16x8_t ka = lds_load16<bf16x8_t>(Kt + (hf * KS + ks) * 512 + lane8);
+                    sb[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], sb[hf], 0, 0, 0);
+                }
             }
-        }
-        const uint32_t row = fdiv((uint32_t)kb, div_nbx);
-        const int kbx = (int)((uint32_t)kb - row * div_nbx.d);
-        const int kby = (int)(row - fdiv(row, div_nby) * div_nby.d);
-        mask_edge_keys(sb, min(kTileSide, g.H - kTileSide * kby),
-                       min(kTileSide, g.W - kTileSide * kbx), hl, kMaskedLogit);
-        float mx = -INFINITY;
+            const uint32_t row = fdiv((uint32_t)kb, div_nbx);
+            const int kbx = (int)((uint32_t)kb - row * div_nbx.d);
+            const int kby = (int)(row - fdiv(row, div_nby) * div_nby.d);
+            mask_edge_keys(sb, min(kTileSide, g.H - kTileSide * kby),
+                           min(kTileSide, g.W - kTileSide * kbx), hl, kMaskedLogit);
+            float mx = -INFINITY;
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
+            for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sb[hf][r]);
-        mx = half_swap_max(mx) * scale_log2;
-        const bool grow = mx > m_ref + kRefLog2;
-        if (__any(grow)) {
-            // moving the reference from m to m': Z' = 2^(m - m') Z,
-            // A' = 2^(m - m') (A + (m - m') Z)
-            const float m_new = grow ? mx : m_ref;
-            const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-            A = alpha * __builtin_fmaf(m_ref - m_new, Z, A);
-            Z *= alpha;
-            m_ref = m_new;
-        }
-        float z0 = 0.f, z1 = 0.f, a0 = 0.f, a1 = 0.f;
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const float x0 = __builtin_fmaf(sb[hf][r], scale_log2, -m_ref);
-                const float x1 = __builtin_fmaf(sb[hf][r + 1], scale_log2, -m_ref);
-                const float e0 = __builtin_amdgcn_exp2f(x0), e1 = __builtin_amdgcn_exp2f(x1);
-                z0 += e0;
-                z1 += e1;
-                a0 = __builtin_fmaf(e0, x0, a0);
-                a1 = __builtin_fmaf(e1, x1, a1);
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sb[hf][r]);
+            mx = half_swap_max(mx) * scale_log2;
+            const bool grow = mx > m_ref + kRefLog2;
+            if (__any(grow)) {
+                // moving the reference from m to m': Z' = 2^(m - m') Z,
+                // A' = 2^(m - m') (A + (m - m') Z)
+                const float m_new = grow ? mx : m_ref;
+                const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+                A = alpha * __builtin_fmaf(m_ref - m_new, Z, A);
+                Z *= alpha;
+                m_ref = m_new;
             }
-        Z += z0 + z1;
-        A += a0 + a1;
+            float z0 = 0.f, z1 = 0.f, a0 = 0.f, a1 = 0.f;
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    const float x0 = __builtin_fmaf(sb[hf][r], scale_log2, -m_ref);
+                    const float x1 = __builtin_fmaf(sb[hf][r + 1], scale_log2, -m_ref);
+                    const float e0 = __builtin_amdgcn_exp2f(x0), e1 = __builtin_amdgcn_exp2f(x1);
+                    z0 += e0;
+                    z1 += e1;
+                    a0 = __builtin_fmaf(e0, x0, a0);
+                    a1 = __builtin_fmaf(e1, x1, a1);
+                }
+            Z += z0 + z1;
+            A += a0 + a1;
+        }
         if (kb + 1 == g.nb) break;
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // the next tile has landed
         __syncthreads();                          // and every wave is done with this one

@@ -171,6 +171,19 @@ def main():
         log(f"[bench] dense layer {ms_dense:.3f} ms")
         return
 
+    # per-step spread of the layer time (a separate pass: one event between
+    # consecutive layers on the launch stream)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(args.steps):
+        layer(c.r_min, c.r_max)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
+    step_median, step_min = float(np.median(per_step)), float(np.min(per_step))
+    log(f"[bench] layer per step: median {step_median:.3f} ms, min {step_min:.3f} ms")
+
     # realised radii / lists of the probe (same kernels as inside the layer)
     radius = torch.empty(heads, nb, dtype=torch.int32, device="cuda")
     tra.tra_probe(qd, kd, T, H, W, heads, d, 64, c.r_min, c.r_max, radius)
@@ -399,6 +412,8 @@ def main():
             "sip_sweep": sip,
             "l1_vs_dense_by_scheme": quality,
             "wall_ms_per_step": round(ms_wall, 4),
+            "layer_ms_median": round(step_median, 4),
+            "layer_ms_min": round(step_min, 4),
             "pv_dtype": "fp16",
         },
     }

@@ -53,6 +53,18 @@ def measured_traffic(workload_key):
     return rec.get("bytes_per_launch")
 
 
+def cpu_model():
+    """The host CPU's model name (first entry of /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(q, k, v, c, budget_s):
     """fp64 oracle on a bounded sample: full probe and block lists, then
     attention rows until about budget_s seconds; extrapolated to one layer."""
@@ -77,6 +89,7 @@ def cpu_baseline(q, k, v, c, budget_s):
         "value": round(ms_layer, 1),
         "unit": "ms/layer",
         "cores": oracle.num_threads(),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"full fp64 probe + block lists ({t_fixed:.1f} s), then {rows_done} of "
                    f"{total_rows} query rows of masked attention on the same radii "

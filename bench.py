@@ -210,16 +210,45 @@ def main():
     rhist = np.bincount(radius.cpu().numpy().ravel(), minlength=c.r_max + 1).tolist()
     del idx
 
-    kern = profiled(lambda: layer(c.r_min, c.r_max), max(5, args.steps // 2))
-    t_attn = kern["attn"]
+    # ---- the attention kernel alone: `reps` back-to-back launches along the
+    # probe radii's walk plan between one pair of HIP events on the launch
+    # stream (no per-kernel brackets); the same for the dense mode ----
+    reps = max(10, args.steps)
+    idx = torch.empty(heads, nb, maxcnt, dtype=torch.int32, device="cuda")
+    tra.tra_mask(radius, T, H, W, heads, 64, c.r_max, idx, cnt)
+    t_attn = tra.tra_time_attn(qd, kd, vd, T, H, W, heads, d, 64, idx, cnt, None, maxcnt, reps, out)
+    t_dense_attn = tra.tra_time_attn(qd, kd, vd, T, H, W, heads, d, 64, None, None, None, 0, reps,
+                                     out)
     achieved = flops_pair * pairs / (t_attn * 1e-3) / 1e12
-    log(f"[bench] kernels (ms): {kern}; density {density:.4f}; attn {achieved:.1f} TFLOP/s")
+    dense_tflops = flops_pair * heads * nb * nb / (t_dense_attn * 1e-3) / 1e12
+    # the same launch counted three ways: per computed 64 x 64 block pair (the
+    # headline), per matrix-core product actually issued (a wave whose 32
+    # queries are all padding issues none), and per real (query, key) token pair
+    cn_h = cnt.cpu().numpy().astype(np.int64)
+    ix_h = idx.cpu().numpy()
+    qn = np.array([min(8, H - 8 * ((b // nbx) % nby)) * min(8, W - 8 * (b % nbx)) for b in range(nb)])
+    waves = (qn + 31) // 32
+    mfma_flops = 4 * 32 * 64 * d * int((cn_h * waves[None, :]).sum())
+    kreal = np.zeros(heads * nb, dtype=np.int64)
+    for h in range(heads):
+        for b in range(nb):
+            kreal[h * nb + b] = qn[ix_h[h, b, :cn_h[h, b]]].sum()
+    real_flops = 4 * d * int((kreal.reshape(heads, nb) * qn[None, :]).sum())
+    del idx, ix_h
+    log(f"[bench] attention kernel {t_attn:.4f} ms ({achieved:.1f} TFLOP/s on computed blocks), "
+        f"dense {t_dense_attn:.4f} ms ({dense_tflops:.1f} TFLOP/s)")
+
+    # diagnostic only: every kernel of the layer bracketed by its own event pair
+    # (the brackets add their own gaps, so these sum to more than the layer)
+    kern = profiled(lambda: layer(c.r_min, c.r_max), max(5, args.steps // 2))
+    log(f"[bench] bracketed kernels (ms): {kern}; density {density:.4f}")
 
     # ---- dense mode of the same kernel ----
     ms_dense, _ = timed(lambda: layer(INF, INF), max(3, args.steps // 2), 2)
-    kd_ = profiled(lambda: layer(INF, INF), 3)
-    dense_tflops = flops_pair * heads * nb * nb / (kd_["attn"] * 1e-3) / 1e12
-    log(f"[bench] dense layer {ms_dense:.3f} ms, attn {kd_['attn']:.3f} ms = {dense_tflops:.1f} TFLOP/s")
+    log(f"[bench] dense layer {ms_dense:.3f} ms")
+
+    def attn_time(ix, cn, mc, lw=None):
+        return tra.tra_time_attn(qd, kd, vd, T, H, W, heads, d, 64, ix, cn, lw, mc, 10, out)
 
     # ---- injected-radius density sweep (attention kernel only) ----
     sweep = []
@@ -237,11 +266,11 @@ def main():
             tra.tra_mask(rd, T, H, W, heads, 64, rmax, ix, cn)
             torch.cuda.synchronize()
             p = int(cn.sum().item())
-            kk = profiled(lambda: tra.tra_attn(qd, kd, vd, T, H, W, heads, d, 64, ix, cn, mc, out), 5)
+            ta = attn_time(ix, cn, mc)
             sweep.append({"radii": name, "density": round(p / (heads * nb * nb), 4),
-                          "attn_ms": round(kk["attn"], 4),
-                          "tflops": round(flops_pair * p / (kk["attn"] * 1e-3) / 1e12, 1),
-                          "speedup_vs_dense_attn": round(kd_["attn"] / kk["attn"], 2)})
+                          "attn_ms": round(ta, 4),
+                          "tflops": round(flops_pair * p / (ta * 1e-3) / 1e12, 1),
+                          "speedup_vs_dense_attn": round(t_dense_attn / ta, 2)})
             log(f"[bench] sweep {sweep[-1]}")
             del ix, cn
 
@@ -277,51 +306,58 @@ def main():
         torch.cuda.synchronize()
         cnn = cn.cpu().numpy()
         p = int(cnn.sum())
-        kk = profiled(lambda: tra.tra_attn(qd, kd, vd, T, H, W, heads, d, 64, ix, cn, nb, out), 5)
+        ta = attn_time(ix, cn, nb)
         routing = {"dense_blocks": round(float((rr == INF).mean()), 4), "local_radius": 1,
                    "density": round(p / (heads * nb * nb), 4),
                    "list_len_min_mean_max": [int(cnn.min()), round(float(cnn.mean()), 1), int(cnn.max())],
-                   "attn_ms": round(kk["attn"], 4),
-                   "tflops": round(flops_pair * p / (kk["attn"] * 1e-3) / 1e12, 1),
-                   "speedup_vs_dense_attn": round(kd_["attn"] / kk["attn"], 2)}
+                   "attn_ms": round(ta, 4),
+                   "tflops": round(flops_pair * p / (ta * 1e-3) / 1e12, 1),
+                   "speedup_vs_dense_attn": round(t_dense_attn / ta, 2)}
         log(f"[bench] binary routing {routing}")
         route_lists = (ix, cn)
         del rd
 
-    # ---- token-level radius policy: entropy warm-up, voting mask, attention on
-    # the voted lists (first step), then steps reusing those lists ----
+    # ---- token-level radius policy: the warm-up (dense attention with every
+    # token's entropy and base radius in the same pass, then the voting mask and
+    # the walk plan), then steps reusing those lists ----
     token = None
     if not args.no_sweep:
         tau, gamma, mv = 1.0, 0.5, 1
         N = T * H * W
         ent = torch.empty(heads, T, H, W, dtype=torch.float32, device="cuda")
         r0 = torch.empty_like(ent)
-        kp = profiled(lambda: tra.tra_token_probe(qd, kd, T, H, W, heads, d, 64, tau, gamma, ent, r0), 3)
         ix = torch.empty(heads, nb, nb, dtype=torch.int32, device="cuda")
         cn = torch.empty(heads, nb, dtype=torch.int32, device="cuda")
-        km = profiled(lambda: tra.tra_token_mask(r0, T, H, W, heads, 64, gamma, mv, ix, cn), 3)
+        plan = torch.empty(tra.tra_plan_bytes(T, H, W, heads, 64, nb), dtype=torch.uint8, device="cuda")
+
+        def warmup_step():
+            tra.tra_token_warmup(qd, kd, vd, T, H, W, heads, d, 64, tau, gamma, out, ent, r0)
+            tra.tra_token_mask(r0, T, H, W, heads, 64, gamma, mv, ix, cn)
+            tra.tra_plan(ix, cn, nb, T, H, W, heads, 64, plan)
+
+        ms_warm_attn, _ = timed(lambda: tra.tra_token_warmup(qd, kd, vd, T, H, W, heads, d, 64, tau,
+                                                             gamma, out, ent, r0), 5, 1)
+        ms_warm, _ = timed(warmup_step, 5, 1)
+        kp = profiled(lambda: tra.tra_token_probe(qd, kd, T, H, W, heads, d, 64, tau, gamma, ent, r0), 3)
         torch.cuda.synchronize()
         p = int(cn.sum().item())
-        ka = profiled(lambda: tra.tra_attn(qd, kd, vd, T, H, W, heads, d, 64, ix, cn, nb, out), 5)
-        ms_first, _ = timed(lambda: tra.tra_token_attention(qd, kd, vd, T, H, W, heads, d, 64, tau,
-                                                            gamma, mv, out), 3, 1)
-        plan = torch.empty(tra.tra_plan_bytes(T, H, W, heads, 64, nb), dtype=torch.uint8, device="cuda")
-        tra.tra_plan(ix, cn, nb, T, H, W, heads, 64, plan)
+        ta = attn_time(ix, cn, nb)
         ms_step, _ = timed(lambda: tra.tra_attn_plan(qd, kd, vd, T, H, W, heads, d, 64, plan, nb, out),
                            max(5, args.steps // 2), 2)
-        # the warm-up's Q.K^T covers every key tile of every query block pair
-        ent_flops = 2 * 64 * 64 * d * heads * nb * nb
+        ms_one_call, _ = timed(lambda: tra.tra_token_attention(qd, kd, vd, T, H, W, heads, d, 64, tau,
+                                                               gamma, mv, out), 3, 1)
         token = {"tau": tau, "gamma": gamma, "min_votes": mv,
                  "entropy_h_mean": round(float(ent.mean().item()), 3), "ln_N": round(math.log(N), 3),
                  "density": round(p / (heads * nb * nb), 4),
-                 "warmup_entropy_ms": round(kp["token_entropy"], 4),
-                 "warmup_entropy_tflops": round(ent_flops / (kp["token_entropy"] * 1e-3) / 1e12, 1),
-                 "mask_ms": round(km["token_mask"], 4),
-                 "attn_ms": round(ka["attn"], 4),
-                 "attn_tflops": round(flops_pair * p / (ka["attn"] * 1e-3) / 1e12, 1),
-                 "first_step_ms": round(ms_first, 4),
+                 "warmup_step_ms": round(ms_warm, 4),
+                 "warmup_dense_attn_with_entropy_ms": round(ms_warm_attn, 4),
+                 "warmup_step_vs_dense_layer": round(ms_warm / ms_dense, 3),
+                 "separate_entropy_pass_ms": round(kp["token_entropy"], 4),
+                 "attn_ms": round(ta, 4),
+                 "attn_tflops": round(flops_pair * p / (ta * 1e-3) / 1e12, 1),
                  "reuse_step_ms": round(ms_step, 4),
-                 "reuse_speedup_vs_dense_layer": round(ms_dense / ms_step, 3)}
+                 "reuse_speedup_vs_dense_layer": round(ms_dense / ms_step, 3),
+                 "one_call_ms": round(ms_one_call, 4)}
         log(f"[bench] token policy {token}")
         del ix, cn, plan, ent, r0
 
@@ -346,12 +382,12 @@ def main():
             ks = profiled(lambda: tra.tra_sip_mask(qd, kd, u, T, H, W, heads, d, 64, m, ix, cn, lw), 3)
             torch.cuda.synchronize()
             p = int(cn.sum().item())
-            kw = profiled(lambda: tra.tra_attn_weighted(qd, kd, vd, T, H, W, heads, d, 64, ix, cn, lw,
-                                                        nb, out), 5)
+            ta = attn_time(ix, cn, nb, lw)
+            tra.tra_attn_weighted(qd, kd, vd, T, H, W, heads, d, 64, ix, cn, lw, nb, out)
             sip.append({"m": m, "density": round(p / (heads * nb * nb), 4),
                         "sip_mask_ms": round(ks["sip"] + ks["entropy"] + ks["pack_pool"], 4),
-                        "attn_ms": round(kw["attn"], 4),
-                        "tflops": round(flops_pair * p / (kw["attn"] * 1e-3) / 1e12, 1),
+                        "attn_ms": round(ta, 4),
+                        "tflops": round(flops_pair * p / (ta * 1e-3) / 1e12, 1),
                         "l1_vs_dense": l1_vs_dense()})
             log(f"[bench] sip {sip[-1]}")
         del ix, cn, lw, u
@@ -411,9 +447,16 @@ def main():
             "block_density": round(density, 4),
             "computed_block_pairs": pairs,
             "radius_histogram": rhist,
-            "kernel_ms": {kk: round(vv, 4) for kk, vv in kern.items() if vv},
+            "attn_ms": round(t_attn, 4),
+            "attn_timing": (f"mean of {reps} back-to-back attention launches between one HIP event "
+                            "pair on the launch stream (tra_time_attn)"),
+            "mfma_executed_tflops_attn": round(mfma_flops / (t_attn * 1e-3) / 1e12, 1),
+            "real_token_tflops_attn": round(real_flops / (t_attn * 1e-3) / 1e12, 1),
+            "flops_per_launch": {"computed_block_pairs": flops_pair * pairs,
+                                 "mfma_executed": mfma_flops, "real_token_pairs": real_flops},
+            "kernel_ms_bracketed_diagnostic": {kk: round(vv, 4) for kk, vv in kern.items() if vv},
             "dense_ms_per_layer": round(ms_dense, 4),
-            "dense_attn_ms": round(kd_["attn"], 4),
+            "dense_attn_ms": round(t_dense_attn, 4),
             "dense_attn_tflops": round(dense_tflops, 1),
             "speedup_vs_dense_layer": round(ms_dense / ms_layer, 3),
             "pack_pool_gbs": round(pack_gbs, 1),

@@ -19,13 +19,14 @@ __all__ = [
     "TRA_RADIUS_INF", "TraError", "library", "tra_attention", "tra_probe", "tra_mask",
     "tra_attn", "tra_grid", "tra_maxcnt", "tra_status_string", "tra_version",
     "tra_plan_bytes", "tra_plan", "tra_attn_plan", "tra_token_probe", "tra_token_mask",
-    "tra_token_attention", "tra_sip_mask", "tra_attn_weighted",
+    "tra_token_attention", "tra_token_warmup", "tra_sip_mask", "tra_attn_weighted",
+    "tra_workspace_bytes", "tra_time_attn", "tra_release_scratch",
     "tra_profile_begin", "tra_profile_end", "KERNEL_KINDS",
 ]
 
 TRA_RADIUS_INF = 2147483647
 KERNEL_KINDS = ("pack_pool", "entropy", "mask", "attn", "fill", "order", "union",
-                "token_entropy", "token_mask", "sip")
+                "token_entropy", "token_mask", "sip", "vmax")
 
 _lib = None
 
@@ -56,7 +57,9 @@ def library() -> ctypes.CDLL:
         lib.tra_maxcnt.restype = L
         lib.tra_attention.argtypes = [P, P, P, I, I, I, I, I, I, I, I, P, P]
         lib.tra_attention.restype = I
-        lib.tra_probe.argtypes = [P, P, I, I, I, I, I, I, I, I, P, P, P]
+        lib.tra_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+        lib.tra_workspace_bytes.restype = L
+        lib.tra_probe.argtypes = [P, P, I, I, I, I, I, I, I, I, P, P, P, P]
         lib.tra_probe.restype = I
         lib.tra_mask.argtypes = [P, I, I, I, I, I, I, P, P, P]
         lib.tra_mask.restype = I
@@ -75,6 +78,13 @@ def library() -> ctypes.CDLL:
         lib.tra_token_mask.restype = I
         lib.tra_token_attention.argtypes = [P, P, P, I, I, I, I, I, I, F, F, I, P, P]
         lib.tra_token_attention.restype = I
+        lib.tra_token_warmup.argtypes = [P, P, P, I, I, I, I, I, I, F, F, P, P, P, P]
+        lib.tra_token_warmup.restype = I
+        lib.tra_time_attn.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P, L, I, P,
+                                      ctypes.POINTER(F), P]
+        lib.tra_time_attn.restype = I
+        lib.tra_release_scratch.argtypes = []
+        lib.tra_release_scratch.restype = I
         lib.tra_sip_mask.argtypes = [P, P, P, I, I, I, I, I, I, F, P, P, P, P]
         lib.tra_sip_mask.restype = I
         lib.tra_attn_weighted.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P, L, P, P]
@@ -160,12 +170,20 @@ def tra_attention(q, k, v, T, H, W, heads, head_dim, block, r_min, r_max, out, s
         head_dim, block, r_min, r_max, _ptr(out, _f32(), "out"), _stream(stream)), "tra_attention")
 
 
+def tra_workspace_bytes(T: int, H: int, W: int, heads: int, head_dim: int, block: int,
+                        r_max: int) -> int:
+    n = library().tra_workspace_bytes(T, H, W, heads, head_dim, block, r_max)
+    if n < 0:
+        raise TraError(int(n), "tra_workspace_bytes")
+    return n
+
+
 def tra_probe(q, k, T, H, W, heads, head_dim, block, r_min, r_max, radius, h_norm=None,
-              stream=None):
+              ws=None, stream=None):
     _check(library().tra_probe(
         _ptr(q, _bf16(), "q"), _ptr(k, _bf16(), "k"), T, H, W, heads, head_dim, block, r_min,
-        r_max, _ptr(radius, _i32(), "radius"), _ptr(h_norm, _f32(), "h_norm"), _stream(stream)),
-        "tra_probe")
+        r_max, _ptr(radius, _i32(), "radius"), _ptr(h_norm, _f32(), "h_norm"),
+        _ptr(ws, None, "ws"), _stream(stream)), "tra_probe")
 
 
 def tra_mask(radius, T, H, W, heads, block, r_max, idx, cnt, stream=None):
@@ -222,6 +240,32 @@ def tra_token_attention(q, k, v, T, H, W, heads, head_dim, block, tau, gamma, mi
         _ptr(q, _bf16(), "q"), _ptr(k, _bf16(), "k"), _ptr(v, _bf16(), "v"), T, H, W, heads,
         head_dim, block, float(tau), float(gamma), int(min_votes), _ptr(out, _f32(), "out"),
         _stream(stream)), "tra_token_attention")
+
+
+def tra_token_warmup(q, k, v, T, H, W, heads, head_dim, block, tau, gamma, out, entropy, r0,
+                     stream=None):
+    _check(library().tra_token_warmup(
+        _ptr(q, _bf16(), "q"), _ptr(k, _bf16(), "k"), _ptr(v, _bf16(), "v"), T, H, W, heads,
+        head_dim, block, float(tau), float(gamma), _ptr(out, _f32(), "out"),
+        _ptr(entropy, _f32(), "entropy"), _ptr(r0, _f32(), "r0"), _stream(stream)),
+        "tra_token_warmup")
+
+
+def tra_time_attn(q, k, v, T, H, W, heads, head_dim, block, idx, cnt, lw, maxcnt, reps, out,
+                  stream=None) -> float:
+    """Mean milliseconds of one attention-kernel launch over ``reps`` back-to-back
+    launches (lists as for tra_attn_weighted; idx = cnt = None is the dense mode)."""
+    ms = ctypes.c_float()
+    _check(library().tra_time_attn(
+        _ptr(q, _bf16(), "q"), _ptr(k, _bf16(), "k"), _ptr(v, _bf16(), "v"), T, H, W, heads,
+        head_dim, block, _ptr(idx, _i32(), "idx"), _ptr(cnt, _i32(), "cnt"),
+        _ptr(lw, _f32(), "lw"), int(maxcnt), int(reps), _ptr(out, _f32(), "out"),
+        ctypes.byref(ms), _stream(stream)), "tra_time_attn")
+    return ms.value
+
+
+def tra_release_scratch():
+    _check(library().tra_release_scratch(), "tra_release_scratch")
 
 
 def tra_sip_mask(q, k, u, T, H, W, heads, head_dim, block, m, idx, cnt, lw, stream=None):

@@ -177,6 +177,54 @@ class ProfScope {
     bool active_ = false;
 };
 
+// Packed K/V of one call: K and V^T tiles, the partial maxima of |v| and the
+// per-head V exponents (see launch_vmax).
+struct PackedOffsets {
+    size_t kt, vt, vpart, vexp;
+};
+struct Packed {
+    uint16_t *kt, *vt;
+    uint32_t *vpart;
+    int32_t *vexp;
+};
+
+PackedOffsets reserve_packed(Scratch &ws, const tra::Grid &g, int heads, int head_dim) {
+    const size_t tiles = (size_t)heads * g.nb * tra::packed_tile_elems(head_dim) * 2;
+    PackedOffsets o;
+    o.kt = ws.reserve(tiles);
+    o.vt = ws.reserve(tiles);
+    o.vpart = ws.reserve((size_t)heads * tra::kVmaxParts * sizeof(uint32_t));
+    o.vexp = ws.reserve((size_t)heads * sizeof(int32_t));
+    return o;
+}
+
+Packed packed_at(const Scratch &ws, const PackedOffsets &o) {
+    return Packed{ws.at<uint16_t>(o.kt), ws.at<uint16_t>(o.vt), ws.at<uint32_t>(o.vpart),
+                  ws.at<int32_t>(o.vexp)};
+}
+
+// The head's largest |v|, then the tile packing of k and v (and, with q given,
+// the pooled means of q and k).
+hipError_t pack_kv(int head_dim, const void *q, const void *k, const void *v, const tra::Grid &g,
+                   int heads, float *qp, float *kp, const Packed &p, hipStream_t stream) {
+    hipError_t e;
+    {
+        ProfScope ps(TRA_KERNEL_VMAX, stream);
+        e = tra::launch_vmax(head_dim, (const uint16_t *)v, g, heads, p.vpart, stream);
+    }
+    if (e != hipSuccess) return e;
+    ProfScope ps(TRA_KERNEL_PACK_POOL, stream);
+    return tra::launch_pack_pool(head_dim, q != nullptr, true, (const uint16_t *)q,
+                                 (const uint16_t *)k, (const uint16_t *)v, g, heads, qp, kp, p.kt,
+                                 p.vt, p.vpart, p.vexp, stream);
+}
+
+// Bytes of tra_probe's workspace: the pooled means of q and k.
+size_t probe_ws_bytes(const tra::Grid &g, int heads, int head_dim) {
+    const size_t pooled = (size_t)heads * g.nb * head_dim * sizeof(float);
+    return 2 * ((pooled + 255) & ~size_t(255));
+}
+
 }  // namespace
 
 extern "C" {
@@ -192,7 +240,7 @@ const char *tra_status_string(int status) {
     }
 }
 
-int tra_version(void) { return 100; }
+int tra_version(void) { return 200; }
 
 int tra_grid(int T, int H, int W, int block, int *nby, int *nbx, int *nb) {
     tra::Grid g;
@@ -212,8 +260,17 @@ int64_t tra_maxcnt(int T, int H, int W, int block, int r_max) {
     return maxcnt_of(g, r_max);
 }
 
+int64_t tra_workspace_bytes(int T, int H, int W, int heads, int head_dim, int block, int r_max) {
+    tra::Grid g;
+    int rc = make_grid(T, H, W, block, &g);
+    if (rc == TRA_OK) rc = check_dims(heads, head_dim, g);
+    if (rc != TRA_OK) return rc;
+    if (r_max < 0) return TRA_ERR_INVALID_ARG;
+    return (int64_t)probe_ws_bytes(g, heads, head_dim);
+}
+
 int tra_probe(const void *q, const void *k, int T, int H, int W, int heads, int head_dim,
-              int block, int r_min, int r_max, int32_t *radius, float *h_norm,
+              int block, int r_min, int r_max, int32_t *radius, float *h_norm, void *ws,
               hipStream_t stream) {
     tra::Grid g;
     int rc = make_grid(T, H, W, block, &g);
@@ -228,15 +285,21 @@ int tra_probe(const void *q, const void *k, int T, int H, int W, int heads, int 
         return hip_status(e);
     }
 
-    Scratch ws(stream);
-    const size_t pooled = (size_t)heads * g.nb * head_dim * sizeof(float);
-    const size_t o_qp = ws.reserve(pooled), o_kp = ws.reserve(pooled);
-    if ((rc = ws.allocate()) != TRA_OK) return rc;
-    float *qp = ws.at<float>(o_qp), *kp = ws.at<float>(o_kp);
+    // the pooled means live in the caller's workspace, else in library scratch
+    Scratch pool(stream);
+    const size_t half = probe_ws_bytes(g, heads, head_dim) / 2;
+    char *base = static_cast<char *>(ws);
+    if (!base) {
+        const size_t o = pool.reserve(2 * half);
+        if ((rc = pool.allocate()) != TRA_OK) return rc;
+        base = pool.at<char>(o);
+    }
+    float *qp = reinterpret_cast<float *>(base), *kp = reinterpret_cast<float *>(base + half);
     {
         ProfScope p(TRA_KERNEL_PACK_POOL, stream);
         e = tra::launch_pack_pool(head_dim, true, false, (const uint16_t *)q, (const uint16_t *)k,
-                                  nullptr, g, heads, qp, kp, nullptr, nullptr, stream);
+                                  nullptr, g, heads, qp, kp, nullptr, nullptr, nullptr, nullptr,
+                                  stream);
     }
     if (e == hipSuccess) {
         ProfScope p(TRA_KERNEL_ENTROPY, stream);
@@ -305,31 +368,30 @@ static hipError_t plan_walk_into(const int32_t *idx, const int32_t *cnt, const f
                      (int32_t *)(plan + L.o_order), stream);
 }
 
+// The attention kernel along a walk plan (nullptr: dense mode) over packed K/V.
+static hipError_t attn_launch(const void *q, const Packed &pk, const tra::Grid &g, int heads,
+                              int head_dim, const char *plan, const PlanLayout &L, void *out,
+                              hipStream_t stream, const tra::EntropyOut *eo = nullptr) {
+    ProfScope p(TRA_KERNEL_ATTN, stream);
+    const int32_t *order = plan ? (const int32_t *)(plan + L.o_order) : nullptr;
+    const int32_t *ulen = plan ? (const int32_t *)(plan + L.o_ulen) : nullptr;
+    const int32_t *ulist = plan ? (const int32_t *)(plan + L.o_ulist) : nullptr;
+    const float2 *ubias = plan && L.weighted ? (const float2 *)(plan + L.o_ubias) : nullptr;
+    return tra::launch_attn(head_dim, (const uint16_t *)q, pk.kt, pk.vt, pk.vexp, ulist, ulen, ubias,
+                            plan ? L.ustride : 0, order, g, heads, (float *)out, stream, eo);
+}
+
 // Pack k and v, then attention along a walk plan (nullptr: dense mode).
 static int attn_with_plan(const void *q, const void *k, const void *v, const tra::Grid &g,
                           int heads, int head_dim, const char *plan, const PlanLayout &L,
                           void *out, hipStream_t stream) {
     Scratch ws(stream);
-    const size_t tiles = (size_t)heads * g.nb * tra::packed_tile_elems(head_dim) * 2;
-    const size_t o_kt = ws.reserve(tiles), o_vt = ws.reserve(tiles);
+    const PackedOffsets po = reserve_packed(ws, g, heads, head_dim);
     int rc = ws.allocate();
     if (rc != TRA_OK) return rc;
-    uint16_t *kt = ws.at<uint16_t>(o_kt), *vt = ws.at<uint16_t>(o_vt);
-    hipError_t e;
-    {
-        ProfScope p(TRA_KERNEL_PACK_POOL, stream);
-        e = tra::launch_pack_pool(head_dim, false, true, nullptr, (const uint16_t *)k,
-                                  (const uint16_t *)v, g, heads, nullptr, nullptr, kt, vt, stream);
-    }
-    if (e == hipSuccess) {
-        ProfScope p(TRA_KERNEL_ATTN, stream);
-        const int32_t *order = plan ? (const int32_t *)(plan + L.o_order) : nullptr;
-        const int32_t *ulen = plan ? (const int32_t *)(plan + L.o_ulen) : nullptr;
-        const int32_t *ulist = plan ? (const int32_t *)(plan + L.o_ulist) : nullptr;
-        const float2 *ubias = plan && L.weighted ? (const float2 *)(plan + L.o_ubias) : nullptr;
-        e = tra::launch_attn(head_dim, (const uint16_t *)q, kt, vt, ulist, ulen, ubias,
-                             plan ? L.ustride : 0, order, g, heads, (float *)out, stream);
-    }
+    const Packed pk = packed_at(ws, po);
+    hipError_t e = pack_kv(head_dim, nullptr, k, v, g, heads, nullptr, nullptr, pk, stream);
+    if (e == hipSuccess) e = attn_launch(q, pk, g, heads, head_dim, plan, L, out, stream);
     return hip_status(e);
 }
 
@@ -367,12 +429,26 @@ int tra_attn_plan(const void *q, const void *k, const void *v, int T, int H, int
     tra::Grid g;
     int rc = make_grid(T, H, W, block, &g);
     if (rc == TRA_OK) rc = check_dims(heads, head_dim, g);
-    if (rc != TRA_OK) return rc;
     if (rc == TRA_OK) rc = check_plan(g, heads, maxcnt);
     if (rc != TRA_OK) return rc;
     if (!q || !k || !v || !out || !plan) return TRA_ERR_INVALID_ARG;
     return attn_with_plan(q, k, v, g, heads, head_dim, static_cast<const char *>(plan),
                           plan_layout(g, heads, maxcnt), out, stream);
+}
+
+// Lists (with optional log-weights) -> walk plan in library scratch -> attention.
+static int attn_lists(const void *q, const void *k, const void *v, const tra::Grid &g, int heads,
+                      int head_dim, const int32_t *idx, const int32_t *cnt, const float *lw,
+                      int64_t maxcnt, void *out, hipStream_t stream) {
+    const PlanLayout L = plan_layout(g, heads, maxcnt, lw != nullptr);
+    Scratch ws(stream);
+    const size_t o_plan = ws.reserve(L.bytes);
+    int rc = ws.allocate();
+    if (rc != TRA_OK) return rc;
+    char *plan = ws.at<char>(o_plan);
+    const hipError_t e = plan_walk_into(idx, cnt, lw, maxcnt, g, heads, plan, L, stream);
+    if (e != hipSuccess) return hip_status(e);
+    return attn_with_plan(q, k, v, g, heads, head_dim, plan, L, out, stream);
 }
 
 int tra_attn(const void *q, const void *k, const void *v, int T, int H, int W, int heads,
@@ -386,15 +462,7 @@ int tra_attn(const void *q, const void *k, const void *v, int T, int H, int W, i
     if ((idx == nullptr) != (cnt == nullptr)) return TRA_ERR_INVALID_ARG;
     if (idx && (rc = check_plan(g, heads, maxcnt)) != TRA_OK) return rc;
     if (!idx) return attn_with_plan(q, k, v, g, heads, head_dim, nullptr, PlanLayout{}, out, stream);
-
-    const PlanLayout L = plan_layout(g, heads, maxcnt);
-    Scratch ws(stream);
-    const size_t o_plan = ws.reserve(L.bytes);
-    if ((rc = ws.allocate()) != TRA_OK) return rc;
-    char *plan = ws.at<char>(o_plan);
-    const hipError_t e = plan_walk_into(idx, cnt, nullptr, maxcnt, g, heads, plan, L, stream);
-    if (e != hipSuccess) return hip_status(e);
-    return attn_with_plan(q, k, v, g, heads, head_dim, plan, L, out, stream);
+    return attn_lists(q, k, v, g, heads, head_dim, idx, cnt, nullptr, maxcnt, out, stream);
 }
 
 int tra_attn_weighted(const void *q, const void *k, const void *v, int T, int H, int W, int heads,
@@ -407,14 +475,49 @@ int tra_attn_weighted(const void *q, const void *k, const void *v, int T, int H,
     if (rc != TRA_OK) return rc;
     if (!q || !k || !v || !out || !idx || !cnt) return TRA_ERR_INVALID_ARG;
     if ((rc = check_plan(g, heads, maxcnt)) != TRA_OK) return rc;
-    const PlanLayout L = plan_layout(g, heads, maxcnt, true);
+    return attn_lists(q, k, v, g, heads, head_dim, idx, cnt, lw, maxcnt, out, stream);
+}
+
+int tra_time_attn(const void *q, const void *k, const void *v, int T, int H, int W, int heads,
+                  int head_dim, int block, const int32_t *idx, const int32_t *cnt,
+                  const float *lw, int64_t maxcnt, int reps, void *out, float *ms,
+                  hipStream_t stream) {
+    tra::Grid g;
+    int rc = make_grid(T, H, W, block, &g);
+    if (rc == TRA_OK) rc = check_dims(heads, head_dim, g);
+    if (rc != TRA_OK) return rc;
+    if (!q || !k || !v || !out || !ms || reps < 1) return TRA_ERR_INVALID_ARG;
+    if ((idx == nullptr) != (cnt == nullptr) || (lw && !idx)) return TRA_ERR_INVALID_ARG;
+    if (idx && (rc = check_plan(g, heads, maxcnt)) != TRA_OK) return rc;
+    const PlanLayout L = idx ? plan_layout(g, heads, maxcnt, lw != nullptr) : PlanLayout{};
     Scratch ws(stream);
-    const size_t o_plan = ws.reserve(L.bytes);
+    const PackedOffsets po = reserve_packed(ws, g, heads, head_dim);
+    const size_t o_plan = idx ? ws.reserve(L.bytes) : 0;
     if ((rc = ws.allocate()) != TRA_OK) return rc;
-    char *plan = ws.at<char>(o_plan);
-    const hipError_t e = plan_walk_into(idx, cnt, lw, maxcnt, g, heads, plan, L, stream);
+    const Packed pk = packed_at(ws, po);
+    char *plan = idx ? ws.at<char>(o_plan) : nullptr;
+    hipError_t e = hipSuccess;
+    if (idx) e = plan_walk_into(idx, cnt, lw, maxcnt, g, heads, plan, L, stream);
+    if (e == hipSuccess) e = pack_kv(head_dim, nullptr, k, v, g, heads, nullptr, nullptr, pk, stream);
     if (e != hipSuccess) return hip_status(e);
-    return attn_with_plan(q, k, v, g, heads, head_dim, plan, L, out, stream);
+    hipEvent_t ev[2];
+    if (hipEventCreate(&ev[0]) != hipSuccess) return TRA_ERR_HIP;
+    if (hipEventCreate(&ev[1]) != hipSuccess) {
+        (void)hipEventDestroy(ev[0]);
+        return TRA_ERR_HIP;
+    }
+    e = hipEventRecord(ev[0], stream);
+    for (int i = 0; i < reps && e == hipSuccess; ++i)
+        e = attn_launch(q, pk, g, heads, head_dim, plan, L, out, stream);
+    if (e == hipSuccess) e = hipEventRecord(ev[1], stream);
+    if (e == hipSuccess) e = hipEventSynchronize(ev[1]);
+    float t = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, ev[0], ev[1]);
+    (void)hipEventDestroy(ev[0]);
+    (void)hipEventDestroy(ev[1]);
+    if (e != hipSuccess) return TRA_ERR_HIP;
+    *ms = t / (float)reps;
+    return TRA_OK;
 }
 
 int tra_sip_mask(const void *q, const void *k, const float *u, int T, int H, int W, int heads,
@@ -440,7 +543,8 @@ int tra_sip_mask(const void *q, const void *k, const float *u, int T, int H, int
     {
         ProfScope p(TRA_KERNEL_PACK_POOL, stream);
         e = tra::launch_pack_pool(head_dim, true, false, (const uint16_t *)q, (const uint16_t *)k,
-                                  nullptr, g, heads, qp, kp, nullptr, nullptr, stream);
+                                  nullptr, g, heads, qp, kp, nullptr, nullptr, nullptr, nullptr,
+                                  stream);
     }
     if (e == hipSuccess) {
         ProfScope p(TRA_KERNEL_ENTROPY, stream);
@@ -458,6 +562,8 @@ static int check_token_params(float tau, float gamma) {
         return TRA_ERR_INVALID_ARG;
     return TRA_OK;
 }
+
+static float two_gamma_log2e(float gamma) { return (float)(2.0 * gamma * 1.4426950408889634); }
 
 int tra_token_probe(const void *q, const void *k, int T, int H, int W, int heads, int head_dim,
                     int block, float tau, float gamma, float *entropy, float *r0,
@@ -488,6 +594,27 @@ int tra_token_probe(const void *q, const void *k, int T, int H, int W, int heads
     return hip_status(e);
 }
 
+int tra_token_warmup(const void *q, const void *k, const void *v, int T, int H, int W, int heads,
+                     int head_dim, int block, float tau, float gamma, void *out, float *entropy,
+                     float *r0, hipStream_t stream) {
+    tra::Grid g;
+    int rc = make_grid(T, H, W, block, &g);
+    if (rc == TRA_OK) rc = check_dims(heads, head_dim, g);
+    if (rc == TRA_OK) rc = check_token_params(tau, gamma);
+    if (rc != TRA_OK) return rc;
+    if (!q || !k || !v || !out || !r0) return TRA_ERR_INVALID_ARG;
+    Scratch ws(stream);
+    const PackedOffsets po = reserve_packed(ws, g, heads, head_dim);
+    const size_t o_ent = entropy ? 0 : ws.reserve((size_t)heads * T * H * W * sizeof(float));
+    if ((rc = ws.allocate()) != TRA_OK) return rc;
+    const Packed pk = packed_at(ws, po);
+    const tra::EntropyOut eo{entropy ? entropy : ws.at<float>(o_ent), r0, tau,
+                             two_gamma_log2e(gamma)};
+    hipError_t e = pack_kv(head_dim, nullptr, k, v, g, heads, nullptr, nullptr, pk, stream);
+    if (e == hipSuccess) e = attn_launch(q, pk, g, heads, head_dim, nullptr, PlanLayout{}, out, stream, &eo);
+    return hip_status(e);
+}
+
 int tra_token_mask(const float *r0, int T, int H, int W, int heads, int block, float gamma,
                    int min_votes, int32_t *idx, int32_t *cnt, hipStream_t stream) {
     tra::Grid g;
@@ -514,41 +641,30 @@ int tra_token_attention(const void *q, const void *k, const void *v, int T, int 
         return TRA_ERR_INVALID_ARG;
     const size_t rows = (size_t)heads * g.nb;
     const size_t toks = (size_t)heads * T * H * W;
-    const size_t tiles = rows * tra::packed_tile_elems(head_dim) * 2;
     const PlanLayout L = plan_layout(g, heads, g.nb);
     Scratch ws(stream);
-    const size_t o_kt = ws.reserve(tiles), o_vt = ws.reserve(tiles);
+    const PackedOffsets po = reserve_packed(ws, g, heads, head_dim);
     const size_t o_ent = ws.reserve(toks * sizeof(float)), o_r0 = ws.reserve(toks * sizeof(float));
     const size_t o_idx = ws.reserve(rows * (size_t)g.nb * sizeof(int32_t));
     const size_t o_cnt = ws.reserve(rows * sizeof(int32_t));
     const size_t o_plan = ws.reserve(L.bytes);
     if ((rc = ws.allocate()) != TRA_OK) return rc;
-    uint16_t *kt = ws.at<uint16_t>(o_kt), *vt = ws.at<uint16_t>(o_vt);
+    const Packed pk = packed_at(ws, po);
     float *ent = ws.at<float>(o_ent), *r0 = ws.at<float>(o_r0);
     int32_t *idx = ws.at<int32_t>(o_idx), *cnt = ws.at<int32_t>(o_cnt);
     char *plan = ws.at<char>(o_plan);
-    hipError_t e;
-    {
-        ProfScope p(TRA_KERNEL_PACK_POOL, stream);
-        e = tra::launch_pack_pool(head_dim, false, true, nullptr, (const uint16_t *)k,
-                                  (const uint16_t *)v, g, heads, nullptr, nullptr, kt, vt, stream);
-    }
+    hipError_t e = pack_kv(head_dim, nullptr, k, v, g, heads, nullptr, nullptr, pk, stream);
     if (e == hipSuccess) {
         ProfScope p(TRA_KERNEL_TOKEN_ENTROPY, stream);
-        e = tra::launch_token_entropy(head_dim, (const uint16_t *)q, kt, g, heads, tau, gamma, ent,
-                                      r0, stream);
+        e = tra::launch_token_entropy(head_dim, (const uint16_t *)q, pk.kt, g, heads, tau, gamma,
+                                      ent, r0, stream);
     }
     if (e == hipSuccess) {
         ProfScope p(TRA_KERNEL_TOKEN_MASK, stream);
         e = tra::launch_token_mask(r0, g, heads, gamma, min_votes, g.nb, idx, cnt, stream);
     }
     if (e == hipSuccess) e = plan_walk_into(idx, cnt, nullptr, g.nb, g, heads, plan, L, stream);
-    if (e == hipSuccess) {
-        ProfScope p(TRA_KERNEL_ATTN, stream);
-        e = tra::launch_attn(head_dim, (const uint16_t *)q, kt, vt, (const int32_t *)(plan + L.o_ulist),
-                             (const int32_t *)(plan + L.o_ulen), nullptr, L.ustride,
-                             (const int32_t *)(plan + L.o_order), g, heads, (float *)out, stream);
-    }
+    if (e == hipSuccess) e = attn_launch(q, pk, g, heads, head_dim, plan, L, out, stream);
     return hip_status(e);
 }
 
@@ -562,48 +678,27 @@ int tra_attention(const void *q, const void *k, const void *v, int T, int H, int
     if (!q || !k || !v || !out) return TRA_ERR_INVALID_ARG;
 
     const bool dense = is_dense(r_min, r_max);
+    if (dense) return attn_with_plan(q, k, v, g, heads, head_dim, nullptr, PlanLayout{}, out, stream);
+
     const int64_t maxcnt = maxcnt_of(g, r_max);
     const size_t rows = (size_t)heads * g.nb;
-    const size_t tiles = rows * tra::packed_tile_elems(head_dim) * 2;
-
+    const PlanLayout L = plan_layout(g, heads, maxcnt);
     Scratch ws(stream);
-    const size_t o_kt = ws.reserve(tiles), o_vt = ws.reserve(tiles);
-    size_t o_qp = 0, o_kp = 0, o_r = 0, o_idx = 0, o_cnt = 0, o_order = 0, o_ulen = 0, o_ulist = 0;
-    if (!dense) {
-        o_qp = ws.reserve(rows * head_dim * sizeof(float));
-        o_kp = ws.reserve(rows * head_dim * sizeof(float));
-        o_r = ws.reserve(rows * sizeof(int32_t));
-        o_cnt = ws.reserve(rows * sizeof(int32_t));
-        o_idx = ws.reserve(rows * (size_t)maxcnt * sizeof(int32_t));
-        o_order = ws.reserve(order_len(g, heads) * sizeof(int32_t));
-        o_ulen = ws.reserve(walk_rows(g, heads) * sizeof(int32_t));
-        o_ulist = ws.reserve(walk_rows(g, heads) * (size_t)tra::union_stride(maxcnt) * sizeof(int32_t));
-    }
+    const PackedOffsets po = reserve_packed(ws, g, heads, head_dim);
+    const size_t o_qp = ws.reserve(rows * head_dim * sizeof(float));
+    const size_t o_kp = ws.reserve(rows * head_dim * sizeof(float));
+    const size_t o_r = ws.reserve(rows * sizeof(int32_t));
+    const size_t o_cnt = ws.reserve(rows * sizeof(int32_t));
+    const size_t o_idx = ws.reserve(rows * (size_t)maxcnt * sizeof(int32_t));
+    const size_t o_plan = ws.reserve(L.bytes);
     if ((rc = ws.allocate()) != TRA_OK) return rc;
-    uint16_t *kt = ws.at<uint16_t>(o_kt), *vt = ws.at<uint16_t>(o_vt);
-    const uint16_t *q16 = (const uint16_t *)q, *k16 = (const uint16_t *)k, *v16 = (const uint16_t *)v;
-    float *o32 = (float *)out;
-
-    hipError_t e;
-    if (dense) {
-        {
-            ProfScope p(TRA_KERNEL_PACK_POOL, stream);
-            e = tra::launch_pack_pool(head_dim, false, true, nullptr, k16, v16, g, heads, nullptr,
-                                      nullptr, kt, vt, stream);
-        }
-        if (e == hipSuccess) {
-            ProfScope p(TRA_KERNEL_ATTN, stream);
-            e = tra::launch_attn(head_dim, q16, kt, vt, nullptr, nullptr, nullptr, 0, nullptr, g,
-                                 heads, o32, stream);
-        }
-        return hip_status(e);
-    }
+    const Packed pk = packed_at(ws, po);
     float *qp = ws.at<float>(o_qp), *kp = ws.at<float>(o_kp);
     int32_t *radius = ws.at<int32_t>(o_r), *cnt = ws.at<int32_t>(o_cnt), *idx = ws.at<int32_t>(o_idx);
-    {
-        ProfScope p(TRA_KERNEL_PACK_POOL, stream);
-        e = tra::launch_pack_pool(head_dim, true, true, q16, k16, v16, g, heads, qp, kp, kt, vt, stream);
-    }
+    char *plan = ws.at<char>(o_plan);
+
+    // one pass over q, k, v: pooled means for the probe and the packed tiles
+    hipError_t e = pack_kv(head_dim, q, k, v, g, heads, qp, kp, pk, stream);
     if (e == hipSuccess) {
         ProfScope p(TRA_KERNEL_ENTROPY, stream);
         e = tra::launch_entropy(head_dim, qp, kp, g, heads, r_min, r_max, radius, nullptr, stream);
@@ -612,16 +707,21 @@ int tra_attention(const void *q, const void *k, const void *v, int T, int H, int
         ProfScope p(TRA_KERNEL_MASK, stream);
         e = tra::launch_mask(radius, g, heads, r_max, maxcnt, idx, cnt, stream);
     }
-    int32_t *order = ws.at<int32_t>(o_order), *ulen = ws.at<int32_t>(o_ulen);
-    int32_t *ulist = ws.at<int32_t>(o_ulist);
-    if (e == hipSuccess)
-        e = plan_walk(idx, cnt, nullptr, maxcnt, g, heads, ulist, ulen, nullptr, order, stream);
-    if (e == hipSuccess) {
-        ProfScope p(TRA_KERNEL_ATTN, stream);
-        e = tra::launch_attn(head_dim, q16, kt, vt, ulist, ulen, nullptr, tra::union_stride(maxcnt),
-                             order, g, heads, o32, stream);
-    }
+    if (e == hipSuccess) e = plan_walk_into(idx, cnt, nullptr, maxcnt, g, heads, plan, L, stream);
+    if (e == hipSuccess) e = attn_launch(q, pk, g, heads, head_dim, plan, L, out, stream);
     return hip_status(e);
+}
+
+int tra_release_scratch(void) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TRA_ERR_HIP;
+    hipMemPool_t p = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_pool_mu);
+        p = g_pool[dev];
+    }
+    if (!p) return TRA_OK;
+    return hip_status(hipMemPoolTrimTo(p, 0));
 }
 
 int tra_profile_begin(void) {

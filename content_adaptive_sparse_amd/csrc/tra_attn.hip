@@ -35,14 +35,19 @@ constexpr float kRescaleLog2 = 8.0f;
 
 // WEIGHTED: every walk entry carries, per side, a log2 weight added to the
 // logits of its keys (inverse inclusion probabilities of sampled blocks).
-template <int D, bool WEIGHTED>
+// ENTROPY: each query also keeps, against the same lazy reference m, the fp32
+// sums Z = sum 2^x and A = sum x 2^x over x = s log2(e) / sqrt(d) - m, and
+// writes its row's entropy H = ln Z - ln 2 A / Z with the base radius it
+// implies (the token policy's warm-up, fused into the attention pass).
+template <int D, bool WEIGHTED, bool ENTROPY>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kt,
-    const uint16_t *__restrict__ vt, const int32_t *__restrict__ ulist,
-    const int32_t *__restrict__ ulen, const float2 *__restrict__ ubias, int64_t ustride,
-    const int32_t *__restrict__ order, Grid g,
+    const uint16_t *__restrict__ vt, const int32_t *__restrict__ vexp,
+    const int32_t *__restrict__ ulist, const int32_t *__restrict__ ulen,
+    const float2 *__restrict__ ubias, int64_t ustride, const int32_t *__restrict__ order, Grid g,
     int heads, int pairs_per_head, int per_xcd, FastDiv div_nbx, FastDiv div_nby,
-    float *__restrict__ out, float scale_log2) {
+    float *__restrict__ out, float scale_log2, EntropyOut eo) {
+    static_assert(!(WEIGHTED && ENTROPY), "entropy of unweighted rows only");
     constexpr int KS = D / 16;                  // k-steps of Q.K^T
     constexpr int MT = D / 32;                  // 32-row tiles of O^T
     constexpr int TILE = 64 * D;                // elements of a packed K or V^T tile
@@ -111,12 +116,19 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
         const int64_t m = ((const const_i32_t *)ulen)[item];
         n = (int)(m < 0 ? 0 : (m > ustride ? ustride : m));
     }
-    if (n == 0) {  // neither block keeps anything: zeros
+    if (n == 0) {  // neither block keeps anything: zeros (and, for ENTROPY, an empty row's H = 0)
         if (qreal)
             for (int c = 0; c < D / 2; c += 4)
                 *reinterpret_cast<float4 *>(o + c + (D / 2) * hl) = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (ENTROPY && qreal && hl == 0) {
+            float r0;
+            eo.ent[qtok] = entropy_and_radius(1.f, 0.f, t, g, eo.tau, eo.two_gamma_log2e, &r0);
+            eo.r0[qtok] = r0;
+        }
         return;
     }
+    // V was packed as v 2^ve (fp16 range); the output is scaled back by 2^-ve
+    const int ve = ((const const_i32_t *)vexp)[h];
     int win = 0, win_next = 0, wbase = 0;
     // this wave's side's weight of every entry, windowed like the entries
     const float *ubw = WEIGHTED ? reinterpret_cast<const float *>(ubias + item * ustride) + side
@@ -188,6 +200,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
     float m_ref = -1e30f, l_run = 0.f;
+    float ent_z = 0.f, ent_a = 0.f;  // ENTROPY: fp32 row sums Z and A of this lane's keys
+    // Missing keys of edge tiles: -inf, or a finite -1e30 when x 2^x is summed
+    // (so that 0 * x stays 0)
+    constexpr float kMaskFill = ENTROPY ? -1e30f : -INFINITY;
 
     int e0 = entry(0);
     float w0 = weight(0);
@@ -239,7 +255,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
             const int kbx = (int)(kb - row * div_nbx.d);
             const int kby = (int)(row - fdiv(row, div_nby) * div_nby.d);
             mask_edge_keys(sb, min(kTileSide, g.H - kTileSide * kby),
-                           min(kTileSide, g.W - kTileSide * kbx), hl, -INFINITY);
+                           min(kTileSide, g.W - kTileSide * kbx), hl, kMaskFill);
         }
         if constexpr (DP) {
             if (rescale) {
@@ -269,15 +285,37 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
             const bool grow = mx > m_ref + kRescaleLog2;
             const float m_new = grow ? mx : m_ref;
             const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+            if constexpr (ENTROPY) {
+                // moving the reference by delta: Z' = 2^-delta Z, A' = 2^-delta (A - delta Z)
+                ent_a = alpha * __builtin_fmaf(m_ref - m_new, ent_z, ent_a);
+                ent_z *= alpha;
+            }
             m_ref = m_new;
             const float bias = w0 - m_ref;
             float psum0 = 0.f, psum1 = 0.f;
             const f16x2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
+                if constexpr (ENTROPY) {
+                    float z0 = 0.f, z1 = 0.f, a0 = 0.f, a1 = 0.f;
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    sb[hf][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[hf][r], scale_log2, bias));
+                    for (int r = 0; r < 16; r += 2) {
+                        const float x0 = __builtin_fmaf(sb[hf][r], scale_log2, bias);
+                        const float x1 = __builtin_fmaf(sb[hf][r + 1], scale_log2, bias);
+                        sb[hf][r] = __builtin_amdgcn_exp2f(x0);
+                        sb[hf][r + 1] = __builtin_amdgcn_exp2f(x1);
+                        z0 += sb[hf][r];
+                        z1 += sb[hf][r + 1];
+                        a0 = __builtin_fmaf(sb[hf][r], x0, a0);
+                        a1 = __builtin_fmaf(sb[hf][r + 1], x1, a1);
+                    }
+                    ent_z += z0 + z1;
+                    ent_a += a0 + a1;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        sb[hf][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[hf][r], scale_log2, bias));
+                }
 #pragma unroll
                 for (int ks2 = 0; ks2 < 2; ++ks2) {
 #pragma unroll
@@ -340,19 +378,27 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 const int d0 = 32 * mt + 8 * g4 + 4 * hl;
-                *reinterpret_cast<float4 *>(o + d0) =
-                    make_float4(acc[mt][4 * g4] * inv, acc[mt][4 * g4 + 1] * inv,
-                                acc[mt][4 * g4 + 2] * inv, acc[mt][4 * g4 + 3] * inv);
+                *reinterpret_cast<float4 *>(o + d0) = make_float4(
+                    ldexpf(acc[mt][4 * g4] * inv, -ve), ldexpf(acc[mt][4 * g4 + 1] * inv, -ve),
+                    ldexpf(acc[mt][4 * g4 + 2] * inv, -ve), ldexpf(acc[mt][4 * g4 + 3] * inv, -ve));
             }
+    }
+    if constexpr (ENTROPY) {
+        const float zt = half_swap_sum(ent_z), at = half_swap_sum(ent_a);
+        if (qreal && hl == 0) {
+            float r0;
+            eo.ent[qtok] = entropy_and_radius(zt, at, t, g, eo.tau, eo.two_gamma_log2e, &r0);
+            eo.r0[qtok] = r0;
+        }
     }
 }
 
 }  // namespace
 
 hipError_t launch_attn(int D, const uint16_t *q, const uint16_t *kt, const uint16_t *vt,
-                       const int32_t *ulist, const int32_t *ulen, const float2 *ubias,
-                       int64_t ustride, const int32_t *order, const Grid &g, int heads,
-                       float *out, hipStream_t s) {
+                       const int32_t *vexp, const int32_t *ulist, const int32_t *ulen,
+                       const float2 *ubias, int64_t ustride, const int32_t *order, const Grid &g,
+                       int heads, float *out, hipStream_t s, const EntropyOut *entropy) {
     const int pph = pairs_per_head(g);
     const int64_t total = (int64_t)heads * pph;
     const int per_xcd = (int)((total + 7) / 8);
@@ -361,18 +407,25 @@ hipError_t launch_attn(int D, const uint16_t *q, const uint16_t *kt, const uint1
         block(kAttnThreads);
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
     const FastDiv div_nbx = make_fastdiv(g.nbx), div_nby = make_fastdiv(g.nby);
-#define TRA_LAUNCH(DD, WW)                                                                    \
-    hipLaunchKernelGGL((attn_kernel<DD, WW>), grid, block, 0, s, q, kt, vt, ulist, ulen, ubias,  \
-                       ustride, order, g, heads, pph, per_xcd, div_nbx, div_nby, out, scale_log2)
+    const EntropyOut eo = entropy ? *entropy : EntropyOut{nullptr, nullptr, 0.f, 0.f};
+#define TRA_LAUNCH(DD, WW, EE)                                                                \
+    hipLaunchKernelGGL((attn_kernel<DD, WW, EE>), grid, block, 0, s, q, kt, vt, vexp, ulist,     \
+                       ulen, ubias, ustride, order, g, heads, pph, per_xcd, div_nbx, div_nby, out, \
+                       scale_log2, eo)
     const bool weighted = ubias != nullptr && ulist != nullptr;
+    if (weighted && entropy) return hipErrorInvalidValue;
     if (D == 128 && weighted)
-        TRA_LAUNCH(128, true);
+        TRA_LAUNCH(128, true, false);
+    else if (D == 128 && entropy)
+        TRA_LAUNCH(128, false, true);
     else if (D == 128)
-        TRA_LAUNCH(128, false);
+        TRA_LAUNCH(128, false, false);
     else if (D == 64 && weighted)
-        TRA_LAUNCH(64, true);
+        TRA_LAUNCH(64, true, false);
+    else if (D == 64 && entropy)
+        TRA_LAUNCH(64, false, true);
     else if (D == 64)
-        TRA_LAUNCH(64, false);
+        TRA_LAUNCH(64, false, false);
     else
         return hipErrorInvalidValue;
 #undef TRA_LAUNCH

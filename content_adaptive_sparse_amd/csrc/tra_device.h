@@ -88,4 +88,23 @@ __device__ __forceinline__ void mask_edge_keys(f32x16_t (&sb)[2], int kny, int k
     }
 }
 
+// Entropy of an attention row from its base-2 sums against a reference m,
+// Z = sum 2^x and A = sum x 2^x with x = s log2(e) / sqrt(d) - m:
+// H = ln Z - ln 2 A / Z (nats).  Token Radius Attention for Efficient Video
+// Generation, "The TRA Pipeline: Entropy-to-Budget" and "Budget-to-Radius":
+// the budget b = tau e^H keys, clamped to [1, T H W], and the base radius r0
+// whose disks r0 e^(-gamma |t' - t|) over the T frames have a total area of b,
+// r0 = sqrt(b / (pi sum_t' e^(-2 gamma |t' - t|))), with 2 gamma log2(e)
+// passed in (formed once on the host).  Returns H, writes r0.
+__device__ __forceinline__ float entropy_and_radius(float Z, float A, int t, const Grid &g,
+                                                    float tau, float two_gamma_log2e, float *r0) {
+    const float H = 0.69314718055994531f * (__builtin_amdgcn_logf(Z) - A / Z);
+    const float N = (float)((int64_t)g.T * g.H * g.W);
+    const float b = fminf(fmaxf(tau * __builtin_amdgcn_exp2f(H * 1.4426950408889634f), 1.0f), N);
+    float S = 0.f;
+    for (int tt = 0; tt < g.T; ++tt) S += __builtin_amdgcn_exp2f(-two_gamma_log2e * (float)abs(tt - t));
+    *r0 = sqrtf(b / (3.14159265358979f * S));
+    return H;
+}
+
 }  // namespace tra

@@ -30,9 +30,21 @@ struct Grid {
 //       (so that the keys of a lane match the probabilities that lane holds).
 size_t packed_tile_elems(int D);
 
+// V enters the P.V product on fp16 matrix cores as v 2^e_h, with one
+// power-of-two exponent e_h per head that puts the head's largest |v| into
+// [2^15, 2^16) (exact for every finite bfloat16 within 2^30 of it); the output
+// is multiplied back by 2^-e_h.  vmax_kernel writes vmax_parts(g, D) partial
+// maxima per head (vpart [heads][parts], bfloat16 bits of |v|); the packing
+// kernel reduces them, scales V and writes e_h to vexp [heads].
+constexpr int kVmaxParts = 64;
+int vmax_parts(const Grid &g, int D);
+hipError_t launch_vmax(int D, const uint16_t *v, const Grid &g, int heads, uint32_t *vpart,
+                       hipStream_t s);
+
 hipError_t launch_pack_pool(int D, bool pool, bool pack, const uint16_t *q, const uint16_t *k,
                             const uint16_t *v, const Grid &g, int heads, float *qp, float *kp,
-                            uint16_t *kt, uint16_t *vt, hipStream_t s);
+                            uint16_t *kt, uint16_t *vt, const uint32_t *vpart, int32_t *vexp,
+                            hipStream_t s);
 
 // logits (optional): the pooled logit matrix [heads][nb][nb] (scaled by 1/sqrt(D)).
 hipError_t launch_entropy(int D, const float *qp, const float *kp, const Grid &g, int heads,
@@ -105,11 +117,22 @@ inline int64_t order_slots(const Grid &g, int heads) { return 8 * order_range_ca
 hipError_t launch_order(const int32_t *ulen, const Grid &g, int heads, int64_t maxcnt,
                         int32_t *order, hipStream_t s);
 
+// Optional per-query entropy of the attention row (the token policy's warm-up
+// fused into dense attention): H_i in nats and the base radius r0_i, both
+// [heads][T][H][W] fp32, with the budget parameter tau and the temporal decay
+// as 2 gamma log2(e).
+struct EntropyOut {
+    float *ent;
+    float *r0;
+    float tau;
+    float two_gamma_log2e;
+};
+
 // ulist == nullptr: the dense mode (every block, both sides; order null, items
-// in XCD-contiguous raster order).
+// in XCD-contiguous raster order).  vexp: the per-head V exponents.
 hipError_t launch_attn(int D, const uint16_t *q, const uint16_t *kt, const uint16_t *vt,
-                       const int32_t *ulist, const int32_t *ulen, const float2 *ubias,
-                       int64_t ustride, const int32_t *order, const Grid &g, int heads,
-                       float *out, hipStream_t s);
+                       const int32_t *vexp, const int32_t *ulist, const int32_t *ulen,
+                       const float2 *ubias, int64_t ustride, const int32_t *order, const Grid &g,
+                       int heads, float *out, hipStream_t s, const EntropyOut *entropy = nullptr);
 
 }  // namespace tra

@@ -27,6 +27,46 @@ __device__ __forceinline__ int swap_bits23(int p) {
     return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1);
 }
 
+// Largest |v| of a head, as the bit pattern of a non-negative bfloat16 (for
+// finite non-negative values the bit patterns order like the values).  Grid
+// (parts, heads): workgroup g scans the g-th of `parts` equal chunks of the
+// head's T H W d elements, eight at a time, and writes its maximum.
+__global__ __launch_bounds__(256) void vmax_kernel(const uint16_t *__restrict__ v, int64_t n,
+                                                   int parts, uint32_t *__restrict__ vpart) {
+    __shared__ uint32_t red[4];
+    const int h = blockIdx.y, gpart = blockIdx.x;
+    const int64_t n8 = n / 8;  // n = T H W d is a multiple of 8 (d in {64, 128})
+    const int64_t chunk = (n8 + parts - 1) / parts;
+    const int64_t lo = min(n8, gpart * chunk), hi = min(n8, lo + chunk);
+    const uint4 *src = reinterpret_cast<const uint4 *>(v + (size_t)h * n);
+    uint32_t mx = 0;
+    for (int64_t i = lo + threadIdx.x; i < hi; i += 256) {
+        const uint4 w = src[i];
+        const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = max(mx, max(a[e] & 0x7fffu, (a[e] >> 16) & 0x7fffu));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        vpart[(size_t)h * parts + gpart] = max(max(red[0], red[1]), max(red[2], red[3]));
+}
+
+// Power-of-two exponent e that puts the head's largest |v| (bfloat16 bits m)
+// into [2^15, 2^16): v 2^e is then exact in fp16 for every |v| of the head
+// down to 2^-30 of the largest (below that, fp16 subnormals round at an
+// absolute 2^-25 of the scaled maximum), and nothing overflows.  e = 0 for an
+// all-zero head.  The attention output is multiplied by 2^-e.
+__device__ __forceinline__ int v_scale_exponent(uint32_t m) {
+    if (m == 0) return 0;
+    const int ex = (int)(m >> 7) & 0xff;  // biased exponent of the bfloat16
+    // floor(log2 |v|): normal ex - 127; subnormal mantissa * 2^-133
+    const int lg = ex ? ex - 127 : (31 - __builtin_clz(m & 0x7fu)) - 133;
+    return 15 - lg;
+}
+
 // One workgroup per (head, block).  256 threads; thread tid owns the 16-byte
 // chunk c = tid % (D/8) of rows w = tid / (D/8) + i * (256 / (D/8)).  PACK
 // writes the packed K tile, PACKV also the packed V^T tile.
@@ -34,7 +74,8 @@ template <int D, bool POOL, bool PACK, bool PACKV = PACK>
 __global__ __launch_bounds__(256) void pack_pool_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, Grid g, float *__restrict__ qp, float *__restrict__ kp,
-    uint16_t *__restrict__ kt, uint16_t *__restrict__ vt) {
+    uint16_t *__restrict__ kt, uint16_t *__restrict__ vt, const uint32_t *__restrict__ vpart,
+    int vparts, int32_t *__restrict__ vexp) {
     constexpr int CH = D / 8;
     constexpr int RG = 256 / CH;
     constexpr int RPT = 64 / RG;
@@ -61,6 +102,15 @@ __global__ __launch_bounds__(256) void pack_pool_kernel(
     float sq[8], sk[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) sq[e] = sk[e] = 0.f;
+
+    // the head's V exponent, from the partial maxima of vmax_kernel
+    int vsc = 0;
+    if (PACKV) {
+        uint32_t m = 0;
+        for (int i = 0; i < vparts; ++i) m = max(m, vpart[(size_t)h * vparts + i]);
+        vsc = v_scale_exponent(m);
+        if (b == 0 && tid == 0) vexp[h] = vsc;
+    }
 
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
@@ -98,9 +148,10 @@ __global__ __launch_bounds__(256) void pack_pool_kernel(
             uint32_t hw[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                // bf16 -> fp16 is exact for |v| in the fp16 normal range
-                const _Float16 lo = (_Float16)bf16_to_float(vw[e] & 0xffffu);
-                const _Float16 hi = (_Float16)bf16_to_float(vw[e] >> 16);
+                // v 2^vsc: exact in fp32, then rounded to fp16 (exact within
+                // 2^30 of the head's largest |v|, which lands in [2^15, 2^16))
+                const _Float16 lo = (_Float16)ldexpf(bf16_to_float(vw[e] & 0xffffu), vsc);
+                const _Float16 hi = (_Float16)ldexpf(bf16_to_float(vw[e] >> 16), vsc);
                 hw[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
                         ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
             }
@@ -298,14 +349,18 @@ __global__ __launch_bounds__(256) void fill_dense_kernel(int64_t n, int32_t *__r
 template <int D>
 hipError_t pack_pool_dispatch(bool pool, bool pack, const uint16_t *q, const uint16_t *k,
                               const uint16_t *v, const Grid &g, int heads, float *qp, float *kp,
-                              uint16_t *kt, uint16_t *vt, hipStream_t s) {
+                              uint16_t *kt, uint16_t *vt, const uint32_t *vpart, int vparts,
+                              int32_t *vexp, hipStream_t s) {
     const dim3 grid(g.nb, heads), block(256);
     if (pool && pack)
-        hipLaunchKernelGGL((pack_pool_kernel<D, true, true>), grid, block, 0, s, q, k, v, g, qp, kp, kt, vt);
+        hipLaunchKernelGGL((pack_pool_kernel<D, true, true>), grid, block, 0, s, q, k, v, g, qp, kp,
+                           kt, vt, vpart, vparts, vexp);
     else if (pool)
-        hipLaunchKernelGGL((pack_pool_kernel<D, true, false>), grid, block, 0, s, q, k, v, g, qp, kp, kt, vt);
+        hipLaunchKernelGGL((pack_pool_kernel<D, true, false>), grid, block, 0, s, q, k, v, g, qp,
+                           kp, kt, vt, vpart, vparts, vexp);
     else if (pack)
-        hipLaunchKernelGGL((pack_pool_kernel<D, false, true>), grid, block, 0, s, q, k, v, g, qp, kp, kt, vt);
+        hipLaunchKernelGGL((pack_pool_kernel<D, false, true>), grid, block, 0, s, q, k, v, g, qp,
+                           kp, kt, vt, vpart, vparts, vexp);
     return hipGetLastError();
 }
 
@@ -318,20 +373,42 @@ hipError_t launch_pack_k(int D, const uint16_t *k, const Grid &g, int heads, uin
     const dim3 grid(g.nb, heads), block(256);
     if (D == 128)
         hipLaunchKernelGGL((pack_pool_kernel<128, false, true, false>), grid, block, 0, s, nullptr,
-                           k, nullptr, g, nullptr, nullptr, kt, nullptr);
+                           k, nullptr, g, nullptr, nullptr, kt, nullptr, nullptr, 0, nullptr);
     else if (D == 64)
         hipLaunchKernelGGL((pack_pool_kernel<64, false, true, false>), grid, block, 0, s, nullptr,
-                           k, nullptr, g, nullptr, nullptr, kt, nullptr);
+                           k, nullptr, g, nullptr, nullptr, kt, nullptr, nullptr, 0, nullptr);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
+int vmax_parts(const Grid &g, int D) {
+    // about 64 K elements per workgroup, at most kVmaxParts per head
+    const int64_t n = (int64_t)g.T * g.H * g.W * D;
+    const int64_t p = (n + 65535) / 65536;
+    return (int)(p < 1 ? 1 : (p > kVmaxParts ? kVmaxParts : p));
+}
+
+hipError_t launch_vmax(int D, const uint16_t *v, const Grid &g, int heads, uint32_t *vpart,
+                       hipStream_t s) {
+    const int parts = vmax_parts(g, D);
+    const int64_t n = (int64_t)g.T * g.H * g.W * D;
+    hipLaunchKernelGGL(vmax_kernel, dim3((unsigned)parts, (unsigned)heads), dim3(256), 0, s, v, n,
+                       parts, vpart);
+    return hipGetLastError();
+}
+
 hipError_t launch_pack_pool(int D, bool pool, bool pack, const uint16_t *q, const uint16_t *k,
                             const uint16_t *v, const Grid &g, int heads, float *qp, float *kp,
-                            uint16_t *kt, uint16_t *vt, hipStream_t s) {
-    if (D == 128) return pack_pool_dispatch<128>(pool, pack, q, k, v, g, heads, qp, kp, kt, vt, s);
-    if (D == 64) return pack_pool_dispatch<64>(pool, pack, q, k, v, g, heads, qp, kp, kt, vt, s);
+                            uint16_t *kt, uint16_t *vt, const uint32_t *vpart, int32_t *vexp,
+                            hipStream_t s) {
+    const int vparts = vmax_parts(g, D);
+    if (D == 128)
+        return pack_pool_dispatch<128>(pool, pack, q, k, v, g, heads, qp, kp, kt, vt, vpart, vparts,
+                                       vexp, s);
+    if (D == 64)
+        return pack_pool_dispatch<64>(pool, pack, q, k, v, g, heads, qp, kp, kt, vt, vpart, vparts,
+                                      vexp, s);
     return hipErrorInvalidValue;
 }
 

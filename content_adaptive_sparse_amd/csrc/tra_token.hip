@@ -165,14 +165,9 @@ __global__ __launch_bounds__(kEntThreads, 2) void token_entropy_kernel(
     const float Zt = half_swap_sum(Z), At = half_swap_sum(A);
     if (qreal && hl == 0) {
         // Z >= 1: the key that last set the reference contributes 2^0
-        const float H = 0.69314718055994531f * (__builtin_amdgcn_logf(Zt) - At / Zt);
-        const float N = (float)((int64_t)g.T * g.H * g.W);
-        const float b = fminf(fmaxf(tau * __builtin_amdgcn_exp2f(H * 1.4426950408889634f), 1.0f), N);
-        float S = 0.f;
-        for (int tt = 0; tt < g.T; ++tt)
-            S += __builtin_amdgcn_exp2f(-two_gamma_log2e * (float)abs(tt - t));
-        ent[head_tok + qtok] = H;
-        r0[head_tok + qtok] = sqrtf(b / (3.14159265358979f * S));
+        float rq;
+        ent[head_tok + qtok] = entropy_and_radius(Zt, At, t, g, tau, two_gamma_log2e, &rq);
+        r0[head_tok + qtok] = rq;
     }
 }
 

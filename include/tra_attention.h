@@ -29,11 +29,18 @@
  * - Softmax scale is 1/sqrt(head_dim).
  * - Radii are integers >= 0; TRA_RADIUS_INF passed as both r_min and r_max
  *   selects the dense mode (every key block kept, probe skipped).
- * - V is multiplied on fp16 matrix cores: every |v| must be below 65504 (a
- *   bfloat16 of magnitude 65536 or more overflows).  Inputs must be finite.
- * - All work is enqueued on `stream`; no entry point synchronises it.  Scratch
- *   memory comes from a library-owned stream-ordered pool (hipMallocAsync
- *   semantics) and is returned to it on `stream` before the call returns.
+ * - V is multiplied on fp16 matrix cores as v 2^e_h, with one power-of-two
+ *   exponent e_h per head that puts the head's largest |v| into [2^15, 2^16);
+ *   the output is multiplied back by 2^-e_h.  This is exact for every finite
+ *   bfloat16 within 2^30 of the head's largest |v| (smaller values round at an
+ *   absolute 2^-25 of it), so any finite bfloat16 V is accepted.  Inputs must
+ *   be finite.
+ * - All work is enqueued on `stream`; no entry point synchronises it (except
+ *   the benchmark helpers tra_time_attn and tra_profile_end).  Scratch memory
+ *   comes from a library-owned stream-ordered pool (hipMallocAsync semantics)
+ *   and is returned to it on `stream` before the call returns; the pool keeps
+ *   freed memory for later calls until tra_release_scratch.  tra_probe can
+ *   instead take a caller-owned workspace of tra_workspace_bytes bytes.
  * - The caller owns every pointer it passes; the library keeps none after the
  *   call returns.  Calls on different streams are independent.
  * - Argument errors are detected on the host before anything is enqueued and
@@ -96,6 +103,13 @@ int tra_attention(const void *q, const void *k, const void *v,
                   int r_min, int r_max, void *out, hipStream_t stream);
 
 /*
+ * Bytes of the caller-owned workspace tra_probe takes for these sizes (the
+ * fp32 block means of q and k, 256-byte aligned); r_max is checked as for
+ * tra_maxcnt.  Returns the size, or a negative status for invalid sizes.
+ */
+int64_t tra_workspace_bytes(int T, int H, int W, int heads, int head_dim, int block, int r_max);
+
+/*
  * Probe (Token Radius Attention ..., "Insight I" and "The TRA Pipeline:
  * Entropy-to-Budget / Budget-to-Radius"), per (head, query block b):
  *   Qbar_b, Kbar_b = means of q and k over the real tokens of block b (fp32);
@@ -108,11 +122,15 @@ int tra_attention(const void *q, const void *k, const void *v,
  *   q, k      device bf16 [heads][T][H][W][head_dim]
  *   radius    device int32 [heads][nb]   (written)
  *   h_norm    device fp32 [heads][nb]    (written; may be NULL)
+ *   ws        device workspace of tra_workspace_bytes(T,H,W,heads,head_dim,block,r_max)
+ *             bytes, owned by the caller and overwritten (its content is
+ *             meaningless afterwards); NULL takes library scratch instead.  A
+ *             workspace must not be used by two calls that may overlap.
  * Dense mode (both radii TRA_RADIUS_INF) fills radius with TRA_RADIUS_INF and
- * h_norm with 0.
+ * h_norm with 0 (ws is not touched).
  */
 int tra_probe(const void *q, const void *k, int T, int H, int W, int heads, int head_dim,
-              int block, int r_min, int r_max, int32_t *radius, float *h_norm,
+              int block, int r_min, int r_max, int32_t *radius, float *h_norm, void *ws,
               hipStream_t stream);
 
 /*
@@ -146,8 +164,9 @@ int tra_mask(const int32_t *radius, int T, int H, int W, int heads, int block, i
  * enters the softmax twice); a query block whose list keeps no key gets zeros.
  * maxcnt must lie in [1, 2^30] when lists are given.
  * Arithmetic: q.k on bf16 matrix cores with fp32 accumulation; online softmax
- * in fp32; probabilities rounded to fp16 and multiplied with v (converted
- * exactly bf16 -> fp16) on fp16 matrix cores with fp32 accumulation.
+ * in fp32; probabilities rounded to fp16 and multiplied with v 2^e_h (the
+ * per-head power-of-two scale above) on fp16 matrix cores with fp32
+ * accumulation.
  */
 int tra_attn(const void *q, const void *k, const void *v, int T, int H, int W, int heads,
              int head_dim, int block, const int32_t *idx, const int32_t *cnt, int64_t maxcnt,
@@ -188,6 +207,23 @@ int tra_token_mask(const float *r0, int T, int H, int W, int heads, int block, f
 int tra_token_attention(const void *q, const void *k, const void *v, int T, int H, int W,
                         int heads, int head_dim, int block, float tau, float gamma,
                         int min_votes, void *out, hipStream_t stream);
+
+/*
+ * The token policy's warm-up fused into one dense attention pass (Token
+ * Radius Attention ..., "The TRA Pipeline: Entropy-to-Budget" and "Fused CUDA
+ * Kernels": the entropy comes from the dense warm-up attention itself).  Writes
+ * the dense attention output (as tra_attn in dense mode) and, for every real
+ * query token, its row's entropy and base radius exactly as tra_token_probe
+ * defines them.
+ *   out      device fp32 [heads][T][H][W][head_dim]
+ *   entropy  device fp32 [heads][T][H][W] (may be NULL)
+ *   r0       device fp32 [heads][T][H][W]
+ * tau > 0 and gamma >= 0 finite.  A warm-up step is this call then
+ * tra_token_mask on r0 (and tra_plan of the lists for the steps that reuse them).
+ */
+int tra_token_warmup(const void *q, const void *k, const void *v, int T, int H, int W, int heads,
+                     int head_dim, int block, float tau, float gamma, void *out, float *entropy,
+                     float *r0, hipStream_t stream);
 
 /*
  * Sampling with inclusion-probability weighting (AB-Attention speeds up video
@@ -246,6 +282,27 @@ int tra_attn_plan(const void *q, const void *k, const void *v, int T, int H, int
                   hipStream_t stream);
 
 /*
+ * Benchmark helper: the attention kernel alone.  Builds the walk plan of the
+ * lists (idx, cnt and optional log-weights lw as for tra_attn_weighted; idx =
+ * cnt = NULL is the dense mode) and packs k and v, then launches the attention
+ * kernel `reps` times back to back on `stream` between one pair of HIP events,
+ * waits for the second event and writes the mean milliseconds per launch to
+ * *ms.  out holds the attention output (as tra_attn_weighted).  reps >= 1.
+ * Unlike the other entry points this one synchronises (on its own event).
+ */
+int tra_time_attn(const void *q, const void *k, const void *v, int T, int H, int W, int heads,
+                  int head_dim, int block, const int32_t *idx, const int32_t *cnt,
+                  const float *lw, int64_t maxcnt, int reps, void *out, float *ms,
+                  hipStream_t stream);
+
+/*
+ * Returns the current device's pooled scratch memory that no call holds any
+ * more to the driver (the pool otherwise keeps it for later calls).  Call it
+ * after the streams that used the library have been synchronised.
+ */
+int tra_release_scratch(void);
+
+/*
  * Optional per-kernel timing, for benchmarks.  Between tra_profile_begin and
  * tra_profile_end every kernel this library enqueues is bracketed by a pair of
  * hipEvents recorded on its own stream (process-wide switch; do not overlap
@@ -265,7 +322,8 @@ enum tra_kernel_kind {
     TRA_KERNEL_TOKEN_ENTROPY = 7, /* per-token entropy and base radius (warm-up) */
     TRA_KERNEL_TOKEN_MASK = 8,    /* token-disk voting lists */
     TRA_KERNEL_SIP = 9,           /* sampled lists with inverse-inclusion weights */
-    TRA_KERNEL_KINDS = 10
+    TRA_KERNEL_VMAX = 10,         /* largest |v| per head (the fp16 scale of V) */
+    TRA_KERNEL_KINDS = 11
 };
 int tra_profile_begin(void);
 int tra_profile_end(double *ms, int *launches, int n);

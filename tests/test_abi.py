@@ -96,9 +96,10 @@ def test_tra_attention_argument_errors(lib):
 
 
 def test_staged_entry_point_argument_errors(lib):
-    assert lib.tra_probe(FAKE, FAKE, 4, 16, 16, 2, 128, 64, 1, 4, None, None, None) == EINVAL
-    assert lib.tra_probe(FAKE, FAKE, 4, 16, 16, 2, 128, 64, 4, 1, FAKE, None, None) == EINVAL
-    assert lib.tra_probe(FAKE, FAKE, 4, 16, 16, 2, 80, 64, 1, 4, FAKE, None, None) == EUNSUP
+    assert lib.tra_probe(FAKE, FAKE, 4, 16, 16, 2, 128, 64, 1, 4, None, None, None, None) == EINVAL
+    assert lib.tra_probe(FAKE, FAKE, 4, 16, 16, 2, 128, 64, 4, 1, FAKE, None, FAKE, None) == EINVAL
+    assert lib.tra_probe(FAKE, FAKE, 4, 16, 16, 2, 80, 64, 1, 4, FAKE, None, FAKE, None) == EUNSUP
+    assert lib.tra_probe(None, FAKE, 4, 16, 16, 2, 128, 64, 1, 4, FAKE, None, FAKE, None) == EINVAL
     assert lib.tra_mask(FAKE, 4, 16, 16, 2, 64, -1, FAKE, FAKE, None) == EINVAL
     assert lib.tra_mask(None, 4, 16, 16, 2, 64, 3, FAKE, FAKE, None) == EINVAL
     assert lib.tra_mask(FAKE, 4, 16, 16, 2, 16, 3, FAKE, FAKE, None) == EUNSUP
@@ -106,6 +107,40 @@ def test_staged_entry_point_argument_errors(lib):
     assert lib.tra_attn(FAKE, FAKE, FAKE, 4, 16, 16, 2, 128, 64, FAKE, None, 5, FAKE, None) == EINVAL
     assert lib.tra_attn(FAKE, FAKE, FAKE, 4, 16, 16, 2, 128, 64, FAKE, FAKE, 0, FAKE, None) == EINVAL
     assert lib.tra_attn(FAKE, FAKE, FAKE, 4, 16, 16, 2, 64, 64, None, None, 0, None, None) == EINVAL
+
+
+def test_workspace_bytes_closed_form(lib):
+    # tra_probe's workspace: the fp32 block means of q and k, each 256-byte aligned
+    def up(x):
+        return (x + 255) // 256 * 256
+
+    for (T, H, W, heads, d, r_max) in [(21, 30, 52, 12, 128, 8), (8, 8, 8, 1, 64, 3),
+                                       (33, 45, 80, 24, 128, 16), (1, 1, 1, 3, 64, INF)]:
+        nb = tra.tra_grid(T, H, W)[2]
+        assert tra.tra_workspace_bytes(T, H, W, heads, d, 64, r_max) == 2 * up(heads * nb * d * 4)
+    assert lib.tra_workspace_bytes(4, 16, 16, 2, 128, 64, -1) == EINVAL
+    assert lib.tra_workspace_bytes(0, 16, 16, 2, 128, 64, 3) == EINVAL
+    assert lib.tra_workspace_bytes(4, 16, 16, 2, 96, 64, 3) == EUNSUP
+    assert lib.tra_workspace_bytes(4, 16, 16, 2, 128, 32, 3) == EUNSUP
+
+
+def test_warmup_and_timing_argument_errors(lib):
+    F = ctypes.c_float
+    ms = F()
+    args = (FAKE, FAKE, FAKE, 4, 16, 16, 2, 128, 64)
+    # tra_token_warmup: r0 and out required; tau > 0, gamma >= 0
+    assert lib.tra_token_warmup(*args, F(1.0), F(0.5), FAKE, None, None, None) == EINVAL
+    assert lib.tra_token_warmup(*args, F(1.0), F(0.5), None, None, FAKE, None) == EINVAL
+    assert lib.tra_token_warmup(*args, F(0.0), F(0.5), FAKE, None, FAKE, None) == EINVAL
+    assert lib.tra_token_warmup(*args, F(1.0), F(-1.0), FAKE, None, FAKE, None) == EINVAL
+    assert lib.tra_token_warmup(FAKE, FAKE, FAKE, 4, 16, 16, 2, 96, 64, F(1.0), F(0.5), FAKE,
+                                None, FAKE, None) == EUNSUP
+    # tra_time_attn: reps >= 1, ms given, idx/cnt together, weights only with lists
+    assert lib.tra_time_attn(*args, None, None, None, 0, 0, FAKE, ctypes.byref(ms), None) == EINVAL
+    assert lib.tra_time_attn(*args, None, None, None, 0, 3, FAKE, None, None) == EINVAL
+    assert lib.tra_time_attn(*args, FAKE, None, None, 5, 3, FAKE, ctypes.byref(ms), None) == EINVAL
+    assert lib.tra_time_attn(*args, None, None, FAKE, 0, 3, FAKE, ctypes.byref(ms), None) == EINVAL
+    assert lib.tra_time_attn(*args, FAKE, FAKE, None, 0, 3, FAKE, ctypes.byref(ms), None) == EINVAL
 
 
 def test_plan_bytes_closed_form(lib):

@@ -27,6 +27,7 @@ INF = tra.TRA_RADIUS_INF
 MAX_ABS = 1e-2
 L1_REL = 1e-3
 BAND = 1e-4
+HN_ABS = 1e-5   # fp32 pooled logits and entropy against fp64
 
 
 # ---------------------------------------------------------------- helpers --
@@ -99,8 +100,10 @@ def check_radii(hn_gpu, r_gpu, hn_ref, r_ref, r_min, r_max, what):
     assert np.array_equal(own, r_gpu), f"{what}: radius does not follow its own h_norm"
     band = boundary_blocks(hn_ref, r_min, r_max)
     diff = r_gpu != r_ref
-    print(f"[parity] {what}: h_norm max|d|={np.abs(hn_gpu - hn_ref).max():.2e}, "
+    hn_err = float(np.abs(hn_gpu.astype(np.float64) - hn_ref).max())
+    print(f"[parity] {what}: h_norm max|d|={hn_err:.2e}, "
           f"boundary blocks={int(band.sum())}, radius mismatches={int(diff.sum())}", flush=True)
+    assert hn_err <= HN_ABS, f"{what}: h_norm max|d| {hn_err}"
     for h, b in zip(*np.nonzero(band)):
         print(f"[boundary] {what} head {h} block {b}: h_norm oracle={hn_ref[h, b]:.7f} "
               f"gpu={hn_gpu[h, b]:.7f} r oracle={r_ref[h, b]} gpu={r_gpu[h, b]}", flush=True)
@@ -127,6 +130,31 @@ def sample_rows(shape, n, seed=0):
         for t, y, x in ((0, 0, 0), (T - 1, H - 1, W - 1), (T // 2, H - 1, 0), (0, 0, W - 1)):
             rows.add(h * N + (t * H + y) * W + x)
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def item_rows(shape, per_block=1, seed=0):
+    """Seeded rows covering every attention work item: for each head and each
+    pair of vertically adjacent query blocks (frame t, tile rows 2p and 2p + 1,
+    tile column bx), `per_block` random real query tokens of each block of the
+    pair (the first drawn among the block's first 32 real queries, the next
+    among the rest when there are any, so both waves of a block are reached)."""
+    heads, T, H, W, d = shape
+    N = T * H * W
+    nby, nbx = -(-H // 8), -(-W // 8)
+    rng = np.random.default_rng(seed)
+    rows = []
+    for h in range(heads):
+        for t in range(T):
+            for by in range(nby):
+                for bx in range(nbx):
+                    ny, nx = min(8, H - 8 * by), min(8, W - 8 * bx)
+                    nq = ny * nx
+                    for j in range(per_block):
+                        lo, hi = (0, min(32, nq)) if j % 2 == 0 or nq <= 32 else (32, nq)
+                        qi = int(rng.integers(lo, hi))
+                        y, x = 8 * by + qi // nx, 8 * bx + qi % nx
+                        rows.append(h * N + (t * H + y) * W + x)
+    return np.unique(np.array(rows, dtype=np.int64))
 
 
 # ------------------------------------------------------ small full grids --
@@ -323,19 +351,28 @@ def test_plan_reuse_across_steps():
         assert_close(out.cpu().numpy().reshape(-1, d)[rows], ref, f"plan reuse step {step}")
 
 
-def test_work_order_ranges():
+@pytest.mark.parametrize("skewed", [False, True], ids=["balanced", "capped"])
+def test_work_order_ranges(skewed):
     # The work order deals the walk items to eight XCD ranges: contiguous raster
     # ranges cut at equal shares of the total work (walk length + 4 per item),
     # each of at most cap = 2 ceil(items / 8) items, taken longest first into
-    # grid slots 8 k + x, -1 past a range's end.  Every item appears once.
+    # grid slots 8 k + x, -1 past a range's end.  Every item appears once.  The
+    # skewed case puts nearly all the work in the first items, so equal-work
+    # cuts would leave the later ranges above the cap: the cap moves the cuts.
     T, H, W, heads = 6, 30, 52, 3
     shp = (heads, T, H, W, 128)
-    print(f"[case] work order {shp}", flush=True)
+    print(f"[case] work order {shp} skewed={skewed}", flush=True)
     nb = tra.tra_grid(T, H, W)[2]
     rng = np.random.default_rng(17)
-    radii = rng.integers(2, 4, size=(heads, nb)).astype(np.int32)
-    radii[:, : nb // 3] = 1  # a cheap third: equal counts would not balance the work
-    idx, cnt, maxcnt = gpu_mask(radii, shp, 3)
+    if skewed:
+        radii = np.zeros((heads, nb), dtype=np.int32)
+        radii[0, : nb // 4] = 6          # a few long walks at the very start
+        r_max = 6
+    else:
+        radii = rng.integers(2, 4, size=(heads, nb)).astype(np.int32)
+        radii[:, : nb // 3] = 1  # a cheap third: equal counts would not balance the work
+        r_max = 3
+    idx, cnt, maxcnt = gpu_mask(radii, shp, r_max)
     plan = torch.zeros(tra.tra_plan_bytes(T, H, W, heads, 64, maxcnt), dtype=torch.uint8,
                        device="cuda")
     tra.tra_plan(idx, cnt, maxcnt, T, H, W, heads, 64, plan)
@@ -363,14 +400,26 @@ def test_work_order_ranges():
         clamped |= hi != cut
         col = order[x::8]
         n = hi - lo
+        assert n <= cap, f"range {x} above the cap"
         assert np.array_equal(np.sort(col[:n]), np.arange(lo, hi)), f"range {x}"
         assert (col[n:] == -1).all(), f"range {x}: slots past the end"
         assert (np.diff(ulen[col[:n]]) <= 0).all(), f"range {x}: not longest first"
         works.append(int(cost[lo:hi].sum()))
     print(f"[order] items {items} cap {cap} range work {works} mean {total / 8:.0f} "
           f"clamped {clamped}", flush=True)
-    assert not clamped  # this workload fits the cap, so the cuts are the equal shares
-    assert max(works) <= total / 8 + cost.max()
+    assert hi == items
+    if skewed:
+        assert clamped  # the cap had to move at least one cut
+    else:
+        assert not clamped  # this workload fits the cap, so the cuts are the equal shares
+        assert max(works) <= total / 8 + cost.max()
+    # the attention along the capped order is still exact
+    if skewed:
+        q, k, v = ti.random_qkv(T, H, W, heads, 128, seed=23)
+        out = gpu_attn(dev16(q), dev16(k), dev16(v), shp, idx, cnt, maxcnt).cpu().numpy()
+        rows = item_rows(shp, 1, seed=5)
+        ref = oracle.attention_rows(q, k, v, radii, rows)
+        assert_close(out.reshape(-1, 128)[rows], ref, "attention along the capped order")
 
 
 def test_binary_routing():
@@ -447,9 +496,50 @@ def workload_inputs(wid):
     return _CACHE[wid]
 
 
-@pytest.mark.parametrize("wid", [ti.WAN13B_81F, ti.WAN13B_241F, ti.WAN14B_81F, ti.HUNYUAN_129F],
+def test_wan13b_81f_every_row():
+    # The headline layer in full: probe radii, lists, and every one of its
+    # heads x T x H x W output rows against the oracle on the GPU's radii.
+    c = ti.WORKLOADS[ti.WAN13B_81F]
+    shp = (c.heads, c.T, c.H, c.W, c.d)
+    print(f"[case] {c.slug} every row {shp} r=[{c.r_min},{c.r_max}]", flush=True)
+    q, k, v = workload_inputs(ti.WAN13B_81F)
+    qd, kd, vd = dev16(q), dev16(k), dev16(v)
+    hn_g, r_g = gpu_probe(qd, kd, shp, c.r_min, c.r_max)
+    hn_o, r_o = oracle.probe(q, k, c.r_min, c.r_max)
+    check_radii(hn_g, r_g, hn_o, r_o, c.r_min, c.r_max, f"{c.slug} probe")
+    idx, cnt, maxcnt = gpu_mask(r_g, shp, c.r_max)
+    check_lists(idx, cnt, r_g, shp, maxcnt, f"{c.slug} mask")
+    nb = tra.tra_grid(c.T, c.H, c.W)[2]
+    print(f"[parity] {c.slug}: block density {cnt.sum().item() / (c.heads * nb * nb):.4f}",
+          flush=True)
+    del idx, cnt
+    got = gpu_attention(qd, kd, vd, shp, c.r_min, c.r_max).cpu().numpy()
+    ref = oracle.attention(q, k, v, r_g)
+    assert_close(got, ref, f"{c.slug} attention (all {c.heads * c.N} rows)")
+
+
+def test_wan13b_81f_dense_mode():
+    c = ti.WORKLOADS[ti.WAN13B_81F]
+    shp = (c.heads, c.T, c.H, c.W, c.d)
+    print(f"[case] {c.slug} dense {shp}", flush=True)
+    q, k, v = workload_inputs(ti.WAN13B_81F)
+    qd, kd, vd = dev16(q), dev16(k), dev16(v)
+    out = gpu_attention(qd, kd, vd, shp, INF, INF)
+    # two rows of every query block (one per wave where the block has more
+    # than 32 real queries): every work item of the dense launch
+    rows = np.union1d(item_rows(shp, 2, seed=11), sample_rows(shp, 0, seed=11))
+    got = out.view(-1, c.d)[torch.from_numpy(rows).cuda()].cpu().numpy()
+    nb = tra.tra_grid(c.T, c.H, c.W)[2]
+    ref = oracle.attention_rows(q, k, v, oracle.dense_radii(c.heads, nb), rows)
+    assert_close(got, ref, f"{c.slug} dense ({rows.size} rows, every query block)")
+
+
+@pytest.mark.parametrize("wid", [ti.WAN13B_241F, ti.WAN14B_81F, ti.HUNYUAN_129F],
                          ids=lambda w: ti.WORKLOADS[w].slug)
 def test_full_workload(wid):
+    # The larger layers: probe, lists in full; outputs on one random row of
+    # every query block (so every work item and walk of the launch is
+    # compared) plus edge-tile rows.
     c = ti.WORKLOADS[wid]
     shp = (c.heads, c.T, c.H, c.W, c.d)
     print(f"[case] {c.slug} {shp} r=[{c.r_min},{c.r_max}]", flush=True)
@@ -465,22 +555,114 @@ def test_full_workload(wid):
     print(f"[parity] {c.slug}: block density {density:.4f}", flush=True)
     del idx, cnt
     out = gpu_attention(qd, kd, vd, shp, c.r_min, c.r_max)
-    rows = sample_rows(shp, 96, seed=wid)
+    rows = np.union1d(item_rows(shp, 1, seed=wid), sample_rows(shp, 0, seed=wid))
     got = out.view(-1, c.d)[torch.from_numpy(rows).cuda()].cpu().numpy()
     del out
     ref = oracle.attention_rows(q, k, v, r_g, rows)
-    assert_close(got, ref, f"{c.slug} attention (sampled rows)")
+    assert_close(got, ref, f"{c.slug} attention ({rows.size} rows, every query block)")
 
 
-def test_wan13b_81f_dense_mode():
-    c = ti.WORKLOADS[ti.WAN13B_81F]
-    shp = (c.heads, c.T, c.H, c.W, c.d)
-    print(f"[case] {c.slug} dense {shp}", flush=True)
-    q, k, v = workload_inputs(ti.WAN13B_81F)
+# ------------------------------------------------------- the range of V --
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_v_of_any_finite_magnitude(d):
+    # V enters the fp16 P.V product scaled by a power of two per head: heads
+    # whose values reach 1e5 (beyond fp16's 65504) or stay near 1e-6 (below
+    # fp16's normal range), and one head mixing both extremes, must all match
+    # the oracle within the usual bars (dense mode and lists).
+    T, H, W, heads = 3, 20, 28, 4
+    shp = (heads, T, H, W, d)
+    print(f"[case] V magnitudes {shp}", flush=True)
+    q, k, v = ti.random_qkv(T, H, W, heads, d, seed=31)
+    vf = ti.bf16_to_f32(v).astype(np.float64)
+    scale = np.array([1e5 / 4.5, 1e-6, 1.0, 1.0])[:, None, None, None, None]
+    vf = vf * scale
+    # head 3: a few values at 1e5 among N(0, 1) values and values near 1e-6
+    rng = np.random.default_rng(2)
+    flat = vf[3].reshape(-1)
+    pick = rng.choice(flat.size, size=64, replace=False)
+    flat[pick[:8]] = 1e5 * np.sign(rng.standard_normal(8))
+    flat[pick[8:]] = 1e-6 * rng.standard_normal(56)
+    v2 = ti.bf16_from_f32(vf.astype(np.float32))
+    vmax = np.abs(ti.bf16_to_f32(v2)).reshape(heads, -1).max(axis=1)
+    print(f"[case] per-head max|v| {vmax}", flush=True)
+    assert vmax[0] > 65504 and vmax[1] < 6.1e-5
+    qd, kd, vd = dev16(q), dev16(k), dev16(v2)
+    nb = tra.tra_grid(T, H, W)[2]
+    dense = gpu_attn(qd, kd, vd, shp).cpu().numpy()
+    ref = oracle.attention(q, k, v2, oracle.dense_radii(heads, nb))
+    assert_close(dense[2], ref[2], "dense, head 2 (N(0, 1) values)")
+    # Every head against the L1-relative bar, and the max-abs bar in units of
+    # the head's value scale: max|v| / 4 (about 1 for N(0, 1) values, whose
+    # largest |v| over a head is 4 to 5).  fp16 probabilities carry a relative
+    # rounding of 2^-12 whatever V is, so an output row that averages values
+    # of 1e5 has an absolute error of order 1e5 2^-12 and only such a bar is
+    # scale-free.
+    bar = MAX_ABS * vmax / 4.0
+    for h in range(heads):
+        err = np.abs(dense[h].astype(np.float64) - ref[h])
+        print(f"[parity] V magnitudes dense head {h}: max_abs={err.max():.3e} (bar {bar[h]:.3e}) "
+              f"l1_rel={err.sum() / np.abs(ref[h]).sum():.3e}", flush=True)
+        assert np.isfinite(dense[h]).all()
+        assert err.sum() / np.abs(ref[h]).sum() <= L1_REL
+        assert err.max() <= bar[h]
+    radii = np.random.default_rng(3).integers(0, 3, size=(heads, nb)).astype(np.int32)
+    idx, cnt, maxcnt = gpu_mask(radii, shp, 2)
+    sparse = gpu_attn(qd, kd, vd, shp, idx, cnt, maxcnt).cpu().numpy()
+    ref = oracle.attention(q, k, v2, radii)
+    for h in range(heads):
+        err = np.abs(sparse[h].astype(np.float64) - ref[h])
+        assert np.isfinite(sparse[h]).all()
+        assert err.sum() / np.abs(ref[h]).sum() <= L1_REL, f"lists, head {h}"
+        assert err.max() <= bar[h], f"lists, head {h}"
+    # the fused layer (probe radii) over the same values
+    out = gpu_attention(qd, kd, vd, shp, 0, 2).cpu().numpy()
+    hn_g, r_g = gpu_probe(qd, kd, shp, 0, 2)
+    ref = oracle.attention(q, k, v2, r_g)
+    for h in range(heads):
+        err = np.abs(out[h].astype(np.float64) - ref[h])
+        assert np.isfinite(out[h]).all()
+        assert err.sum() / np.abs(ref[h]).sum() <= L1_REL, f"layer, head {h}"
+        assert err.max() <= bar[h], f"layer, head {h}"
+
+
+# ------------------------------------------------- workspace and timing --
+
+def test_probe_with_caller_workspace():
+    # tra_probe with a caller-owned workspace of tra_workspace_bytes bytes gives
+    # the same bits as with library scratch, and writes nothing past it.
+    T, H, W, heads, d = 3, 20, 28, 2, 128
+    shp = (heads, T, H, W, d)
+    q, k, _ = ti.make_inputs(T, H, W, heads, d, seed=4, family=33)
+    qd, kd = dev16(q), dev16(k)
+    nb = tra.tra_grid(T, H, W)[2]
+    nbytes = tra.tra_workspace_bytes(T, H, W, heads, d, 64, 3)
+    guard = 4096
+    ws = torch.full((nbytes + guard,), 0x5A, dtype=torch.uint8, device="cuda")
+    r1 = torch.empty(heads, nb, dtype=torch.int32, device="cuda")
+    h1 = torch.empty(heads, nb, dtype=torch.float32, device="cuda")
+    tra.tra_probe(qd, kd, T, H, W, heads, d, 64, 0, 3, r1, h1, ws=ws)
+    hn_g, r_g = gpu_probe(qd, kd, shp, 0, 3)
+    torch.cuda.synchronize()
+    assert np.array_equal(r1.cpu().numpy(), r_g)
+    assert np.array_equal(h1.cpu().numpy(), hn_g)
+    assert (ws[nbytes:].cpu().numpy() == 0x5A).all(), "wrote past the workspace"
+
+
+def test_timed_attention_matches_attention():
+    # The benchmark helper runs the same kernel: its output equals tra_attn's,
+    # for lists and for the dense mode.
+    T, H, W, heads, d = 4, 24, 40, 2, 128
+    shp = (heads, T, H, W, d)
+    q, k, v = ti.make_inputs(T, H, W, heads, d, seed=6, family=34)
     qd, kd, vd = dev16(q), dev16(k), dev16(v)
-    out = gpu_attention(qd, kd, vd, shp, INF, INF)
-    rows = sample_rows(shp, 48, seed=11)
-    got = out.view(-1, c.d)[torch.from_numpy(rows).cuda()].cpu().numpy()
-    nb = tra.tra_grid(c.T, c.H, c.W)[2]
-    ref = oracle.attention_rows(q, k, v, oracle.dense_radii(c.heads, nb), rows)
-    assert_close(got, ref, f"{c.slug} dense (sampled rows)")
+    nb = tra.tra_grid(T, H, W)[2]
+    radii = np.random.default_rng(8).integers(0, 3, size=(heads, nb)).astype(np.int32)
+    idx, cnt, maxcnt = gpu_mask(radii, shp, 2)
+    for lists in (True, False):
+        out = torch.full(shp, float("nan"), dtype=torch.float32, device="cuda")
+        ms = tra.tra_time_attn(qd, kd, vd, T, H, W, heads, d, 64, idx if lists else None,
+                               cnt if lists else None, None, maxcnt if lists else 0, 3, out)
+        ref = gpu_attn(qd, kd, vd, shp, idx, cnt, maxcnt) if lists else gpu_attn(qd, kd, vd, shp)
+        assert ms > 0.0
+        assert torch.equal(out, ref)

@@ -20,7 +20,8 @@ __all__ = [
     "tra_attn", "tra_grid", "tra_maxcnt", "tra_status_string", "tra_version",
     "tra_plan_bytes", "tra_plan", "tra_attn_plan", "tra_token_probe", "tra_token_mask",
     "tra_token_attention", "tra_token_warmup", "tra_sip_mask", "tra_attn_weighted",
-    "tra_workspace_bytes", "tra_time_attn", "tra_release_scratch",
+    "tra_workspace_bytes", "tra_time_attn", "tra_release_scratch", "tra_probe_static",
+    "tra_static_scratch_bytes",
     "tra_profile_begin", "tra_profile_end", "KERNEL_KINDS",
 ]
 
@@ -61,6 +62,10 @@ def library() -> ctypes.CDLL:
         lib.tra_workspace_bytes.restype = L
         lib.tra_probe.argtypes = [P, P, I, I, I, I, I, I, I, I, P, P, P, P]
         lib.tra_probe.restype = I
+        lib.tra_probe_static.argtypes = [P, P, I, I, I, I, I, I, I, I, P, P, P]
+        lib.tra_probe_static.restype = I
+        lib.tra_static_scratch_bytes.argtypes = []
+        lib.tra_static_scratch_bytes.restype = L
         lib.tra_mask.argtypes = [P, I, I, I, I, I, I, P, P, P]
         lib.tra_mask.restype = I
         lib.tra_attn.argtypes = [P, P, P, I, I, I, I, I, I, P, P, L, P, P]
@@ -184,6 +189,18 @@ def tra_probe(q, k, T, H, W, heads, head_dim, block, r_min, r_max, radius, h_nor
         _ptr(q, _bf16(), "q"), _ptr(k, _bf16(), "k"), T, H, W, heads, head_dim, block, r_min,
         r_max, _ptr(radius, _i32(), "radius"), _ptr(h_norm, _f32(), "h_norm"),
         _ptr(ws, None, "ws"), _stream(stream)), "tra_probe")
+
+
+def tra_probe_static(q, k, T, H, W, heads, head_dim, block, r_min, r_max, radius, h_norm=None,
+                     stream=None):
+    _check(library().tra_probe_static(
+        _ptr(q, _bf16(), "q"), _ptr(k, _bf16(), "k"), T, H, W, heads, head_dim, block, r_min,
+        r_max, _ptr(radius, _i32(), "radius"), _ptr(h_norm, _f32(), "h_norm"), _stream(stream)),
+        "tra_probe_static")
+
+
+def tra_static_scratch_bytes() -> int:
+    return int(library().tra_static_scratch_bytes())
 
 
 def tra_mask(radius, T, H, W, heads, block, r_max, idx, cnt, stream=None):

@@ -236,6 +236,7 @@ const char *tra_status_string(int status) {
         case TRA_ERR_UNSUPPORTED: return "TRA_ERR_UNSUPPORTED";
         case TRA_ERR_HIP: return "TRA_ERR_HIP";
         case TRA_ERR_NOMEM: return "TRA_ERR_NOMEM";
+        case TRA_ERR_TOO_LARGE: return "TRA_ERR_TOO_LARGE";
         default: return "TRA_ERR_UNKNOWN";
     }
 }
@@ -307,6 +308,24 @@ int tra_probe(const void *q, const void *k, int T, int H, int W, int heads, int 
     }
     return hip_status(e);
 }
+
+int tra_probe_static(const void *q, const void *k, int T, int H, int W, int heads, int head_dim,
+                     int block, int r_min, int r_max, int32_t *radius, float *h_norm,
+                     hipStream_t stream) {
+    tra::Grid g;
+    int rc = make_grid(T, H, W, block, &g);
+    if (rc == TRA_OK) rc = check_dims(heads, head_dim, g);
+    if (rc == TRA_OK) rc = check_radii(r_min, r_max);
+    if (rc != TRA_OK) return rc;
+    if (!q || !k || !radius) return TRA_ERR_INVALID_ARG;
+    if (probe_ws_bytes(g, heads, head_dim) > tra::kStaticScratchBytes) return TRA_ERR_TOO_LARGE;
+    void *ws = nullptr;
+    if (tra::static_scratch(&ws) != hipSuccess) return TRA_ERR_HIP;
+    return tra_probe(q, k, T, H, W, heads, head_dim, block, r_min, r_max, radius, h_norm, ws,
+                     stream);
+}
+
+int64_t tra_static_scratch_bytes(void) { return (int64_t)tra::kStaticScratchBytes; }
 
 int tra_mask(const int32_t *radius, int T, int H, int W, int heads, int block, int r_max,
              int32_t *idx, int32_t *cnt, hipStream_t stream) {

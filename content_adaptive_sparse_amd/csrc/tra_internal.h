@@ -135,4 +135,11 @@ hipError_t launch_attn(int D, const uint16_t *q, const uint16_t *kt, const uint1
                        const float2 *ubias, int64_t ustride, const int32_t *order, const Grid &g,
                        int heads, float *out, hipStream_t s, const EntropyOut *entropy = nullptr);
 
+// Static device scratch of tra_probe_static (tra_static.hip): one array of
+// kStaticScratchBytes per GPU, held until the process ends.  static_scratch
+// returns the current device's copy (its address taken with
+// hipGetSymbolAddress on the first call on that device).
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+hipError_t static_scratch(void **ptr);
+
 }  // namespace tra

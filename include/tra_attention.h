@@ -66,7 +66,8 @@ enum tra_status {
     TRA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, r_min > r_max, negative radius */
     TRA_ERR_UNSUPPORTED = -2, /* block != 64, head_dim not in {64,128}, sizes beyond int32 indexing */
     TRA_ERR_HIP = -3,         /* a HIP call or kernel launch failed */
-    TRA_ERR_NOMEM = -4        /* scratch allocation failed */
+    TRA_ERR_NOMEM = -4,       /* scratch allocation failed */
+    TRA_ERR_TOO_LARGE = -5    /* needs more than the static scratch of tra_probe_static holds */
 };
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -132,6 +133,24 @@ int64_t tra_workspace_bytes(int T, int H, int W, int heads, int head_dim, int bl
 int tra_probe(const void *q, const void *k, int T, int H, int W, int heads, int head_dim,
               int block, int r_min, int r_max, int32_t *radius, float *h_norm, void *ws,
               hipStream_t stream);
+
+/*
+ * tra_probe for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments and results as tra_probe (bit for bit), but the pooled means live
+ * in a static device array of tra_static_scratch_bytes() bytes (64 MiB) that
+ * every GPU the library runs on holds until the process ends; the call makes
+ * no allocation of any kind.  Sizes whose workspace
+ * (tra_workspace_bytes) exceeds the array return TRA_ERR_TOO_LARGE before
+ * anything is enqueued.  Every call on one GPU shares that GPU's array (its
+ * content is left from the last call and nothing in it needs clearing: the
+ * probe writes every value it reads), so calls that may overlap on one GPU --
+ * on different streams or from different threads without ordering -- race.
+ */
+int tra_probe_static(const void *q, const void *k, int T, int H, int W, int heads, int head_dim,
+                     int block, int r_min, int r_max, int32_t *radius, float *h_norm,
+                     hipStream_t stream);
+int64_t tra_static_scratch_bytes(void);
 
 /*
  * Key-block lists (Token Radius Attention ..., "The TRA Pipeline: Fused CUDA

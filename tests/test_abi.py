@@ -50,6 +50,7 @@ def test_status_strings(lib):
     assert tra.tra_status_string(-2) == "TRA_ERR_UNSUPPORTED"
     assert tra.tra_status_string(-3) == "TRA_ERR_HIP"
     assert tra.tra_status_string(-4) == "TRA_ERR_NOMEM"
+    assert tra.tra_status_string(-5) == "TRA_ERR_TOO_LARGE"
     assert tra.tra_status_string(7) == "TRA_ERR_UNKNOWN"
     assert tra.tra_version() >= 100
 
@@ -141,6 +142,16 @@ def test_warmup_and_timing_argument_errors(lib):
     assert lib.tra_time_attn(*args, FAKE, None, None, 5, 3, FAKE, ctypes.byref(ms), None) == EINVAL
     assert lib.tra_time_attn(*args, None, None, FAKE, 0, 3, FAKE, ctypes.byref(ms), None) == EINVAL
     assert lib.tra_time_attn(*args, FAKE, FAKE, None, 0, 3, FAKE, ctypes.byref(ms), None) == EINVAL
+
+
+def test_static_probe_argument_errors(lib):
+    # validated on the host before the static array is touched
+    assert lib.tra_static_scratch_bytes() == 64 << 20
+    assert lib.tra_probe_static(FAKE, FAKE, 4, 16, 16, 2, 128, 64, 1, 4, None, None, None) == EINVAL
+    assert lib.tra_probe_static(FAKE, FAKE, 4, 16, 16, 2, 80, 64, 1, 4, FAKE, None, None) == EUNSUP
+    assert lib.tra_probe_static(FAKE, FAKE, 4, 16, 16, 2, 128, 64, 4, 1, FAKE, None, None) == EINVAL
+    # block means of 64 heads of a 33 x 45 x 80 grid need more than the 64 MiB array
+    assert lib.tra_probe_static(FAKE, FAKE, 33, 45, 80, 64, 128, 64, 1, 4, FAKE, None, None) == -5
 
 
 def test_plan_bytes_closed_form(lib):

@@ -27,7 +27,7 @@ __all__ = [
 
 TRA_RADIUS_INF = 2147483647
 KERNEL_KINDS = ("pack_pool", "entropy", "mask", "attn", "fill", "order", "union",
-                "token_entropy", "token_mask", "sip", "vmax")
+                "token_entropy", "token_mask", "sip", "vmax", "pair")
 
 _lib = None
 

@@ -339,15 +339,20 @@ int tra_mask(const int32_t *radius, int T, int H, int W, int heads, int block, i
     return hip_status(tra::launch_mask(radius, g, heads, r_max, maxcnt_of(g, r_max), idx, cnt, stream));
 }
 
-// The attention walk of the lists: union of each pair's two lists, then the
-// longest-first order of the pairs.
+// The attention walk of the lists: the pair table, the union of each pair's
+// two lists, then the longest-first order of the pairs.
 static hipError_t plan_walk(const int32_t *idx, const int32_t *cnt, const float *lw,
-                            int64_t maxcnt, const tra::Grid &g, int heads, int32_t *ulist,
-                            int32_t *ulen, float2 *ubias, int32_t *order, hipStream_t stream) {
+                            int64_t maxcnt, const tra::Grid &g, int heads, int2 *pairs,
+                            int32_t *ulist, int32_t *ulen, float2 *ubias, int32_t *order,
+                            hipStream_t stream) {
     hipError_t e;
     {
+        ProfScope p(TRA_KERNEL_PAIR, stream);
+        e = tra::launch_pair(cnt, maxcnt, g, heads, pairs, stream);
+    }
+    if (e == hipSuccess) {
         ProfScope p(TRA_KERNEL_UNION, stream);
-        e = tra::launch_union(idx, cnt, lw, maxcnt, g, heads, ulist, ulen, ubias, stream);
+        e = tra::launch_union(idx, cnt, lw, maxcnt, g, heads, pairs, ulist, ulen, ubias, stream);
     }
     if (e == hipSuccess) {
         ProfScope p(TRA_KERNEL_ORDER, stream);
@@ -356,10 +361,11 @@ static hipError_t plan_walk(const int32_t *idx, const int32_t *cnt, const float 
     return e;
 }
 
-// Layout of a walk plan in one buffer: work order, walk lengths, walks and (for
-// weighted lists) the walks' per-side log2 weights; each part 256-byte aligned.
+// Layout of a walk plan in one buffer: work order, walk lengths, walks, the
+// pair table and (for weighted lists) the walks' per-side log2 weights; each
+// part 256-byte aligned.
 struct PlanLayout {
-    size_t o_order, o_ulen, o_ulist, o_ubias, bytes;
+    size_t o_order, o_ulen, o_ulist, o_pairs, o_ubias, bytes;
     int64_t ustride;
     bool weighted;
 };
@@ -374,7 +380,8 @@ static PlanLayout plan_layout(const tra::Grid &g, int heads, int64_t maxcnt,
     L.o_order = 0;
     L.o_ulen = up(order_len(g, heads) * sizeof(int32_t));
     L.o_ulist = L.o_ulen + up(rows * sizeof(int32_t));
-    L.o_ubias = L.o_ulist + up(rows * (size_t)L.ustride * sizeof(int32_t));
+    L.o_pairs = L.o_ulist + up(rows * (size_t)L.ustride * sizeof(int32_t));
+    L.o_ubias = L.o_pairs + up(rows * sizeof(int2));
     L.bytes = L.o_ubias + (weighted ? up(rows * (size_t)L.ustride * sizeof(float2)) : 0);
     return L;
 }
@@ -382,8 +389,9 @@ static PlanLayout plan_layout(const tra::Grid &g, int heads, int64_t maxcnt,
 static hipError_t plan_walk_into(const int32_t *idx, const int32_t *cnt, const float *lw,
                                  int64_t maxcnt, const tra::Grid &g, int heads, char *plan,
                                  const PlanLayout &L, hipStream_t stream) {
-    return plan_walk(idx, cnt, lw, maxcnt, g, heads, (int32_t *)(plan + L.o_ulist),
-                     (int32_t *)(plan + L.o_ulen), L.weighted ? (float2 *)(plan + L.o_ubias) : nullptr,
+    return plan_walk(idx, cnt, lw, maxcnt, g, heads, (int2 *)(plan + L.o_pairs),
+                     (int32_t *)(plan + L.o_ulist), (int32_t *)(plan + L.o_ulen),
+                     L.weighted ? (float2 *)(plan + L.o_ubias) : nullptr,
                      (int32_t *)(plan + L.o_order), stream);
 }
 
@@ -396,8 +404,10 @@ static hipError_t attn_launch(const void *q, const Packed &pk, const tra::Grid &
     const int32_t *ulen = plan ? (const int32_t *)(plan + L.o_ulen) : nullptr;
     const int32_t *ulist = plan ? (const int32_t *)(plan + L.o_ulist) : nullptr;
     const float2 *ubias = plan && L.weighted ? (const float2 *)(plan + L.o_ubias) : nullptr;
-    return tra::launch_attn(head_dim, (const uint16_t *)q, pk.kt, pk.vt, pk.vexp, ulist, ulen, ubias,
-                            plan ? L.ustride : 0, order, g, heads, (float *)out, stream, eo);
+    const int2 *pairs = plan ? (const int2 *)(plan + L.o_pairs) : nullptr;
+    return tra::launch_attn(head_dim, (const uint16_t *)q, pk.kt, pk.vt, pk.vexp, pairs, ulist,
+                            ulen, ubias, plan ? L.ustride : 0, order, g, heads, (float *)out,
+                            stream, eo);
 }
 
 // Pack k and v, then attention along a walk plan (nullptr: dense mode).

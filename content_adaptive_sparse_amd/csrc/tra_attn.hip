@@ -14,7 +14,9 @@
 // (the next block lands while the current one is computed), and each wave
 // whose block keeps it computes, per 32-key half:
 //   S^T = K Q^T        v_mfma_f32_32x32x16_bf16, fp32 accumulation
-//   online softmax     per query = per lane column, exp2 with the scale folded
+//   online softmax     per query = per lane column, exp2 with the scale folded,
+//                      against a running reference that only moves when a
+//                      probability would overflow fp16 (no max per tile)
 //   O^T += V^T P^T     v_mfma_f32_32x32x16_f16 (P rounded to fp16)
 // Working on the transposed products keeps every query's logits and output in
 // one lane pair (lanes l and l + 32), so the softmax needs a single cross-lane
@@ -27,10 +29,13 @@ namespace tra {
 namespace {
 
 constexpr int kAttnThreads = 256;
-// The running max is only moved (and O, l rescaled) when a tile's max exceeds
-// it by more than this many powers of two; in between, probabilities are
-// taken against the stale max (at most 2^8, exact in fp16) and the final
-// normalisation by l uses the same reference, so the result is unchanged.
+// Probabilities are taken against a running reference m: 2^(s log2(e)/sqrt(d)
+// - m) in fp16, which holds up to 2^16.  m is not the running max: a tile only
+// moves it when one of its probabilities overflows fp16 (the row sum becomes
+// inf), and then to the tile's max if that exceeds m by more than this many
+// powers of two (O and l rescaled).  The final normalisation by l uses the same
+// reference, so the result does not depend on it; fp16 keeps 11 significant
+// bits anywhere in its normal range.
 constexpr float kRescaleLog2 = 8.0f;
 
 // WEIGHTED: every walk entry carries, per side, a log2 weight added to the
@@ -43,7 +48,8 @@ template <int D, bool WEIGHTED, bool ENTROPY>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kt,
     const uint16_t *__restrict__ vt, const int32_t *__restrict__ vexp,
-    const int32_t *__restrict__ ulist, const int32_t *__restrict__ ulen,
+    const int2 *__restrict__ pairs, const int32_t *__restrict__ ulist,
+    const int32_t *__restrict__ ulen,
     const float2 *__restrict__ ubias, int64_t ustride, const int32_t *__restrict__ order, Grid g,
     int heads, int pairs_per_head, int per_xcd, FastDiv div_nbx, FastDiv div_nby,
     float *__restrict__ out, float scale_log2, EntropyOut eo) {
@@ -63,12 +69,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     __shared__ __attribute__((aligned(1024))) uint16_t kring[2][TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t vring[2][TILE];
 
-    // Work item: a pair of vertically adjacent query blocks of one head.
-    // Consecutive workgroup ids land on different XCDs; every XCD is given a
-    // contiguous range of items so its L2 sees neighbouring query blocks.  With
-    // a work order (lists of unequal length) the ranges hold equal shares of
-    // the total work and each is taken longest first; without one (dense mode:
-    // equal work) the ranges hold equal item counts in raster order.
+    // Work item: two query blocks of one head -- the plan's pair table, or
+    // vertically adjacent blocks in dense mode.  Consecutive workgroup ids land
+    // on different XCDs; every XCD is given a contiguous range of items so its
+    // L2 sees neighbouring query blocks.  With a work order (lists of unequal
+    // length) the ranges hold equal shares of the total work and each is taken
+    // longest first; without one (dense mode: equal work) the ranges hold equal
+    // item counts in raster order.
     const int64_t total = (int64_t)heads * pairs_per_head;
     int64_t item;
     if (order) {
@@ -80,7 +87,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     if (item >= total) return;
     const int h = (int)(item / pairs_per_head);
     int blk[2];
-    pair_blocks((int)(item % pairs_per_head), g, blk[0], blk[1]);
+    if (pairs) {
+        const int2 pr = reinterpret_cast<const int2 *>(pairs)[item];
+        blk[0] = __builtin_amdgcn_readfirstlane(pr.x);
+        blk[1] = __builtin_amdgcn_readfirstlane(pr.y);
+        if (blk[0] < 0) return;  // an unused slot of the pair table
+    } else {
+        pair_blocks((int)(item % pairs_per_head), g, blk[0], blk[1]);
+    }
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -220,6 +234,77 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     }
     __syncthreads();
 
+    // Row sums of fp16 probabilities (two independent chains).
+    auto row_sum_f16 = [&](const f16x8_t &p, float s0, float &s1) -> float {
+        const f16x2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+        for (int e = 0; e < 8; e += 4) {
+            const f16x2_t a = {p[e], p[e + 1]};
+            const f16x2_t b = {p[e + 2], p[e + 3]};
+            s0 = __builtin_amdgcn_fdot2(a, one2, s0, false);
+            s1 = __builtin_amdgcn_fdot2(b, one2, s1, false);
+        }
+        return s0;
+    };
+    // fp16 probabilities 2^(s log2(e) / sqrt(d) + bias) of one tile and their
+    // row sum (this lane's keys).  Missing keys of an edge tile (rows >= kny,
+    // columns >= knx; their logits are 0 from the zero K rows) are cleared in
+    // the fp16 registers: a packed register holds key row 4 hf + 2 ks2 + j / 2
+    // (register j of the 8-element group) and key columns 4 hl + 2 (j % 2) and
+    // the next one.
+    // ENTROPY: the logits of missing keys are already -1e30 (so their
+    // probabilities are 0 here) and the fp32 sums z = sum 2^x, a = sum x 2^x of
+    // this lane's keys are returned as well.
+    auto softmax_fp16 = [&](const f32x16_t (&sv)[2], float bias, int kny_, int knx_,
+                            f16x8_t (&pn)[2][2], float &z, float &a) -> float {
+        float s0 = 0.f, s1 = 0.f;
+        float z0 = 0.f, z1 = 0.f, a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int ks2 = 0; ks2 < 2; ++ks2) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = __builtin_fmaf(sv[hf][8 * ks2 + e], scale_log2, bias);
+                    const float p = __builtin_amdgcn_exp2f(x);
+                    pn[hf][ks2][e] = (_Float16)p;
+                    if constexpr (ENTROPY) {
+                        if (e & 1) {
+                            z1 += p;
+                            a1 = __builtin_fmaf(p, x, a1);
+                        } else {
+                            z0 += p;
+                            a0 = __builtin_fmaf(p, x, a0);
+                        }
+                    }
+                }
+            }
+        z = z0 + z1;
+        a = a0 + a1;
+        if (kny_ < kTileSide || knx_ < kTileSide) {
+            const int cm = knx_ - 4 * hl;  // real columns among this lane's four
+            const uint32_t m01 = cm >= 2 ? 0xffffffffu : (cm == 1 ? 0x0000ffffu : 0u);
+            const uint32_t m23 = cm >= 4 ? 0xffffffffu : (cm == 3 ? 0x0000ffffu : 0u);
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int ks2 = 0; ks2 < 2; ++ks2) {
+                    u32x4_t w = __builtin_bit_cast(u32x4_t, pn[hf][ks2]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const bool row_ok = 4 * hf + 2 * ks2 + j / 2 < kny_;
+                        w[j] &= row_ok ? ((j & 1) ? m23 : m01) : 0u;
+                    }
+                    pn[hf][ks2] = __builtin_bit_cast(f16x8_t, w);
+                }
+        }
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int ks2 = 0; ks2 < 2; ++ks2) s0 = row_sum_f16(pn[hf][ks2], s0, s1);
+        return s0 + s1;
+    };
+
     // Probabilities (fp16) of the previous entry, waiting for their P.V, and
     // the rescale of O their reference asks for.
     f16x8_t pk[2][2];
@@ -238,6 +323,18 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
         constexpr bool DS = decltype(ds_tag)::value != 0;
         constexpr bool DP = decltype(dp_tag)::value != 0;
         f32x16_t sb[2];
+        int kny = kTileSide, knx = kTileSide;
+        // a reference move of the previous entry rescales O before this step's
+        // P.V (the multiply waits for the previous products); taken first so that
+        // the products and the softmax below share one basic block
+        if constexpr (DP) {
+            if (rescale) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[mt][r] *= alpha_o;
+            }
+        }
         if constexpr (DS) {
             const uint16_t *Kt = kring[s];
 #pragma unroll
@@ -254,16 +351,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
             const uint32_t row = fdiv(kb, div_nbx);
             const int kbx = (int)(kb - row * div_nbx.d);
             const int kby = (int)(row - fdiv(row, div_nby) * div_nby.d);
-            mask_edge_keys(sb, min(kTileSide, g.H - kTileSide * kby),
-                           min(kTileSide, g.W - kTileSide * kbx), hl, kMaskFill);
+            kny = min(kTileSide, g.H - kTileSide * kby);
+            knx = min(kTileSide, g.W - kTileSide * kbx);
+            if constexpr (ENTROPY) mask_edge_keys(sb, kny, knx, hl, kMaskFill);
         }
         if constexpr (DP) {
-            if (rescale) {
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[mt][r] *= alpha_o;
-            }
             const uint16_t *Vt = vring[s ^ 1];
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf)
@@ -276,62 +368,45 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
                     }
         }
         if constexpr (DS) {
-            float mx = -INFINITY;
+            // Probabilities against the running reference without a max: a key
+            // more than 2^16 above it overflows fp16 to inf, which the row sum
+            // shows; only then is the step redone against a moved reference.
+            f16x8_t pn[2][2];
+            float z, a;
+            float psum = softmax_fp16(sb, w0 - m_ref, ENTROPY ? kTileSide : kny,
+                                      ENTROPY ? kTileSide : knx, pn, z, a);
+            if (__builtin_expect(__any(!(psum < INFINITY)), 0)) {
+                if constexpr (!ENTROPY) mask_edge_keys(sb, kny, knx, hl, -INFINITY);
+                float mx = -INFINITY;
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sb[hf][r]);
+                mx = half_swap_max(mx) * scale_log2 + w0;
+                const bool grow = mx > m_ref + kRescaleLog2;
+                const float m_new = grow ? mx : m_ref;
+                alpha_o = __builtin_amdgcn_exp2f(m_ref - m_new);
+                if constexpr (ENTROPY) {
+                    // moving the reference by delta: Z' = 2^-delta Z, A' = 2^-delta (A - delta Z)
+                    ent_a = alpha_o * __builtin_fmaf(m_ref - m_new, ent_z, ent_a);
+                    ent_z *= alpha_o;
+                }
+                m_ref = m_new;
+                l_run *= alpha_o;
+                rescale = true;  // O follows before this entry's P.V
+                psum = softmax_fp16(sb, w0 - m_ref, kTileSide, kTileSide, pn, z, a);
+            } else {
+                rescale = false;
+            }
+            l_run += psum;
+            if constexpr (ENTROPY) {
+                ent_z += z;
+                ent_a += a;
+            }
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sb[hf][r]);
-            mx = half_swap_max(mx) * scale_log2 + w0;
-            const bool grow = mx > m_ref + kRescaleLog2;
-            const float m_new = grow ? mx : m_ref;
-            const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-            if constexpr (ENTROPY) {
-                // moving the reference by delta: Z' = 2^-delta Z, A' = 2^-delta (A - delta Z)
-                ent_a = alpha * __builtin_fmaf(m_ref - m_new, ent_z, ent_a);
-                ent_z *= alpha;
-            }
-            m_ref = m_new;
-            const float bias = w0 - m_ref;
-            float psum0 = 0.f, psum1 = 0.f;
-            const f16x2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                if constexpr (ENTROPY) {
-                    float z0 = 0.f, z1 = 0.f, a0 = 0.f, a1 = 0.f;
-#pragma unroll
-                    for (int r = 0; r < 16; r += 2) {
-                        const float x0 = __builtin_fmaf(sb[hf][r], scale_log2, bias);
-                        const float x1 = __builtin_fmaf(sb[hf][r + 1], scale_log2, bias);
-                        sb[hf][r] = __builtin_amdgcn_exp2f(x0);
-                        sb[hf][r + 1] = __builtin_amdgcn_exp2f(x1);
-                        z0 += sb[hf][r];
-                        z1 += sb[hf][r + 1];
-                        a0 = __builtin_fmaf(sb[hf][r], x0, a0);
-                        a1 = __builtin_fmaf(sb[hf][r + 1], x1, a1);
-                    }
-                    ent_z += z0 + z1;
-                    ent_a += a0 + a1;
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        sb[hf][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[hf][r], scale_log2, bias));
-                }
-#pragma unroll
-                for (int ks2 = 0; ks2 < 2; ++ks2) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) pk[hf][ks2][e] = (_Float16)sb[hf][8 * ks2 + e];
-#pragma unroll
-                    for (int e = 0; e < 8; e += 4) {
-                        const f16x2_t a = {pk[hf][ks2][e], pk[hf][ks2][e + 1]};
-                        const f16x2_t b = {pk[hf][ks2][e + 2], pk[hf][ks2][e + 3]};
-                        psum0 = __builtin_amdgcn_fdot2(a, one2, psum0, false);
-                        psum1 = __builtin_amdgcn_fdot2(b, one2, psum1, false);
-                    }
-                }
-            }
-            l_run = l_run * alpha + (psum0 + psum1);
-            rescale = __any(grow);  // O follows before this entry's P.V
-            alpha_o = alpha;
+                for (int ks2 = 0; ks2 < 2; ++ks2) pk[hf][ks2] = pn[hf][ks2];
         }
     };
     using T0 = SlotTag<0>;
@@ -396,9 +471,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
 }  // namespace
 
 hipError_t launch_attn(int D, const uint16_t *q, const uint16_t *kt, const uint16_t *vt,
-                       const int32_t *vexp, const int32_t *ulist, const int32_t *ulen,
-                       const float2 *ubias, int64_t ustride, const int32_t *order, const Grid &g,
-                       int heads, float *out, hipStream_t s, const EntropyOut *entropy) {
+                       const int32_t *vexp, const int2 *pairs, const int32_t *ulist,
+                       const int32_t *ulen, const float2 *ubias, int64_t ustride,
+                       const int32_t *order, const Grid &g, int heads, float *out, hipStream_t s,
+                       const EntropyOut *entropy) {
     const int pph = pairs_per_head(g);
     const int64_t total = (int64_t)heads * pph;
     const int per_xcd = (int)((total + 7) / 8);
@@ -409,9 +485,9 @@ hipError_t launch_attn(int D, const uint16_t *q, const uint16_t *kt, const uint1
     const FastDiv div_nbx = make_fastdiv(g.nbx), div_nby = make_fastdiv(g.nby);
     const EntropyOut eo = entropy ? *entropy : EntropyOut{nullptr, nullptr, 0.f, 0.f};
 #define TRA_LAUNCH(DD, WW, EE)                                                                \
-    hipLaunchKernelGGL((attn_kernel<DD, WW, EE>), grid, block, 0, s, q, kt, vt, vexp, ulist,     \
-                       ulen, ubias, ustride, order, g, heads, pph, per_xcd, div_nbx, div_nby, out, \
-                       scale_log2, eo)
+    hipLaunchKernelGGL((attn_kernel<DD, WW, EE>), grid, block, 0, s, q, kt, vt, vexp, pairs,     \
+                       ulist, ulen, ubias, ustride, order, g, heads, pph, per_xcd, div_nbx,        \
+                       div_nby, out, scale_log2, eo)
     const bool weighted = ubias != nullptr && ulist != nullptr;
     if (weighted && entropy) return hipErrorInvalidValue;
     if (D == 128 && weighted)

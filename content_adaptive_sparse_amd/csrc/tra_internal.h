@@ -36,7 +36,7 @@ size_t packed_tile_elems(int D);
 // is multiplied back by 2^-e_h.  vmax_kernel writes vmax_parts(g, D) partial
 // maxima per head (vpart [heads][parts], bfloat16 bits of |v|); the packing
 // kernel reduces them, scales V and writes e_h to vexp [heads].
-constexpr int kVmaxParts = 64;
+constexpr int kVmaxParts = 256;  // at most the packing kernel's 256 threads
 int vmax_parts(const Grid &g, int D);
 hipError_t launch_vmax(int D, const uint16_t *v, const Grid &g, int heads, uint32_t *vpart,
                        hipStream_t s);
@@ -93,8 +93,15 @@ __host__ __device__ inline void pair_blocks(int p, const Grid &g, int &qa, int &
 // entry's (upper, lower) block weight in log2 units.
 int64_t union_stride(int64_t maxcnt);
 hipError_t launch_union(const int32_t *idx, const int32_t *cnt, const float *lw, int64_t maxcnt,
-                        const Grid &g, int heads, int32_t *ulist, int32_t *ulen, float2 *ubias,
-                        hipStream_t s);
+                        const Grid &g, int heads, const int2 *pairs, int32_t *ulist, int32_t *ulen,
+                        float2 *ubias, hipStream_t s);
+
+// Pair table of a list set (see tra_mask.hip): for every head, pairs_per_head
+// item slots (qa, qb) -- vertical neighbours whose list lengths are within a
+// factor of two, the other blocks re-paired by length class -- then unused
+// slots (-1, -1); qb = -1 marks a single block.
+hipError_t launch_pair(const int32_t *cnt, int64_t maxcnt, const Grid &g, int heads, int2 *pairs,
+                       hipStream_t s);
 
 // Sampled lists with log-weights from the pooled logit matrix and uniforms
 // u[heads][nb][nb] (row stride nb for idx and lw).
@@ -128,12 +135,14 @@ struct EntropyOut {
     float two_gamma_log2e;
 };
 
-// ulist == nullptr: the dense mode (every block, both sides; order null, items
-// in XCD-contiguous raster order).  vexp: the per-head V exponents.
+// ulist == nullptr: the dense mode (every block, both sides; order and pairs
+// null, vertical pairs in XCD-contiguous raster order).  vexp: the per-head V
+// exponents.  pairs: the plan's pair table.
 hipError_t launch_attn(int D, const uint16_t *q, const uint16_t *kt, const uint16_t *vt,
-                       const int32_t *vexp, const int32_t *ulist, const int32_t *ulen,
-                       const float2 *ubias, int64_t ustride, const int32_t *order, const Grid &g,
-                       int heads, float *out, hipStream_t s, const EntropyOut *entropy = nullptr);
+                       const int32_t *vexp, const int2 *pairs, const int32_t *ulist,
+                       const int32_t *ulen, const float2 *ubias, int64_t ustride,
+                       const int32_t *order, const Grid &g, int heads, float *out, hipStream_t s,
+                       const EntropyOut *entropy = nullptr);
 
 // Static device scratch of tra_probe_static (tra_static.hip): one array of
 // kStaticScratchBytes per GPU, held until the process ends.  static_scratch

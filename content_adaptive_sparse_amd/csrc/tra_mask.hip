@@ -66,8 +66,155 @@ hipError_t launch_mask(const int32_t *radius, const Grid &g, int heads, int r_ma
 namespace tra {
 namespace {
 
-// Union of the two key lists of a work item (a pair of vertically adjacent
-// query blocks), the walk the attention kernel takes: entries
+// Work items: which two query blocks of a head share one attention workgroup
+// (and its copied key/value tiles).  Vertically adjacent blocks (tile rows
+// 2 p and 2 p + 1 of one frame and column: short-axis neighbours, whose lists
+// mostly coincide) stay together when their list lengths are within a factor
+// of two.  The blocks of every other vertical pair are re-paired by length
+// class: sorted by a key of four classes per octave of the length, longest
+// first and in raster order inside a class, and paired in that order, so that
+// a block that keeps every key block (binary routing) shares its walk with
+// another such block instead of idling half the workgroup beside a short
+// list.  One workgroup of 1024 threads per head writes the head's
+// pairs_per_head item slots: the kept vertical pairs in raster order, then the
+// re-paired ones, then unused slots (-1, -1).  The counting sort is stable:
+// a chunk's ranks inside each class come from a 1024-bit membership mask.
+constexpr int kScanThreads = 1024;
+
+// Exclusive prefix sum of one value per thread over the block (1024 threads):
+// shuffles within each wave, then the 16 wave totals.  Every thread gets its
+// exclusive prefix; *total receives the block total.
+__device__ int64_t block_exclusive_scan(int64_t v, int64_t *wave_sums, int64_t *total) {
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    int64_t x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int64_t y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) wave_sums[wid] = x;
+    __syncthreads();
+    if (tid == 0) {
+        int64_t run = 0;
+        for (int w = 0; w < kScanThreads / 64; ++w) {
+            const int64_t t = wave_sums[w];
+            wave_sums[w] = run;
+            run += t;
+        }
+        *total = run;
+    }
+    __syncthreads();
+    const int64_t r = wave_sums[wid] + x - v;
+    __syncthreads();  // wave_sums may be reused by the next scan
+    return r;
+}
+
+constexpr int kPairThreads = kScanThreads;
+constexpr int kPairClasses = 128;
+
+__device__ __forceinline__ int length_class(int c) {
+    const uint32_t x = (uint32_t)(c < 0 ? 0 : c) + 1u;
+    const int e = 31 - __builtin_clz(x);  // floor(log2 x) <= 30
+    const uint32_t f = e >= 2 ? (x >> (e - 2)) & 3u : (x << (2 - e)) & 3u;
+    return 4 * e + (int)f;  // < 124
+}
+
+__device__ __forceinline__ bool lengths_pair_well(int a, int b) {
+    return 2 * (int64_t)min(a, b) >= (int64_t)max(a, b);
+}
+
+__global__ __launch_bounds__(kPairThreads) void pair_kernel(const int32_t *__restrict__ cnt,
+                                                           int64_t maxcnt, Grid g, int pph,
+                                                           int2 *__restrict__ pairs) {
+    __shared__ int64_t wave_sums[kPairThreads / 64];
+    __shared__ int64_t total_sh;
+    __shared__ int start[kPairClasses], run[kPairClasses];
+    __shared__ uint32_t member[kPairClasses][kPairThreads / 32];
+    const int h = blockIdx.x, tid = threadIdx.x;
+    const int32_t *ch = cnt + (int64_t)h * g.nb;
+    int2 *out = pairs + (int64_t)h * pph;
+    auto len = [&](int b) -> int {
+        const int64_t m = ch[b];
+        return (int)(m < 0 ? 0 : (m > maxcnt ? maxcnt : m));
+    };
+    // the vertical partner of block b (-1 when its tile row has none)
+    auto partner = [&](int b) -> int {
+        const int by = (b / g.nbx) % g.nby;
+        const int o = (by & 1) ? b - g.nbx : b + g.nbx;
+        return ((by & 1) || by + 1 < g.nby) ? o : -1;
+    };
+    auto orphan = [&](int b) -> bool {
+        const int o = partner(b);
+        return o >= 0 && !lengths_pair_well(len(b), len(o));
+    };
+    // kept vertical pairs, compacted in raster order
+    int64_t kept = 0;
+    for (int p0 = 0; p0 < pph; p0 += kPairThreads) {
+        const int p = p0 + tid;
+        int qa = -1, qb = -1;
+        bool keep = false;
+        if (p < pph) {
+            pair_blocks(p, g, qa, qb);
+            keep = qb < 0 || lengths_pair_well(len(qa), len(qb));
+        }
+        int64_t tot;
+        const int64_t at = block_exclusive_scan(keep ? 1 : 0, wave_sums, &total_sh);
+        tot = total_sh;
+        if (keep) out[kept + at] = make_int2(qa, qb);
+        kept += tot;
+        __syncthreads();
+    }
+    // orphans per length class, longest class first
+    for (int k = tid; k < kPairClasses; k += kPairThreads) start[k] = run[k] = 0;
+    __syncthreads();
+    for (int b = tid; b < g.nb; b += kPairThreads)
+        if (orphan(b)) atomicAdd(&start[length_class(len(b))], 1);
+    __syncthreads();
+    int64_t norph = 0;
+    if (tid == 0) {
+        int acc = 0;
+        for (int k = kPairClasses - 1; k >= 0; --k) {
+            const int c = start[k];
+            start[k] = acc;
+            acc += c;
+        }
+        total_sh = acc;
+    }
+    __syncthreads();
+    norph = total_sh;
+    // stable scatter: position = class start + earlier orphans of the class
+    for (int b0 = 0; b0 < g.nb; b0 += kPairThreads) {
+        for (int i = tid; i < kPairClasses * (kPairThreads / 32); i += kPairThreads)
+            (&member[0][0])[i] = 0u;
+        __syncthreads();
+        const int b = b0 + tid;
+        const bool orph = b < g.nb && orphan(b);
+        const int k = orph ? length_class(len(b)) : 0;
+        if (orph) atomicOr(&member[k][tid >> 5], 1u << (tid & 31));
+        __syncthreads();
+        if (orph) {
+            int rank = __popc(member[k][tid >> 5] & ((1u << (tid & 31)) - 1u));
+            for (int w = 0; w < (tid >> 5); ++w) rank += __popc(member[k][w]);
+            const int64_t pos = start[k] + run[k] + rank;
+            int *slot = reinterpret_cast<int *>(out + kept + pos / 2) + (pos & 1);
+            *slot = b;
+        }
+        __syncthreads();
+        for (int kk = tid; kk < kPairClasses; kk += kPairThreads) {
+            int c = 0;
+            for (int w = 0; w < kPairThreads / 32; ++w) c += __popc(member[kk][w]);
+            run[kk] += c;
+        }
+        __syncthreads();
+    }
+    // an odd orphan count leaves the last item single; unused slots after it
+    const int64_t used = kept + (norph + 1) / 2;
+    if (tid == 0 && (norph & 1)) reinterpret_cast<int *>(out + kept + norph / 2)[1] = -1;
+    for (int64_t i = used + tid; i < pph; i += kPairThreads) out[i] = make_int2(-1, -1);
+}
+
+// Union of the two key lists of a work item (a pair of query blocks from the
+// pair table), the walk the attention kernel takes: entries
 // (block << 2) | sides, bit 0 set when the upper block keeps the block, bit 1
 // when the lower one does.  One wave64 per item.  For strictly ascending lists
 // inside [0, nb) (as the radius mask writes them) the union is ascending and
@@ -115,15 +262,19 @@ __device__ bool list_ascending(const int32_t *l, int n, int nb, int lane) {
 __global__ __launch_bounds__(64 * kUnionWaves) void union_kernel(
     const int32_t *__restrict__ idx, const int32_t *__restrict__ cnt,
     const float *__restrict__ lw, int64_t maxcnt, Grid g, int64_t items, int pairs_per_head,
-    int64_t ustride, int32_t *__restrict__ ulist, int32_t *__restrict__ ulen,
-    float2 *__restrict__ ubias) {
+    const int2 *__restrict__ pairs, int64_t ustride, int32_t *__restrict__ ulist,
+    int32_t *__restrict__ ulen, float2 *__restrict__ ubias) {
     constexpr float kLog2e = 1.4426950408889634f;
     const int64_t item = (int64_t)blockIdx.x * kUnionWaves + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (item >= items) return;
     const int64_t h = item / pairs_per_head;
-    int qa, qb;
-    pair_blocks((int)(item % pairs_per_head), g, qa, qb);
+    const int2 pr = pairs[item];
+    const int qa = pr.x, qb = pr.y;
+    if (qa < 0) {  // an unused item slot: an empty walk
+        if (lane == 0) ulen[item] = 0;
+        return;
+    }
     auto len = [&](int b) -> int {
         if (b < 0) return 0;
         const int64_t m = cnt[h * g.nb + b];
@@ -215,38 +366,10 @@ __global__ __launch_bounds__(64 * kUnionWaves) void union_kernel(
 // below each share; then a histogram of its range's lengths in LDS, a
 // descending prefix scan and a scatter (the order among equal lengths is
 // arbitrary; results do not depend on it).
-constexpr int kOrderThreads = 1024;
+constexpr int kOrderThreads = kScanThreads;
 constexpr int kOrderMaxBin = 8191;
 constexpr int kXcds = 8;
 constexpr int kItemCost = 4;  // prologue and epilogue of an item, in walk steps
-
-// Exclusive prefix sum of one value per thread over the block (1024 threads):
-// shuffles within each wave, then the 16 wave totals.  Every thread gets its
-// exclusive prefix; *total receives the block total.
-__device__ int64_t block_exclusive_scan(int64_t v, int64_t *wave_sums, int64_t *total) {
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    int64_t x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int64_t y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    if (lane == 63) wave_sums[wid] = x;
-    __syncthreads();
-    if (tid == 0) {
-        int64_t run = 0;
-        for (int w = 0; w < kOrderThreads / 64; ++w) {
-            const int64_t t = wave_sums[w];
-            wave_sums[w] = run;
-            run += t;
-        }
-        *total = run;
-    }
-    __syncthreads();
-    const int64_t r = wave_sums[wid] + x - v;
-    __syncthreads();  // wave_sums may be reused by the next scan
-    return r;
-}
 
 __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *__restrict__ ulen,
                                                               int64_t items, int64_t cap,
@@ -372,13 +495,20 @@ __global__ __launch_bounds__(256) void sip_kernel(const float *__restrict__ logi
 int64_t union_stride(int64_t maxcnt) { return (2 * maxcnt + 63) / 64 * 64; }
 
 hipError_t launch_union(const int32_t *idx, const int32_t *cnt, const float *lw, int64_t maxcnt,
-                        const Grid &g, int heads, int32_t *ulist, int32_t *ulen, float2 *ubias,
-                        hipStream_t s) {
+                        const Grid &g, int heads, const int2 *pairs, int32_t *ulist, int32_t *ulen,
+                        float2 *ubias, hipStream_t s) {
     const int pph = pairs_per_head(g);
     const int64_t items = (int64_t)heads * pph;
     hipLaunchKernelGGL(union_kernel, dim3((unsigned)((items + kUnionWaves - 1) / kUnionWaves)),
-                       dim3(64 * kUnionWaves), 0, s, idx, cnt, lw, maxcnt, g, items, pph,
+                       dim3(64 * kUnionWaves), 0, s, idx, cnt, lw, maxcnt, g, items, pph, pairs,
                        union_stride(maxcnt), ulist, ulen, ubias);
+    return hipGetLastError();
+}
+
+hipError_t launch_pair(const int32_t *cnt, int64_t maxcnt, const Grid &g, int heads, int2 *pairs,
+                       hipStream_t s) {
+    hipLaunchKernelGGL(pair_kernel, dim3((unsigned)heads), dim3(kPairThreads), 0, s, cnt, maxcnt,
+                       g, pairs_per_head(g), pairs);
     return hipGetLastError();
 }
 

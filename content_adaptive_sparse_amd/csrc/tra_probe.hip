@@ -103,12 +103,17 @@ __global__ __launch_bounds__(256) void pack_pool_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) sq[e] = sk[e] = 0.f;
 
-    // the head's V exponent, from the partial maxima of vmax_kernel
+    // the head's V exponent, from the partial maxima of vmax_kernel (one per
+    // thread, kVmaxParts <= 256, then a workgroup max)
+    __shared__ uint32_t vred[PACKV ? 4 : 1];
     int vsc = 0;
     if (PACKV) {
-        uint32_t m = 0;
-        for (int i = 0; i < vparts; ++i) m = max(m, vpart[(size_t)h * vparts + i]);
-        vsc = v_scale_exponent(m);
+        uint32_t m = tid < vparts ? vpart[(size_t)h * vparts + tid] : 0u;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+        if ((tid & 63) == 0) vred[tid >> 6] = m;
+        __syncthreads();
+        vsc = v_scale_exponent(max(max(vred[0], vred[1]), max(vred[2], vred[3])));
         if (b == 0 && tid == 0) vexp[h] = vsc;
     }
 
@@ -197,12 +202,14 @@ __global__ __launch_bounds__(256) void pack_pool_kernel(
     }
 }
 
-// Pooled-logit entropy and radius.  One workgroup per (head, 32 query
-// blocks); the key blocks stream through LDS in chunks of 64.  Thread
-// (tq = tid / 16, tk = tid % 16) handles queries 2 tq, 2 tq + 1 and keys
-// tk + 16 j of each chunk, keeping an online (max, sum, weighted-log) state
-// per query that is merged over the 16 tk lanes at the end.
-constexpr int kEntQ = 32;
+// Pooled-logit entropy and radius.  One workgroup per (head, kEntQ query
+// blocks: 16, so that even the smallest layer fills the chip); the key blocks
+// stream through LDS in chunks of 64.  Thread (tq = tid / 16, tk = tid % 16)
+// handles queries kEntQPT tq + i and keys tk + 16 j of each chunk, keeping an
+// online (max, sum, weighted-log) state per query that is merged over the 16
+// tk lanes at the end.
+constexpr int kEntQ = 16;
+constexpr int kEntQPT = kEntQ / 16;  // queries per thread
 constexpr int kEntK = 64;
 
 struct EntState {
@@ -242,9 +249,9 @@ __global__ __launch_bounds__(256) void entropy_kernel(
         *reinterpret_cast<float4 *>(&Qs[r][4 * c4]) = val;
     }
 
-    EntState st[2];
+    EntState st[kEntQPT];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) st[i] = EntState{-1e30f, 0.f, 0.f};
+    for (int i = 0; i < kEntQPT; ++i) st[i] = EntState{-1e30f, 0.f, 0.f};
 
     // Key chunks are double-buffered through registers: the next chunk's loads
     // are in flight while the current one is computed from LDS.
@@ -270,32 +277,34 @@ __global__ __launch_bounds__(256) void entropy_kernel(
         }
         __syncthreads();
         if (c0 + kEntK < g.nb) load_chunk(c0 + kEntK);
-        float s[2][4];
+        float s[kEntQPT][4];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < kEntQPT; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) s[i][j] = 0.f;
 #pragma unroll 2
         for (int dd = 0; dd < D; dd += 4) {
-            const float4 a0 = *reinterpret_cast<const float4 *>(&Qs[2 * tq][dd]);
-            const float4 a1 = *reinterpret_cast<const float4 *>(&Qs[2 * tq + 1][dd]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float4 kk = *reinterpret_cast<const float4 *>(&Ks[tk + 16 * j][dd]);
-                s[0][j] += a0.x * kk.x + a0.y * kk.y + a0.z * kk.z + a0.w * kk.w;
-                s[1][j] += a1.x * kk.x + a1.y * kk.y + a1.z * kk.z + a1.w * kk.w;
+            for (int i = 0; i < kEntQPT; ++i) {
+                const float4 a = *reinterpret_cast<const float4 *>(&Qs[kEntQPT * tq + i][dd]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float4 kk = *reinterpret_cast<const float4 *>(&Ks[tk + 16 * j][dd]);
+                    s[i][j] += a.x * kk.x + a.y * kk.y + a.z * kk.z + a.w * kk.w;
+                }
             }
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < kEntQPT; ++i) {
             float mx = st[i].m;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 s[i][j] *= scale;
                 if (c0 + tk + 16 * j < g.nb) mx = fmaxf(mx, s[i][j]);
                 // the pooled logit matrix [heads][nb][nb], when asked for
-                if (logits && c0 + tk + 16 * j < g.nb && q0 + 2 * tq + i < g.nb)
-                    logits[((size_t)h * g.nb + q0 + 2 * tq + i) * g.nb + c0 + tk + 16 * j] = s[i][j];
+                if (logits && c0 + tk + 16 * j < g.nb && q0 + kEntQPT * tq + i < g.nb)
+                    logits[((size_t)h * g.nb + q0 + kEntQPT * tq + i) * g.nb + c0 + tk + 16 * j] =
+                        s[i][j];
             }
             if (mx > st[i].m) {
                 const float a = expf(st[i].m - mx);
@@ -316,7 +325,7 @@ __global__ __launch_bounds__(256) void entropy_kernel(
     }
 
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < kEntQPT; ++i) {
 #pragma unroll
         for (int off = 1; off < 16; off <<= 1) {
             EntState o;
@@ -325,7 +334,7 @@ __global__ __launch_bounds__(256) void entropy_kernel(
             o.A = __shfl_xor(st[i].A, off);
             st[i] = ent_merge(st[i], o);
         }
-        const int b = q0 + 2 * tq + i;
+        const int b = q0 + kEntQPT * tq + i;
         if (tk == 0 && b < g.nb) {
             const float Hb = logf(st[i].Z) - st[i].A / st[i].Z;
             const float hn = Hb * inv_ln_nb;
@@ -383,9 +392,9 @@ hipError_t launch_pack_k(int D, const uint16_t *k, const Grid &g, int heads, uin
 }
 
 int vmax_parts(const Grid &g, int D) {
-    // about 64 K elements per workgroup, at most kVmaxParts per head
+    // about 16 K elements per workgroup, at most kVmaxParts per head
     const int64_t n = (int64_t)g.T * g.H * g.W * D;
-    const int64_t p = (n + 65535) / 65536;
+    const int64_t p = (n + 16383) / 16384;
     return (int)(p < 1 ? 1 : (p > kVmaxParts ? kVmaxParts : p));
 }
 

@@ -278,9 +278,11 @@ int tra_attn_weighted(const void *q, const void *k, const void *v, int T, int H,
  * Plan / execute split with cross-step reuse (Token Radius Attention ...,
  * "The TRA Pipeline: Cross-Step Reuse": the sparsity decided in a warm-up step
  * is reused by the later denoising steps).  tra_plan turns key-block lists into
- * the attention walk (per pair of vertically adjacent query blocks: the union of
- * their two lists; then the work order) and stores it in a caller-owned device
- * buffer of tra_plan_bytes bytes; tra_attn_plan then runs the attention of new
+ * the attention walk -- the pairing of query blocks into work items (vertical
+ * neighbours whose list lengths are within a factor of two; the other blocks
+ * re-paired by length class, so that long lists share a walk with long ones),
+ * the union of each item's two lists, then the work order -- and stores it in a
+ * caller-owned device buffer of tra_plan_bytes bytes; tra_attn_plan then runs the attention of new
  * q, k, v along that walk, so later steps skip the list processing.
  * tra_attn(idx, cnt) is tra_plan followed by tra_attn_plan on library scratch.
  *   plan      device buffer, tra_plan_bytes(T,H,W,heads,block,maxcnt) bytes,
@@ -342,7 +344,8 @@ enum tra_kernel_kind {
     TRA_KERNEL_TOKEN_MASK = 8,    /* token-disk voting lists */
     TRA_KERNEL_SIP = 9,           /* sampled lists with inverse-inclusion weights */
     TRA_KERNEL_VMAX = 10,         /* largest |v| per head (the fp16 scale of V) */
-    TRA_KERNEL_KINDS = 11
+    TRA_KERNEL_PAIR = 11,         /* pair table: which two query blocks share a work item */
+    TRA_KERNEL_KINDS = 12
 };
 int tra_profile_begin(void);
 int tra_profile_end(double *ms, int *launches, int n);

@@ -164,7 +164,8 @@ def test_plan_bytes_closed_form(lib):
         slots = -(-items // 8) * 8
         order = 8 * 2 * -(-items // 8)  # eight ranges of at most twice the mean count
         stride = -(-(2 * maxcnt) // 64) * 64
-        want = up(4 * order) + up(4 * slots) + up(4 * slots * stride)
+        # work order, walk lengths, walks, pair table (two int32 per item slot)
+        want = up(4 * order) + up(4 * slots) + up(4 * slots * stride) + up(8 * slots)
         assert tra.tra_plan_bytes(T, H, W, heads, 64, maxcnt) == want
 
 

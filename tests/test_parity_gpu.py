@@ -279,8 +279,8 @@ def test_list_edge_cases():
 
 
 def test_list_walk_cases():
-    # Each attention work item walks the union of a vertically adjacent pair
-    # of query blocks' lists: ascending lists merge (overlaps computed once,
+    # Each attention work item walks the union of its two query blocks' lists
+    # (the plan's pair table): ascending lists merge (overlaps computed once,
     # unions longer than 64 entries), other lists (descending, duplicates)
     # are walked as they stand.  Every block must still see exactly its own
     # list, a duplicate counting twice.
@@ -422,6 +422,95 @@ def test_work_order_ranges(skewed):
         assert_close(out.reshape(-1, 128)[rows], ref, "attention along the capped order")
 
 
+def pair_table_model(cnt, T, H, W):
+    """The pair table the plan must hold, from the list lengths alone: per head,
+    the vertical pairs (tile rows 2p, 2p + 1) whose lengths are within a factor
+    of two, in raster order; then the other blocks sorted by length class (four
+    per octave of length + 1), longest class first, raster order inside a class,
+    paired in that order; then (-1, -1) up to the head's slot count."""
+    heads, nb = cnt.shape
+    nby, nbx = -(-H // 8), -(-W // 8)
+    npy = (nby + 1) // 2
+    pph = T * npy * nbx
+
+    def cls(c):
+        x = max(int(c), 0) + 1
+        e = x.bit_length() - 1
+        f = (x >> (e - 2)) & 3 if e >= 2 else (x << (2 - e)) & 3
+        return 4 * e + f
+
+    def good(a, b):
+        return 2 * min(a, b) >= max(a, b)
+
+    table = np.full((heads, pph, 2), -1, dtype=np.int64)
+    for h in range(heads):
+        c = cnt[h]
+        items, orph = [], []
+        for p in range(pph):
+            t, pr, bx = p // (npy * nbx), (p // nbx) % npy, p % nbx
+            qa = (t * nby + 2 * pr) * nbx + bx
+            qb = qa + nbx if 2 * pr + 1 < nby else -1
+            if qb < 0 or good(c[qa], c[qb]):
+                items.append((qa, qb))
+        for b in range(nb):
+            by = (b // nbx) % nby
+            o = b - nbx if by & 1 else (b + nbx if by + 1 < nby else -1)
+            if o >= 0 and not good(c[b], c[o]):
+                orph.append(b)
+        orph.sort(key=lambda b: -cls(c[b]))  # stable: raster order inside a class
+        items += [(orph[i], orph[i + 1] if i + 1 < len(orph) else -1) for i in range(0, len(orph), 2)]
+        table[h, :len(items)] = items
+    return table
+
+
+def plan_pair_table(plan, T, H, W, heads, maxcnt):
+    nby, nbx = -(-H // 8), -(-W // 8)
+    items = heads * T * ((nby + 1) // 2) * nbx
+    rows = -(-items // 8) * 8
+    cap = 2 * -(-items // 8)
+    stride = -(-(2 * maxcnt) // 64) * 64
+    up = lambda x: -(-x // 256) * 256
+    o = up(4 * 8 * cap) + up(4 * rows) + up(4 * rows * stride)
+    raw = plan.cpu().numpy()[o: o + 8 * items].view(np.int32)
+    return raw.reshape(heads, -1, 2).astype(np.int64)
+
+
+@pytest.mark.parametrize("kind", ["routing", "radii"])
+def test_pair_table(kind):
+    # The plan's pair table equals the rule applied to the list lengths, every
+    # query block appears in exactly one item, and attention along it is exact.
+    T, H, W, heads, d = 5, 40, 56, 2, 128
+    shp = (heads, T, H, W, d)
+    print(f"[case] pair table {kind} {shp}", flush=True)
+    nb = tra.tra_grid(T, H, W)[2]
+    rng = np.random.default_rng(29)
+    if kind == "routing":
+        radii = np.where(rng.random((heads, nb)) < 0.2, INF, 1).astype(np.int32)
+        r_max = INF
+    else:
+        radii = rng.integers(0, 5, size=(heads, nb)).astype(np.int32)
+        r_max = 4
+    idx, cnt, maxcnt = gpu_mask(radii, shp, r_max)
+    plan = torch.zeros(tra.tra_plan_bytes(T, H, W, heads, 64, maxcnt), dtype=torch.uint8,
+                       device="cuda")
+    tra.tra_plan(idx, cnt, maxcnt, T, H, W, heads, 64, plan)
+    torch.cuda.synchronize()
+    got = plan_pair_table(plan, T, H, W, heads, maxcnt)
+    want = pair_table_model(cnt.cpu().numpy(), T, H, W)
+    assert np.array_equal(got, want), "pair table differs from the rule"
+    for h in range(heads):
+        blocks = got[h].ravel()
+        assert np.array_equal(np.sort(blocks[blocks >= 0]), np.arange(nb)), "not a partition"
+    repaired = int(np.sum(got[:, :, 1] >= 0) - 0)
+    print(f"[pairs] {kind}: {repaired} two-block items of {got.shape[1] * heads} slots", flush=True)
+    q, k, v = ti.make_inputs(T, H, W, heads, d, seed=8, family=35)
+    out = torch.full(shp, float("nan"), dtype=torch.float32, device="cuda")
+    tra.tra_attn_plan(dev16(q), dev16(k), dev16(v), T, H, W, heads, d, 64, plan, maxcnt, out)
+    torch.cuda.synchronize()
+    ref = oracle.attention(q, k, v, radii)
+    assert_close(out.cpu().numpy(), ref, f"attention along the pair table ({kind})")
+
+
 def test_binary_routing():
     # HetA-style routing: every block either local (radius 1) or dense (radius
     # infinite) from a supplied difficulty map; the mask with r_max infinite
@@ -463,6 +552,38 @@ def test_negative_logit_rows_on_edge_tiles(d, mixed):
         dense = gpu_attn(qd, kd, vd, shp).cpu().numpy()
         assert_close(dense, oracle.attention(q, k, v, oracle.dense_radii(heads, nb)),
                      f"negative logits dense {shp}")
+
+
+@pytest.mark.parametrize("step", [3.0, 9.0, 17.0])
+def test_logits_growing_along_the_walk(step):
+    # Keys whose logits grow by `step` (base 2) with every frame: along the
+    # ascending walk each key tile sits above everything before it, so the
+    # running reference must move when a probability would leave fp16 (17 per
+    # tile: at every tile; 9: every other; 3: every sixth) and stay put in
+    # between, with O and l rescaled consistently.  Dense mode and lists.
+    T, H, W, heads, d = 12, 16, 16, 2, 128
+    shp = (heads, T, H, W, d)
+    print(f"[case] growing logits {shp} step={step}", flush=True)
+    rng = np.random.default_rng(41)
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    t = np.arange(T)[None, :, None, None, None]
+    # q . k = a t' b with |q| = b, |k| = a t' along u: step log2 units per frame
+    b = 4.0
+    a = step / (np.log2(np.e) / np.sqrt(d)) / b
+    q = b * u + 0.05 * rng.standard_normal((heads, T, H, W, d))
+    k = (a * t) * u + 0.05 * rng.standard_normal((heads, T, H, W, d))
+    v = rng.standard_normal((heads, T, H, W, d))
+    q, k, v = (ti.bf16_from_f32(x.astype(np.float32)) for x in (q, k, v))
+    qd, kd, vd = dev16(q), dev16(k), dev16(v)
+    nb = tra.tra_grid(T, H, W)[2]
+    dense = gpu_attn(qd, kd, vd, shp).cpu().numpy()
+    assert_close(dense, oracle.attention(q, k, v, oracle.dense_radii(heads, nb)),
+                 f"growing logits, dense, step {step}")
+    radii = rng.integers(1, 6, size=(heads, nb)).astype(np.int32)
+    idx, cnt, maxcnt = gpu_mask(radii, shp, 5)
+    out = gpu_attn(qd, kd, vd, shp, idx, cnt, maxcnt).cpu().numpy()
+    assert_close(out, oracle.attention(q, k, v, radii), f"growing logits, lists, step {step}")
 
 
 def test_mask_clamps_radius_to_r_max():

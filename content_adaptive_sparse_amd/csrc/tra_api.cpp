@@ -417,6 +417,27 @@ static hipError_t plan_walk(const int32_t *idx, const int32_t *cnt, const float 
     return e;
 }
 
+// The walk plan of the radius mask's lists, taken straight from the radii
+// (pair table, walks, order; the same plan plan_walk makes of the lists).
+static hipError_t plan_walk_radius(const int32_t *radius, int r_max, int64_t maxcnt,
+                                   const tra::Grid &g, int heads, int2 *pairs, int32_t *ulist,
+                                   int32_t *ulen, int32_t *order, hipStream_t stream) {
+    hipError_t e;
+    {
+        ProfScope p(TRA_KERNEL_PAIR, stream);
+        e = tra::launch_pair_radius(radius, r_max, maxcnt, g, heads, pairs, stream);
+    }
+    if (e == hipSuccess) {
+        ProfScope p(TRA_KERNEL_UNION, stream);
+        e = tra::launch_radius_walk(radius, r_max, maxcnt, g, heads, pairs, ulist, ulen, stream);
+    }
+    if (e == hipSuccess) {
+        ProfScope p(TRA_KERNEL_ORDER, stream);
+        e = tra::launch_order(ulen, g, heads, maxcnt, order, stream);
+    }
+    return e;
+}
+
 // Layout of a walk plan in one buffer: work order, walk lengths, walks, the
 // pair table and (for weighted lists) the walks' per-side log2 weights; each
 // part 256-byte aligned.
@@ -784,41 +805,28 @@ int tra_attention(const void *q, const void *k, const void *v, int T, int H, int
     const size_t o_qp = ws.reserve(rows * head_dim * sizeof(float));
     const size_t o_kp = ws.reserve(rows * head_dim * sizeof(float));
     const size_t o_r = ws.reserve(rows * sizeof(int32_t));
-    const size_t o_cnt = ws.reserve(rows * sizeof(int32_t));
-    const size_t o_idx = ws.reserve(rows * (size_t)maxcnt * sizeof(int32_t));
     const size_t o_plan = ws.reserve(L.bytes);
     if ((rc = ws.allocate()) != TRA_OK) return rc;
     const Packed pk = packed_at(ws, po);
     float *qp = ws.at<float>(o_qp), *kp = ws.at<float>(o_kp);
-    int32_t *radius = ws.at<int32_t>(o_r), *cnt = ws.at<int32_t>(o_cnt), *idx = ws.at<int32_t>(o_idx);
+    int32_t *radius = ws.at<int32_t>(o_r);
     char *plan = ws.at<char>(o_plan);
 
-    // The packing of k and v (HBM-bound) runs on the side stream while this
-    // stream pools q and k and builds radii, lists and the walk plan (mostly
-    // latency-bound kernels); the attention waits for both.
-    hipError_t e;
-    {
-        Fork fork(stream);
-        if (!fork.ok()) return TRA_ERR_HIP;
-        e = pack_kv(head_dim, nullptr, k, v, g, heads, nullptr, nullptr, pk, fork.side());
-        if (e == hipSuccess) {
-            ProfScope p(TRA_KERNEL_PACK_POOL, stream);
-            e = tra::launch_pack_pool(head_dim, true, false, (const uint16_t *)q, (const uint16_t *)k,
-                                      nullptr, g, heads, qp, kp, nullptr, nullptr, nullptr,
-                                      nullptr, stream);
-        }
-        if (e == hipSuccess) {
-            ProfScope p(TRA_KERNEL_ENTROPY, stream);
-            e = tra::launch_entropy(head_dim, qp, kp, g, heads, r_min, r_max, radius, nullptr, stream);
-        }
-        if (e == hipSuccess) {
-            ProfScope p(TRA_KERNEL_MASK, stream);
-            e = tra::launch_mask(radius, g, heads, r_max, maxcnt, idx, cnt, stream);
-        }
-        if (e == hipSuccess) e = plan_walk_into(idx, cnt, nullptr, maxcnt, g, heads, plan, L, stream);
-        const hipError_t ej = fork.join();
-        if (e == hipSuccess) e = ej;
+    // One stream: V's scale, then one pass over q, k, v that pools q and k and
+    // packs k and v, the entropy, and the walk plan straight from the radii
+    // (the radius mask's lists are never written out).  Packing on a second
+    // stream beside the latency-bound entropy and plan kernels measured no
+    // faster: the HBM-bound packing slows the kernels beside it as much as it
+    // overlaps them.
+    hipError_t e = pack_kv(head_dim, q, k, v, g, heads, qp, kp, pk, stream);
+    if (e == hipSuccess) {
+        ProfScope p(TRA_KERNEL_ENTROPY, stream);
+        e = tra::launch_entropy(head_dim, qp, kp, g, heads, r_min, r_max, radius, nullptr, stream);
     }
+    if (e == hipSuccess)
+        e = plan_walk_radius(radius, r_max, maxcnt, g, heads, (int2 *)(plan + L.o_pairs),
+                             (int32_t *)(plan + L.o_ulist), (int32_t *)(plan + L.o_ulen),
+                             (int32_t *)(plan + L.o_order), stream);
     if (e == hipSuccess) e = attn_launch(q, pk, g, heads, head_dim, plan, L, out, stream);
     return hip_status(e);
 }

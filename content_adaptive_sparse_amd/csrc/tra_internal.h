@@ -103,6 +103,17 @@ hipError_t launch_union(const int32_t *idx, const int32_t *cnt, const float *lw,
 hipError_t launch_pair(const int32_t *cnt, int64_t maxcnt, const Grid &g, int heads, int2 *pairs,
                        hipStream_t s);
 
+// The same two steps for the radius mask's lists taken straight from the radii
+// (no lists): the pair table from the lists' lengths (box sizes, at most
+// maxcnt), then each item's walk, the union of its two blocks' key boxes --
+// identical to launch_pair + launch_union of tra_mask's lists when maxcnt
+// holds the largest box (tra_maxcnt), so that no list is cut short.
+hipError_t launch_pair_radius(const int32_t *radius, int r_max, int64_t maxcnt, const Grid &g,
+                              int heads, int2 *pairs, hipStream_t s);
+hipError_t launch_radius_walk(const int32_t *radius, int r_max, int64_t maxcnt, const Grid &g,
+                              int heads, const int2 *pairs, int32_t *ulist, int32_t *ulen,
+                              hipStream_t s);
+
 // Sampled lists with log-weights from the pooled logit matrix and uniforms
 // u[heads][nb][nb] (row stride nb for idx and lw).
 hipError_t launch_sip(const float *logits, const float *u, const Grid &g, int heads, float m,

@@ -123,18 +123,48 @@ __device__ __forceinline__ bool lengths_pair_well(int a, int b) {
     return 2 * (int64_t)min(a, b) >= (int64_t)max(a, b);
 }
 
+// The key blocks of query block b within Chebyshev radius r (clamped to
+// [0, r_max] as the radius mask clamps it) in block coordinates: a box of the
+// (frame, tile row, tile column) grid.
+struct KeyBox {
+    int t0, t1, y0, y1, x0, x1;  // inclusive bounds; t0 > t1 when empty
+    __device__ bool contains(int t, int y, int x) const {
+        return t >= t0 && t <= t1 && y >= y0 && y <= y1 && x >= x0 && x <= x1;
+    }
+    __device__ int64_t count() const {
+        return t0 > t1 ? 0 : (int64_t)(t1 - t0 + 1) * (y1 - y0 + 1) * (x1 - x0 + 1);
+    }
+};
+
+__device__ KeyBox key_box(int b, int32_t radius, int r_max, const Grid &g) {
+    const int64_t r = radius < 0 ? 0 : (radius > r_max ? r_max : radius);
+    const int plane = g.nby * g.nbx;
+    const int t = b / plane, y = (b / g.nbx) % g.nby, x = b % g.nbx;
+    KeyBox k;
+    k.t0 = (int)max((int64_t)0, t - r);
+    k.t1 = (int)min((int64_t)g.T - 1, t + r);
+    k.y0 = (int)max((int64_t)0, y - r);
+    k.y1 = (int)min((int64_t)g.nby - 1, y + r);
+    k.x0 = (int)max((int64_t)0, x - r);
+    k.x1 = (int)min((int64_t)g.nbx - 1, x + r);
+    return k;
+}
+
+// cnt: list lengths; or, with radius non-null, the lengths of the radius
+// mask's lists computed from the radii (its boxes, at most maxcnt).
 __global__ __launch_bounds__(kPairThreads) void pair_kernel(const int32_t *__restrict__ cnt,
-                                                           int64_t maxcnt, Grid g, int pph,
-                                                           int2 *__restrict__ pairs) {
+                                                           const int32_t *__restrict__ radius,
+                                                           int r_max, int64_t maxcnt, Grid g,
+                                                           int pph, int2 *__restrict__ pairs) {
     __shared__ int64_t wave_sums[kPairThreads / 64];
     __shared__ int64_t total_sh;
     __shared__ int start[kPairClasses], run[kPairClasses];
     __shared__ uint32_t member[kPairClasses][kPairThreads / 32];
     const int h = blockIdx.x, tid = threadIdx.x;
-    const int32_t *ch = cnt + (int64_t)h * g.nb;
+    const int32_t *ch = radius ? radius + (int64_t)h * g.nb : cnt + (int64_t)h * g.nb;
     int2 *out = pairs + (int64_t)h * pph;
     auto len = [&](int b) -> int {
-        const int64_t m = ch[b];
+        const int64_t m = radius ? key_box(b, ch[b], r_max, g).count() : ch[b];
         return (int)(m < 0 ? 0 : (m > maxcnt ? maxcnt : m));
     };
     // the vertical partner of block b (-1 when its tile row has none)
@@ -352,6 +382,49 @@ __global__ __launch_bounds__(64 * kUnionWaves) void union_kernel(
     if (lane == 0) ulen[item] = n;
 }
 
+// The walk of a work item straight from the two blocks' radii: the union of
+// their key boxes in ascending block order, each entry (block << 2) | sides --
+// exactly what union_kernel makes of the radius mask's lists, without the
+// lists.  One wave64 per item scans the frames either box touches, 64
+// candidate blocks at a time, and compacts with a ballot.
+__global__ __launch_bounds__(64 * kUnionWaves) void radius_walk_kernel(
+    const int32_t *__restrict__ radius, int r_max, Grid g, int64_t items, int pairs_per_head,
+    const int2 *__restrict__ pairs, int64_t ustride, int32_t *__restrict__ ulist,
+    int32_t *__restrict__ ulen) {
+    const int64_t item = (int64_t)blockIdx.x * kUnionWaves + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (item >= items) return;
+    const int64_t h = item / pairs_per_head;
+    const int2 pr = pairs[item];
+    if (pr.x < 0) {  // an unused item slot: an empty walk
+        if (lane == 0) ulen[item] = 0;
+        return;
+    }
+    const int32_t *rh = radius + h * g.nb;
+    const KeyBox A = key_box(pr.x, rh[pr.x], r_max, g);
+    KeyBox B = A;
+    if (pr.y >= 0) B = key_box(pr.y, rh[pr.y], r_max, g);
+    const int plane = g.nby * g.nbx;
+    const int first = min(A.t0, B.t0) * plane, end = (max(A.t1, B.t1) + 1) * plane;
+    const bool single = pr.y < 0;
+    int32_t *out = ulist + item * ustride;
+    int64_t n = 0;
+    for (int c0 = first; c0 < end; c0 += 64) {
+        const int kb = c0 + lane;
+        int sides = 0;
+        if (kb < end) {
+            const int t = kb / plane, rem = kb - t * plane;
+            const int y = rem / g.nbx, x = rem - y * g.nbx;
+            sides = (A.contains(t, y, x) ? 1 : 0) | (!single && B.contains(t, y, x) ? 2 : 0);
+        }
+        const uint64_t bal = __ballot(sides != 0);
+        const int64_t o = n + lanes_before(bal);
+        if (sides && o < ustride) out[o] = (kb << 2) | sides;
+        n += __popcll(bal);
+    }
+    if (lane == 0) ulen[item] = (int32_t)(n < ustride ? n : ustride);
+}
+
 // Work order for the attention kernel.  Workgroup ids are dealt to the eight
 // XCDs round robin (id % 8), each XCD with its own L2, so XCD x is given a
 // contiguous raster range of the items (neighbouring query blocks of the same
@@ -507,8 +580,26 @@ hipError_t launch_union(const int32_t *idx, const int32_t *cnt, const float *lw,
 
 hipError_t launch_pair(const int32_t *cnt, int64_t maxcnt, const Grid &g, int heads, int2 *pairs,
                        hipStream_t s) {
-    hipLaunchKernelGGL(pair_kernel, dim3((unsigned)heads), dim3(kPairThreads), 0, s, cnt, maxcnt,
-                       g, pairs_per_head(g), pairs);
+    hipLaunchKernelGGL(pair_kernel, dim3((unsigned)heads), dim3(kPairThreads), 0, s, cnt, nullptr,
+                       0, maxcnt, g, pairs_per_head(g), pairs);
+    return hipGetLastError();
+}
+
+hipError_t launch_pair_radius(const int32_t *radius, int r_max, int64_t maxcnt, const Grid &g,
+                              int heads, int2 *pairs, hipStream_t s) {
+    hipLaunchKernelGGL(pair_kernel, dim3((unsigned)heads), dim3(kPairThreads), 0, s, nullptr,
+                       radius, r_max, maxcnt, g, pairs_per_head(g), pairs);
+    return hipGetLastError();
+}
+
+hipError_t launch_radius_walk(const int32_t *radius, int r_max, int64_t maxcnt, const Grid &g,
+                              int heads, const int2 *pairs, int32_t *ulist, int32_t *ulen,
+                              hipStream_t s) {
+    const int pph = pairs_per_head(g);
+    const int64_t items = (int64_t)heads * pph;
+    hipLaunchKernelGGL(radius_walk_kernel, dim3((unsigned)((items + kUnionWaves - 1) / kUnionWaves)),
+                       dim3(64 * kUnionWaves), 0, s, radius, r_max, g, items, pph, pairs,
+                       union_stride(maxcnt), ulist, ulen);
     return hipGetLastError();
 }
 

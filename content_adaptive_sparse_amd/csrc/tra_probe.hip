@@ -202,15 +202,19 @@ __global__ __launch_bounds__(256) void pack_pool_kernel(
     }
 }
 
-// Pooled-logit entropy and radius.  One workgroup per (head, kEntQ query
-// blocks: 16, so that even the smallest layer fills the chip); the key blocks
-// stream through LDS in chunks of 64.  Thread (tq = tid / 16, tk = tid % 16)
-// handles queries kEntQPT tq + i and keys tk + 16 j of each chunk, keeping an
-// online (max, sum, weighted-log) state per query that is merged over the 16
-// tk lanes at the end.
-constexpr int kEntQ = 16;
-constexpr int kEntQPT = kEntQ / 16;  // queries per thread
-constexpr int kEntK = 64;
+// Pooled-logit entropy and radius.  The logits s = scale qbar . kbar of 16
+// query blocks against 16 key blocks are one fp32 matrix-core product chain
+// (v_mfma_f32_16x16x4_f32, D / 4 steps): the key tile is the A operand and
+// the query tile the B operand, so that lane l ends with the logits of query
+// block q0 + l % 16 against key blocks 4 (l / 16) + r, r = 0..3, of the tile.
+// Step s takes dims kq D / 4 + s from lane group kq = l / 16 (the dot product
+// does not depend on the order of the dims), so every lane reads one
+// contiguous quarter row of its query and of its key.  The workgroup's waves
+// take the key tiles round robin, each keeping an online (max, sum,
+// weighted-log) state per lane; the four lane groups and the waves are merged
+// at the end.
+constexpr int kEntWaves = 8;   // waves per workgroup
+constexpr int kEntQB = 16;     // query blocks per workgroup
 
 struct EntState {
     float m, Z, A;  // running max, sum e^(s-m), sum e^(s-m) (s-m)
@@ -227,116 +231,115 @@ __device__ __forceinline__ EntState ent_merge(EntState a, EntState b) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void entropy_kernel(
+__global__ __launch_bounds__(64 * kEntWaves) void entropy_kernel(
     const float *__restrict__ qp, const float *__restrict__ kp, Grid g, int r_min,
     int64_t R, int r_max, float inv_ln_nb, float scale, int32_t *__restrict__ radius,
     float *__restrict__ h_norm, float *__restrict__ logits) {
-    constexpr int P = D + 4;
-    __shared__ __attribute__((aligned(16))) float Qs[kEntQ][P];
-    __shared__ __attribute__((aligned(16))) float Ks[kEntK][P];
+    constexpr int QD = D / 4;  // dims per lane group
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    __shared__ float red[3][kEntWaves][kEntQB];
 
     const int h = blockIdx.y;
-    const int q0 = blockIdx.x * kEntQ;
-    const int tid = threadIdx.x;
-    const int tq = tid >> 4, tk = tid & 15;
+    const int q0 = blockIdx.x * kEntQB;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int col = lane & 15, kq = lane >> 4;
     const float *qh = qp + (size_t)h * g.nb * D;
     const float *kh = kp + (size_t)h * g.nb * D;
 
-    for (int e = tid; e < kEntQ * D / 4; e += 256) {
-        const int r = e / (D / 4), c4 = e % (D / 4);
-        float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (q0 + r < g.nb) val = reinterpret_cast<const float4 *>(qh + (size_t)(q0 + r) * D)[c4];
-        *reinterpret_cast<float4 *>(&Qs[r][4 * c4]) = val;
+    // B operand: query block q0 + col, dims kq QD .. kq QD + QD (zeros past nb)
+    float qv[QD];
+    {
+        const int qi = q0 + col;
+        const float4 *src =
+            reinterpret_cast<const float4 *>(qh + (size_t)min(qi, g.nb - 1) * D + kq * QD);
+#pragma unroll
+        for (int c = 0; c < QD / 4; ++c) {
+            float4 t = src[c];
+            if (qi >= g.nb) t = make_float4(0.f, 0.f, 0.f, 0.f);
+            qv[4 * c] = t.x;
+            qv[4 * c + 1] = t.y;
+            qv[4 * c + 2] = t.z;
+            qv[4 * c + 3] = t.w;
+        }
     }
 
-    EntState st[kEntQPT];
+    const int ntiles = (g.nb + 15) / 16;
+    EntState st{-1e30f, 0.f, 0.f};
+    // A operand: key block 16 t + col, dims kq QD .. (rows past nb read the
+    // last real row; their logits are left out below)
+    float kv[QD];
+    auto load_keys = [&](int t) {
+        const float4 *src = reinterpret_cast<const float4 *>(
+            kh + (size_t)min(16 * t + col, g.nb - 1) * D + kq * QD);
 #pragma unroll
-    for (int i = 0; i < kEntQPT; ++i) st[i] = EntState{-1e30f, 0.f, 0.f};
-
-    // Key chunks are double-buffered through registers: the next chunk's loads
-    // are in flight while the current one is computed from LDS.
-    constexpr int KCH = kEntK * D / 4 / 256;  // float4 per thread and chunk
-    static_assert(KCH * 256 * 4 == kEntK * D, "chunk split");
-    float4 stage[KCH];
-    auto load_chunk = [&](int c0) {
-#pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int e = tid + 256 * i;
-            const int r = e / (D / 4), c4 = e % (D / 4);
-            stage[i] = c0 + r < g.nb ? reinterpret_cast<const float4 *>(kh + (size_t)(c0 + r) * D)[c4]
-                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int c = 0; c < QD / 4; ++c) {
+            const float4 x = src[c];
+            kv[4 * c] = x.x;
+            kv[4 * c + 1] = x.y;
+            kv[4 * c + 2] = x.z;
+            kv[4 * c + 3] = x.w;
         }
     };
-    load_chunk(0);
-    for (int c0 = 0; c0 < g.nb; c0 += kEntK) {
-        __syncthreads();
+    if (wave < ntiles) load_keys(wave);
+    for (int t = wave; t < ntiles; t += kEntWaves) {
+        f32x4_t acc = {};
 #pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int e = tid + 256 * i;
-            *reinterpret_cast<float4 *>(&Ks[e / (D / 4)][4 * (e % (D / 4))]) = stage[i];
+        for (int s = 0; s < QD; ++s)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[s], qv[s], acc, 0, 0, 0);
+        // the next tile's loads under this tile's VALU work
+        if (t + kEntWaves < ntiles) load_keys(t + kEntWaves);
+        const int key0 = 16 * t + 4 * kq;
+        float sv[4];
+        float mx = st.m;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            sv[r] = acc[r] * scale;
+            if (key0 + r < g.nb) mx = fmaxf(mx, sv[r]);
         }
-        __syncthreads();
-        if (c0 + kEntK < g.nb) load_chunk(c0 + kEntK);
-        float s[kEntQPT][4];
+        if (logits && q0 + col < g.nb) {
+            float *row = logits + ((size_t)h * g.nb + q0 + col) * g.nb;
 #pragma unroll
-        for (int i = 0; i < kEntQPT; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) s[i][j] = 0.f;
-#pragma unroll 2
-        for (int dd = 0; dd < D; dd += 4) {
-#pragma unroll
-            for (int i = 0; i < kEntQPT; ++i) {
-                const float4 a = *reinterpret_cast<const float4 *>(&Qs[kEntQPT * tq + i][dd]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float4 kk = *reinterpret_cast<const float4 *>(&Ks[tk + 16 * j][dd]);
-                    s[i][j] += a.x * kk.x + a.y * kk.y + a.z * kk.z + a.w * kk.w;
-                }
-            }
+            for (int r = 0; r < 4; ++r)
+                if (key0 + r < g.nb) row[key0 + r] = sv[r];
+        }
+        if (mx > st.m) {
+            const float a = expf(st.m - mx);
+            st.A = a * (st.A + (st.m - mx) * st.Z);
+            st.Z *= a;
+            st.m = mx;
         }
 #pragma unroll
-        for (int i = 0; i < kEntQPT; ++i) {
-            float mx = st[i].m;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                s[i][j] *= scale;
-                if (c0 + tk + 16 * j < g.nb) mx = fmaxf(mx, s[i][j]);
-                // the pooled logit matrix [heads][nb][nb], when asked for
-                if (logits && c0 + tk + 16 * j < g.nb && q0 + kEntQPT * tq + i < g.nb)
-                    logits[((size_t)h * g.nb + q0 + kEntQPT * tq + i) * g.nb + c0 + tk + 16 * j] =
-                        s[i][j];
-            }
-            if (mx > st[i].m) {
-                const float a = expf(st[i].m - mx);
-                st[i].A = a * (st[i].A + (st[i].m - mx) * st[i].Z);
-                st[i].Z *= a;
-                st[i].m = mx;
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (c0 + tk + 16 * j < g.nb) {
-                    const float x = s[i][j] - st[i].m;
-                    const float e = expf(x);
-                    st[i].Z += e;
-                    st[i].A += e * x;
-                }
+        for (int r = 0; r < 4; ++r) {
+            if (key0 + r < g.nb) {
+                const float x = sv[r] - st.m;
+                const float e = expf(x);
+                st.Z += e;
+                st.A += e * x;
             }
         }
     }
-
+    // the four lane groups hold the same query block's other keys
 #pragma unroll
-    for (int i = 0; i < kEntQPT; ++i) {
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-            EntState o;
-            o.m = __shfl_xor(st[i].m, off);
-            o.Z = __shfl_xor(st[i].Z, off);
-            o.A = __shfl_xor(st[i].A, off);
-            st[i] = ent_merge(st[i], o);
-        }
-        const int b = q0 + kEntQPT * tq + i;
-        if (tk == 0 && b < g.nb) {
-            const float Hb = logf(st[i].Z) - st[i].A / st[i].Z;
+    for (int off = 16; off <= 32; off <<= 1) {
+        EntState o;
+        o.m = __shfl_xor(st.m, off);
+        o.Z = __shfl_xor(st.Z, off);
+        o.A = __shfl_xor(st.A, off);
+        st = ent_merge(st, o);
+    }
+    if (kq == 0) {
+        red[0][wave][col] = st.m;
+        red[1][wave][col] = st.Z;
+        red[2][wave][col] = st.A;
+    }
+    __syncthreads();
+    if (wave == 0 && kq == 0) {
+        EntState acc{red[0][0][col], red[1][0][col], red[2][0][col]};
+        for (int w = 1; w < kEntWaves; ++w)
+            acc = ent_merge(acc, EntState{red[0][w][col], red[1][w][col], red[2][w][col]});
+        const int b = q0 + col;
+        if (b < g.nb) {
+            const float Hb = logf(acc.Z) - acc.A / acc.Z;
             const float hn = Hb * inv_ln_nb;
             int64_t r = (int64_t)r_min + (int64_t)floor((double)hn * (double)R);
             r = r < r_min ? r_min : (r > r_max ? r_max : r);
@@ -424,7 +427,7 @@ hipError_t launch_pack_pool(int D, bool pool, bool pack, const uint16_t *q, cons
 hipError_t launch_entropy(int D, const float *qp, const float *kp, const Grid &g, int heads,
                           int r_min, int r_max, int32_t *radius, float *h_norm, hipStream_t s,
                           float *logits) {
-    const dim3 grid((g.nb + kEntQ - 1) / kEntQ, heads), block(256);
+    const dim3 grid((g.nb + kEntQB - 1) / kEntQB, heads), block(64 * kEntWaves);
     const int64_t R = (int64_t)r_max - (int64_t)r_min + 1;
     const float inv_ln_nb = g.nb > 1 ? (float)(1.0 / log((double)g.nb)) : 0.f;
     const float scale = (float)(1.0 / sqrt((double)D));

@@ -95,9 +95,10 @@ int64_t tra_maxcnt(int T, int H, int W, int block, int r_max);
  *   q, k, v   device bf16 [heads][T][H][W][head_dim]
  *   r_min, r_max  0 <= r_min <= r_max, or both TRA_RADIUS_INF (dense mode)
  *   out       device fp32 [heads][T][H][W][head_dim]
- * Equivalent to tra_probe, then tra_mask, then tra_attn on one stream (the
- * fused path reads q, k and v from HBM once for the probe and the key/value
- * tile packing).
+ * Equivalent to tra_probe, then tra_mask, then tra_attn on one stream, bit for
+ * bit (the fused path reads q, k and v from HBM once for the probe and the
+ * key/value tile packing, and builds the attention walks straight from the
+ * radii without writing the lists out).
  */
 int tra_attention(const void *q, const void *k, const void *v,
                   int T, int H, int W, int heads, int head_dim, int block,

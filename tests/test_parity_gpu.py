@@ -633,8 +633,13 @@ def test_wan13b_81f_every_row():
     nb = tra.tra_grid(c.T, c.H, c.W)[2]
     print(f"[parity] {c.slug}: block density {cnt.sum().item() / (c.heads * nb * nb):.4f}",
           flush=True)
+    staged = gpu_attn(qd, kd, vd, shp, idx, cnt, maxcnt).cpu().numpy()
     del idx, cnt
     got = gpu_attention(qd, kd, vd, shp, c.r_min, c.r_max).cpu().numpy()
+    # the fused call builds its walks from the radii without the lists: the
+    # same walks, so the same bits as the staged calls
+    assert np.array_equal(got, staged), f"{c.slug}: fused call differs from the staged calls"
+    del staged
     ref = oracle.attention(q, k, v, r_g)
     assert_close(got, ref, f"{c.slug} attention (all {c.heads * c.N} rows)")
 
@@ -674,8 +679,11 @@ def test_full_workload(wid):
     nb = tra.tra_grid(c.T, c.H, c.W)[2]
     density = cnt.sum().item() / (c.heads * nb * nb)
     print(f"[parity] {c.slug}: block density {density:.4f}", flush=True)
+    staged = gpu_attn(qd, kd, vd, shp, idx, cnt, maxcnt)
     del idx, cnt
     out = gpu_attention(qd, kd, vd, shp, c.r_min, c.r_max)
+    assert torch.equal(out, staged), f"{c.slug}: fused call differs from the staged calls"
+    del staged
     rows = np.union1d(item_rows(shp, 1, seed=wid), sample_rows(shp, 0, seed=wid))
     got = out.view(-1, c.d)[torch.from_numpy(rows).cuda()].cpu().numpy()
     del out

@@ -82,9 +82,11 @@ namespace {
 constexpr int kScanThreads = 1024;
 
 // Exclusive prefix sum of one value per thread over the block (1024 threads):
-// shuffles within each wave, then the 16 wave totals.  Every thread gets its
-// exclusive prefix; *total receives the block total.
+// shuffles within each wave, then the same over the 16 wave totals in the
+// first wave.  Every thread gets its exclusive prefix; *total receives the
+// block total.
 __device__ int64_t block_exclusive_scan(int64_t v, int64_t *wave_sums, int64_t *total) {
+    constexpr int kWaves = kScanThreads / 64;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     int64_t x = v;
 #pragma unroll
@@ -94,17 +96,18 @@ __device__ int64_t block_exclusive_scan(int64_t v, int64_t *wave_sums, int64_t *
     }
     if (lane == 63) wave_sums[wid] = x;
     __syncthreads();
-    if (tid == 0) {
-        int64_t run = 0;
-        for (int w = 0; w < kScanThreads / 64; ++w) {
-            const int64_t t = wave_sums[w];
-            wave_sums[w] = run;
-            run += t;
+    if (wid == 0) {
+        int64_t w = lane < kWaves ? wave_sums[lane] : 0;
+#pragma unroll
+        for (int off = 1; off < kWaves; off <<= 1) {
+            const int64_t y = __shfl_up(w, off);
+            if (lane >= off) w += y;
         }
-        *total = run;
+        if (lane < kWaves) wave_sums[lane] = w;  // inclusive
+        if (lane == kWaves - 1) *total = w;
     }
     __syncthreads();
-    const int64_t r = wave_sums[wid] + x - v;
+    const int64_t r = (wid ? wave_sums[wid - 1] : 0) + x - v;
     __syncthreads();  // wave_sums may be reused by the next scan
     return r;
 }
@@ -443,6 +446,7 @@ constexpr int kOrderThreads = kScanThreads;
 constexpr int kOrderMaxBin = 8191;
 constexpr int kXcds = 8;
 constexpr int kItemCost = 4;  // prologue and epilogue of an item, in walk steps
+constexpr int kOrderRegItems = 8;  // chunk lengths held in registers (items <= 8192)
 
 __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *__restrict__ ulen,
                                                               int64_t items, int64_t cap,
@@ -457,25 +461,42 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *__r
         const int len = ulen[it];
         return len < 0 ? 0 : (len > maxlen ? maxlen : len);
     };
-    // chunk sums and their exclusive block scan
+    // chunk sums and their exclusive block scan (a chunk of up to
+    // kOrderRegItems lengths is loaded once, all loads in flight together)
     const int64_t chunk = (items + kOrderThreads - 1) / kOrderThreads;
     const int64_t c0 = min(items, tid * chunk), c1 = min(items, c0 + chunk);
+    const bool in_regs = chunk <= kOrderRegItems;
+    int len_reg[kOrderRegItems];
     int64_t mine = 0;
-    for (int64_t it = c0; it < c1; ++it) mine += length_of(it) + kItemCost;
-    if (tid < kXcds) below[tid] = 0;
+    if (in_regs) {
+#pragma unroll
+        for (int i = 0; i < kOrderRegItems; ++i) len_reg[i] = c0 + i < c1 ? length_of(c0 + i) : 0;
+#pragma unroll
+        for (int i = 0; i < kOrderRegItems; ++i) mine += c0 + i < c1 ? len_reg[i] + kItemCost : 0;
+    } else {
+        for (int64_t it = c0; it < c1; ++it) mine += length_of(it) + kItemCost;
+    }
+    if (tid < kXcds) below[tid] = tid == 0 ? 0 : items;
     int64_t start = block_exclusive_scan(mine, wave_sums, &total_work);
     const int64_t total = total_work;
-    // count, for every share, the items of this chunk starting below it
+    // below[s] = the number of items whose work starts below share s of the
+    // total (8 start < s total).  Starts increase strictly (every item costs
+    // at least kItemCost), so that count is one past the item whose work
+    // interval [8 start, 8 (start + w)) holds s total: its thread writes it.
     {
-        int64_t cnt[kXcds] = {};
-        for (int64_t it = c0; it < c1; ++it) {
+        auto mark = [&](int64_t it, int64_t w) {
 #pragma unroll
-            for (int s = 1; s < kXcds; ++s) cnt[s] += start * kXcds < s * total ? 1 : 0;
-            start += length_of(it) + kItemCost;
+            for (int s = 1; s < kXcds; ++s)
+                if (start * kXcds < s * total && s * total <= (start + w) * kXcds) below[s] = it + 1;
+            start += w;
+        };
+        if (in_regs) {
+#pragma unroll
+            for (int i = 0; i < kOrderRegItems; ++i)
+                if (c0 + i < c1) mark(c0 + i, len_reg[i] + kItemCost);
+        } else {
+            for (int64_t it = c0; it < c1; ++it) mark(it, length_of(it) + kItemCost);
         }
-#pragma unroll
-        for (int s = 1; s < kXcds; ++s)
-            if (cnt[s]) atomicAdd((unsigned long long *)&below[s], (unsigned long long)cnt[s]);
     }
     for (int i = tid; i <= maxlen; i += kOrderThreads) bins[i] = 0;
     __syncthreads();

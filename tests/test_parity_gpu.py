@@ -351,17 +351,20 @@ def test_plan_reuse_across_steps():
         assert_close(out.cpu().numpy().reshape(-1, d)[rows], ref, f"plan reuse step {step}")
 
 
-@pytest.mark.parametrize("skewed", [False, True], ids=["balanced", "capped"])
-def test_work_order_ranges(skewed):
+@pytest.mark.parametrize("case", ["balanced", "capped", "many"])
+def test_work_order_ranges(case):
     # The work order deals the walk items to eight XCD ranges: contiguous raster
     # ranges cut at equal shares of the total work (walk length + 4 per item),
     # each of at most cap = 2 ceil(items / 8) items, taken longest first into
     # grid slots 8 k + x, -1 past a range's end.  Every item appears once.  The
     # skewed case puts nearly all the work in the first items, so equal-work
     # cuts would leave the later ranges above the cap: the cap moves the cuts.
-    T, H, W, heads = 6, 30, 52, 3
+    # "many" has more than 8192 items (more than eight per thread of the order
+    # kernel's workgroup, which then reads the lengths in a loop).
+    skewed = case == "capped"
+    T, H, W, heads = (21, 45, 80, 16) if case == "many" else (6, 30, 52, 3)
     shp = (heads, T, H, W, 128)
-    print(f"[case] work order {shp} skewed={skewed}", flush=True)
+    print(f"[case] work order {shp} {case}", flush=True)
     nb = tra.tra_grid(T, H, W)[2]
     rng = np.random.default_rng(17)
     if skewed:

@@ -211,18 +211,19 @@ __global__ __launch_bounds__(256) void pack_pool_kernel(
 // does not depend on the order of the dims), so every lane reads one
 // contiguous quarter row of its query and of its key.  The workgroup's waves
 // take the key tiles round robin, each keeping an online (max, sum,
-// weighted-log) state per lane; the four lane groups and the waves are merged
-// at the end.
-constexpr int kEntWaves = 8;   // waves per workgroup
+// weighted-log) state per lane in base 2 (x = s log2(e), sums of 2^(x - m):
+// one v_exp_f32 per logit); the four lane groups and the waves are merged at
+// the end, and H = ln Z - ln(2) A / Z.
+constexpr int kEntWaves = 4;   // waves per workgroup
 constexpr int kEntQB = 16;     // query blocks per workgroup
 
 struct EntState {
-    float m, Z, A;  // running max, sum e^(s-m), sum e^(s-m) (s-m)
+    float m, Z, A;  // running max of x, sum 2^(x-m), sum 2^(x-m) (x-m)
 };
 
 __device__ __forceinline__ EntState ent_merge(EntState a, EntState b) {
     const float mn = fmaxf(a.m, b.m);
-    const float ea = expf(a.m - mn), eb = expf(b.m - mn);
+    const float ea = __builtin_amdgcn_exp2f(a.m - mn), eb = __builtin_amdgcn_exp2f(b.m - mn);
     EntState r;
     r.m = mn;
     r.Z = ea * a.Z + eb * b.Z;
@@ -239,6 +240,7 @@ __global__ __launch_bounds__(64 * kEntWaves) void entropy_kernel(
     typedef float f32x4_t __attribute__((ext_vector_type(4)));
     __shared__ float red[3][kEntWaves][kEntQB];
 
+    const float scale2 = scale * 1.4426950408889634f;
     const int h = blockIdx.y;
     const int q0 = blockIdx.x * kEntQB;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -293,17 +295,17 @@ __global__ __launch_bounds__(64 * kEntWaves) void entropy_kernel(
         float mx = st.m;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            sv[r] = acc[r] * scale;
+            sv[r] = acc[r] * scale2;
             if (key0 + r < g.nb) mx = fmaxf(mx, sv[r]);
         }
         if (logits && q0 + col < g.nb) {
             float *row = logits + ((size_t)h * g.nb + q0 + col) * g.nb;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                if (key0 + r < g.nb) row[key0 + r] = sv[r];
+                if (key0 + r < g.nb) row[key0 + r] = acc[r] * scale;
         }
         if (mx > st.m) {
-            const float a = expf(st.m - mx);
+            const float a = __builtin_amdgcn_exp2f(st.m - mx);
             st.A = a * (st.A + (st.m - mx) * st.Z);
             st.Z *= a;
             st.m = mx;
@@ -312,7 +314,7 @@ __global__ __launch_bounds__(64 * kEntWaves) void entropy_kernel(
         for (int r = 0; r < 4; ++r) {
             if (key0 + r < g.nb) {
                 const float x = sv[r] - st.m;
-                const float e = expf(x);
+                const float e = __builtin_amdgcn_exp2f(x);
                 st.Z += e;
                 st.A += e * x;
             }
@@ -339,7 +341,7 @@ __global__ __launch_bounds__(64 * kEntWaves) void entropy_kernel(
             acc = ent_merge(acc, EntState{red[0][w][col], red[1][w][col], red[2][w][col]});
         const int b = q0 + col;
         if (b < g.nb) {
-            const float Hb = logf(acc.Z) - acc.A / acc.Z;
+            const float Hb = logf(acc.Z) - 0.69314718055994531f * (acc.A / acc.Z);
             const float hn = Hb * inv_ln_nb;
             int64_t r = (int64_t)r_min + (int64_t)floor((double)hn * (double)R);
             r = r < r_min ? r_min : (r > r_max ? r_max : r);

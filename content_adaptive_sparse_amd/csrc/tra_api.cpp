@@ -94,62 +94,6 @@ hipError_t pool_for_current_device(hipMemPool_t *out) {
     return hipSuccess;
 }
 
-// Per-device side stream (default priority, non-blocking): the packing of k and
-// v runs on it while the caller's stream builds the lists and the walk plan, the
-// two joined with events before the attention.
-std::mutex g_side_mu;
-hipStream_t g_side[kMaxDevices] = {};
-
-hipError_t side_stream(hipStream_t *out) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-    std::lock_guard<std::mutex> lock(g_side_mu);
-    if (!g_side[dev]) {
-        e = hipStreamCreateWithFlags(&g_side[dev], hipStreamNonBlocking);
-        if (e != hipSuccess) return e;
-    }
-    *out = g_side[dev];
-    return hipSuccess;
-}
-
-// A fork of `main` onto the side stream and the join back: work enqueued on
-// side() after the constructor runs after everything enqueued on main before
-// it; join() (also run by the destructor, so that no path returns with side
-// work unjoined before the scratch is freed on main) makes main wait for it.
-class Fork {
-  public:
-    explicit Fork(hipStream_t main) : main_(main) {
-        if (side_stream(&side_) != hipSuccess) return;
-        if (hipEventCreateWithFlags(&fork_, hipEventDisableTiming) != hipSuccess) return;
-        if (hipEventCreateWithFlags(&join_, hipEventDisableTiming) != hipSuccess) {
-            (void)hipEventDestroy(fork_);
-            return;
-        }
-        ok_ = hipEventRecord(fork_, main_) == hipSuccess &&
-              hipStreamWaitEvent(side_, fork_, 0) == hipSuccess;
-        live_ = true;
-    }
-    ~Fork() { (void)join(); }
-    bool ok() const { return ok_; }
-    hipStream_t side() const { return side_; }
-    hipError_t join() {
-        if (!live_) return hipSuccess;
-        live_ = false;
-        hipError_t e = hipEventRecord(join_, side_);
-        if (e == hipSuccess) e = hipStreamWaitEvent(main_, join_, 0);
-        (void)hipEventDestroy(fork_);
-        (void)hipEventDestroy(join_);
-        return e;
-    }
-
-  private:
-    hipStream_t main_, side_ = nullptr;
-    hipEvent_t fork_ = nullptr, join_ = nullptr;
-    bool ok_ = false, live_ = false;
-};
-
 // Scratch carved from one stream-ordered allocation; freed on the stream when
 // the scope ends (after every kernel that uses it has been enqueued).
 class Scratch {
@@ -542,8 +486,10 @@ int tra_attn_plan(const void *q, const void *k, const void *v, int T, int H, int
                           plan_layout(g, heads, maxcnt), out, stream);
 }
 
-// Lists (with optional log-weights) -> walk plan in library scratch -> attention;
-// the packing of k and v runs on the side stream meanwhile.
+// Lists (with optional log-weights) -> walk plan in library scratch -> attention,
+// all on the caller's stream.  (Packing k and v on a second stream beside the
+// latency-bound plan kernels measured slightly slower: the HBM-bound packing
+// slows the kernels beside it more than it overlaps them.)
 static int attn_lists(const void *q, const void *k, const void *v, const tra::Grid &g, int heads,
                       int head_dim, const int32_t *idx, const int32_t *cnt, const float *lw,
                       int64_t maxcnt, void *out, hipStream_t stream) {
@@ -555,15 +501,8 @@ static int attn_lists(const void *q, const void *k, const void *v, const tra::Gr
     if (rc != TRA_OK) return rc;
     const Packed pk = packed_at(ws, po);
     char *plan = ws.at<char>(o_plan);
-    hipError_t e;
-    {
-        Fork fork(stream);
-        if (!fork.ok()) return TRA_ERR_HIP;
-        e = pack_kv(head_dim, nullptr, k, v, g, heads, nullptr, nullptr, pk, fork.side());
-        if (e == hipSuccess) e = plan_walk_into(idx, cnt, lw, maxcnt, g, heads, plan, L, stream);
-        const hipError_t ej = fork.join();
-        if (e == hipSuccess) e = ej;
-    }
+    hipError_t e = pack_kv(head_dim, nullptr, k, v, g, heads, nullptr, nullptr, pk, stream);
+    if (e == hipSuccess) e = plan_walk_into(idx, cnt, lw, maxcnt, g, heads, plan, L, stream);
     if (e == hipSuccess) e = attn_launch(q, pk, g, heads, head_dim, plan, L, out, stream);
     return hip_status(e);
 }

@@ -211,14 +211,24 @@ def main():
     del idx
 
     # ---- the attention kernel alone: `reps` back-to-back launches along the
-    # probe radii's walk plan between one pair of HIP events on the launch
-    # stream (no per-kernel brackets); the same for the dense mode ----
+    # probe radii's walk plan (built from the radii as the layer builds it)
+    # between one pair of HIP events on the launch stream (no per-kernel
+    # brackets); the same for the dense mode ----
     reps = max(10, args.steps)
+
+    def radius_plan(rd, rmax):
+        mc = tra.tra_maxcnt(T, H, W, 64, rmax)
+        pl = torch.empty(tra.tra_plan_bytes(T, H, W, heads, 64, mc), dtype=torch.uint8,
+                         device="cuda")
+        tra.tra_plan_radius(rd, T, H, W, heads, 64, rmax, pl)
+        return pl, mc
+
+    plan, _ = radius_plan(radius, c.r_max)
+    t_attn = tra.tra_time_attn_plan(qd, kd, vd, T, H, W, heads, d, 64, plan, maxcnt, reps, out)
+    t_dense_attn = tra.tra_time_attn_plan(qd, kd, vd, T, H, W, heads, d, 64, None, 0, reps, out)
+    del plan
     idx = torch.empty(heads, nb, maxcnt, dtype=torch.int32, device="cuda")
     tra.tra_mask(radius, T, H, W, heads, 64, c.r_max, idx, cnt)
-    t_attn = tra.tra_time_attn(qd, kd, vd, T, H, W, heads, d, 64, idx, cnt, None, maxcnt, reps, out)
-    t_dense_attn = tra.tra_time_attn(qd, kd, vd, T, H, W, heads, d, 64, None, None, None, 0, reps,
-                                     out)
     achieved = flops_pair * pairs / (t_attn * 1e-3) / 1e12
     dense_tflops = flops_pair * heads * nb * nb / (t_dense_attn * 1e-3) / 1e12
     # the same launch counted three ways: per computed 64 x 64 block pair (the
@@ -250,6 +260,10 @@ def main():
     def attn_time(ix, cn, mc, lw=None):
         return tra.tra_time_attn(qd, kd, vd, T, H, W, heads, d, 64, ix, cn, lw, mc, 10, out)
 
+    def attn_time_radii(rd, rmax):
+        pl, mc = radius_plan(rd, rmax)
+        return tra.tra_time_attn_plan(qd, kd, vd, T, H, W, heads, d, 64, pl, mc, 10, out)
+
     # ---- injected-radius density sweep (attention kernel only) ----
     sweep = []
     if not args.no_sweep:
@@ -266,7 +280,7 @@ def main():
             tra.tra_mask(rd, T, H, W, heads, 64, rmax, ix, cn)
             torch.cuda.synchronize()
             p = int(cn.sum().item())
-            ta = attn_time(ix, cn, mc)
+            ta = attn_time_radii(rd, rmax)
             sweep.append({"radii": name, "density": round(p / (heads * nb * nb), 4),
                           "attn_ms": round(ta, 4),
                           "tflops": round(flops_pair * p / (ta * 1e-3) / 1e12, 1),
@@ -274,22 +288,18 @@ def main():
             log(f"[bench] sweep {sweep[-1]}")
             del ix, cn
 
-    # ---- cross-step reuse: probe, mask and walk plan once (the warm-up step);
-    # every later step packs k, v and runs the attention along the stored plan ----
+    # ---- cross-step reuse: probe and walk plan once (the warm-up step); every
+    # later step packs k, v and runs the attention along the stored plan ----
     reuse, routing, route_lists = None, None, None
     if not args.no_sweep:
-        idx = torch.empty(heads, nb, maxcnt, dtype=torch.int32, device="cuda")
-        tra.tra_mask(radius, T, H, W, heads, 64, c.r_max, idx, cnt)
-        plan = torch.empty(tra.tra_plan_bytes(T, H, W, heads, 64, maxcnt), dtype=torch.uint8,
-                           device="cuda")
-        tra.tra_plan(idx, cnt, maxcnt, T, H, W, heads, 64, plan)
+        plan, _ = radius_plan(radius, c.r_max)
         step = lambda: tra.tra_attn_plan(qd, kd, vd, T, H, W, heads, d, 64, plan, maxcnt, out)
         ms_reuse, _ = timed(step, max(5, args.steps // 2), 2)
         reuse = {"ms_per_step": round(ms_reuse, 4),
                  "speedup_vs_dense_layer": round(ms_dense / ms_reuse, 3),
                  "plan_bytes": int(plan.numel())}
         log(f"[bench] cross-step reuse {reuse}")
-        del idx, plan
+        del plan
 
         # ---- binary routing: the 20% of blocks per head with the highest
         # pooled-probe entropy attend densely, the rest with radius 1 ----
@@ -306,7 +316,7 @@ def main():
         torch.cuda.synchronize()
         cnn = cn.cpu().numpy()
         p = int(cnn.sum())
-        ta = attn_time(ix, cn, nb)
+        ta = attn_time_radii(rd, INF)
         routing = {"dense_blocks": round(float((rr == INF).mean()), 4), "local_radius": 1,
                    "density": round(p / (heads * nb * nb), 4),
                    "list_len_min_mean_max": [int(cnn.min()), round(float(cnn.mean()), 1), int(cnn.max())],
@@ -449,7 +459,8 @@ def main():
             "radius_histogram": rhist,
             "attn_ms": round(t_attn, 4),
             "attn_timing": (f"mean of {reps} back-to-back attention launches between one HIP event "
-                            "pair on the launch stream (tra_time_attn)"),
+                            "pair on the launch stream, along the walk plan the layer builds from the radii "
+                            "(tra_plan_radius, tra_time_attn_plan)"),
             "mfma_executed_tflops_attn": round(mfma_flops / (t_attn * 1e-3) / 1e12, 1),
             "real_token_tflops_attn": round(real_flops / (t_attn * 1e-3) / 1e12, 1),
             "flops_per_launch": {"computed_block_pairs": flops_pair * pairs,

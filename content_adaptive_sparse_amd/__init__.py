@@ -21,7 +21,7 @@ __all__ = [
     "tra_plan_bytes", "tra_plan", "tra_attn_plan", "tra_token_probe", "tra_token_mask",
     "tra_token_attention", "tra_token_warmup", "tra_sip_mask", "tra_attn_weighted",
     "tra_workspace_bytes", "tra_time_attn", "tra_release_scratch", "tra_probe_static",
-    "tra_static_scratch_bytes",
+    "tra_static_scratch_bytes", "tra_plan_radius", "tra_time_attn_plan",
     "tra_profile_begin", "tra_profile_end", "KERNEL_KINDS",
 ]
 
@@ -76,6 +76,8 @@ def library() -> ctypes.CDLL:
         lib.tra_plan.restype = I
         lib.tra_attn_plan.argtypes = [P, P, P, I, I, I, I, I, I, P, L, P, P]
         lib.tra_attn_plan.restype = I
+        lib.tra_plan_radius.argtypes = [P, I, I, I, I, I, I, P, P]
+        lib.tra_plan_radius.restype = I
         F = ctypes.c_float
         lib.tra_token_probe.argtypes = [P, P, I, I, I, I, I, I, F, F, P, P, P]
         lib.tra_token_probe.restype = I
@@ -88,6 +90,9 @@ def library() -> ctypes.CDLL:
         lib.tra_time_attn.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P, L, I, P,
                                       ctypes.POINTER(F), P]
         lib.tra_time_attn.restype = I
+        lib.tra_time_attn_plan.argtypes = [P, P, P, I, I, I, I, I, I, P, L, I, P,
+                                           ctypes.POINTER(F), P]
+        lib.tra_time_attn_plan.restype = I
         lib.tra_release_scratch.argtypes = []
         lib.tra_release_scratch.restype = I
         lib.tra_sip_mask.argtypes = [P, P, P, I, I, I, I, I, I, F, P, P, P, P]
@@ -230,6 +235,14 @@ def tra_plan(idx, cnt, maxcnt, T, H, W, heads, block, plan, stream=None):
         _ptr(plan, None, "plan"), _stream(stream)), "tra_plan")
 
 
+def tra_plan_radius(radius, T, H, W, heads, block, r_max, plan, stream=None):
+    """Walk plan of the radius mask's lists straight from the radii into ``plan``
+    (tra_plan_bytes with maxcnt = tra_maxcnt(..., r_max))."""
+    _check(library().tra_plan_radius(
+        _ptr(radius, _i32(), "radius"), T, H, W, heads, block, int(r_max),
+        _ptr(plan, None, "plan"), _stream(stream)), "tra_plan_radius")
+
+
 def tra_attn_plan(q, k, v, T, H, W, heads, head_dim, block, plan, maxcnt, out, stream=None):
     _check(library().tra_attn_plan(
         _ptr(q, _bf16(), "q"), _ptr(k, _bf16(), "k"), _ptr(v, _bf16(), "v"), T, H, W, heads,
@@ -278,6 +291,18 @@ def tra_time_attn(q, k, v, T, H, W, heads, head_dim, block, idx, cnt, lw, maxcnt
         head_dim, block, _ptr(idx, _i32(), "idx"), _ptr(cnt, _i32(), "cnt"),
         _ptr(lw, _f32(), "lw"), int(maxcnt), int(reps), _ptr(out, _f32(), "out"),
         ctypes.byref(ms), _stream(stream)), "tra_time_attn")
+    return ms.value
+
+
+def tra_time_attn_plan(q, k, v, T, H, W, heads, head_dim, block, plan, maxcnt, reps, out,
+                       stream=None) -> float:
+    """Mean milliseconds of one attention-kernel launch along a stored plan
+    (plan = None is the dense mode)."""
+    ms = ctypes.c_float()
+    _check(library().tra_time_attn_plan(
+        _ptr(q, _bf16(), "q"), _ptr(k, _bf16(), "k"), _ptr(v, _bf16(), "v"), T, H, W, heads,
+        head_dim, block, _ptr(plan, None, "plan"), int(maxcnt), int(reps),
+        _ptr(out, _f32(), "out"), ctypes.byref(ms), _stream(stream)), "tra_time_attn_plan")
     return ms.value
 
 

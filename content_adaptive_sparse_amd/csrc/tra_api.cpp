@@ -473,6 +473,23 @@ int tra_plan(const int32_t *idx, const int32_t *cnt, int64_t maxcnt, int T, int 
                                      plan_layout(g, heads, maxcnt), stream));
 }
 
+int tra_plan_radius(const int32_t *radius, int T, int H, int W, int heads, int block, int r_max,
+                    void *plan, hipStream_t stream) {
+    tra::Grid g;
+    int rc = make_grid(T, H, W, block, &g);
+    if (rc == TRA_OK) rc = check_dims(heads, 64, g);
+    if (rc != TRA_OK) return rc;
+    if (r_max < 0) return TRA_ERR_INVALID_ARG;
+    const int64_t maxcnt = maxcnt_of(g, r_max);
+    if ((rc = check_plan(g, heads, maxcnt)) != TRA_OK) return rc;
+    if (!radius || !plan) return TRA_ERR_INVALID_ARG;
+    const PlanLayout L = plan_layout(g, heads, maxcnt);
+    char *pl = static_cast<char *>(plan);
+    return hip_status(plan_walk_radius(radius, r_max, maxcnt, g, heads, (int2 *)(pl + L.o_pairs),
+                                       (int32_t *)(pl + L.o_ulist), (int32_t *)(pl + L.o_ulen),
+                                       (int32_t *)(pl + L.o_order), stream));
+}
+
 int tra_attn_plan(const void *q, const void *k, const void *v, int T, int H, int W, int heads,
                   int head_dim, int block, const void *plan, int64_t maxcnt, void *out,
                   hipStream_t stream) {
@@ -534,6 +551,34 @@ int tra_attn_weighted(const void *q, const void *k, const void *v, int T, int H,
     return attn_lists(q, k, v, g, heads, head_dim, idx, cnt, lw, maxcnt, out, stream);
 }
 
+// Packs k and v into pk, then times `reps` back-to-back attention launches
+// along the plan (nullptr: dense mode) between one pair of events on `stream`.
+static int time_attn_launches(const void *q, const void *k, const void *v, const tra::Grid &g,
+                              int heads, int head_dim, const char *plan, const PlanLayout &L,
+                              const Packed &pk, int reps, void *out, float *ms,
+                              hipStream_t stream) {
+    hipError_t e = pack_kv(head_dim, nullptr, k, v, g, heads, nullptr, nullptr, pk, stream);
+    if (e != hipSuccess) return hip_status(e);
+    hipEvent_t ev[2];
+    if (hipEventCreate(&ev[0]) != hipSuccess) return TRA_ERR_HIP;
+    if (hipEventCreate(&ev[1]) != hipSuccess) {
+        (void)hipEventDestroy(ev[0]);
+        return TRA_ERR_HIP;
+    }
+    e = hipEventRecord(ev[0], stream);
+    for (int i = 0; i < reps && e == hipSuccess; ++i)
+        e = attn_launch(q, pk, g, heads, head_dim, plan, L, out, stream);
+    if (e == hipSuccess) e = hipEventRecord(ev[1], stream);
+    if (e == hipSuccess) e = hipEventSynchronize(ev[1]);
+    float t = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, ev[0], ev[1]);
+    (void)hipEventDestroy(ev[0]);
+    (void)hipEventDestroy(ev[1]);
+    if (e != hipSuccess) return TRA_ERR_HIP;
+    *ms = t / (float)reps;
+    return TRA_OK;
+}
+
 int tra_time_attn(const void *q, const void *k, const void *v, int T, int H, int W, int heads,
                   int head_dim, int block, const int32_t *idx, const int32_t *cnt,
                   const float *lw, int64_t maxcnt, int reps, void *out, float *ms,
@@ -554,26 +599,25 @@ int tra_time_attn(const void *q, const void *k, const void *v, int T, int H, int
     char *plan = idx ? ws.at<char>(o_plan) : nullptr;
     hipError_t e = hipSuccess;
     if (idx) e = plan_walk_into(idx, cnt, lw, maxcnt, g, heads, plan, L, stream);
-    if (e == hipSuccess) e = pack_kv(head_dim, nullptr, k, v, g, heads, nullptr, nullptr, pk, stream);
     if (e != hipSuccess) return hip_status(e);
-    hipEvent_t ev[2];
-    if (hipEventCreate(&ev[0]) != hipSuccess) return TRA_ERR_HIP;
-    if (hipEventCreate(&ev[1]) != hipSuccess) {
-        (void)hipEventDestroy(ev[0]);
-        return TRA_ERR_HIP;
-    }
-    e = hipEventRecord(ev[0], stream);
-    for (int i = 0; i < reps && e == hipSuccess; ++i)
-        e = attn_launch(q, pk, g, heads, head_dim, plan, L, out, stream);
-    if (e == hipSuccess) e = hipEventRecord(ev[1], stream);
-    if (e == hipSuccess) e = hipEventSynchronize(ev[1]);
-    float t = 0.f;
-    if (e == hipSuccess) e = hipEventElapsedTime(&t, ev[0], ev[1]);
-    (void)hipEventDestroy(ev[0]);
-    (void)hipEventDestroy(ev[1]);
-    if (e != hipSuccess) return TRA_ERR_HIP;
-    *ms = t / (float)reps;
-    return TRA_OK;
+    return time_attn_launches(q, k, v, g, heads, head_dim, plan, L, pk, reps, out, ms, stream);
+}
+
+int tra_time_attn_plan(const void *q, const void *k, const void *v, int T, int H, int W,
+                       int heads, int head_dim, int block, const void *plan, int64_t maxcnt,
+                       int reps, void *out, float *ms, hipStream_t stream) {
+    tra::Grid g;
+    int rc = make_grid(T, H, W, block, &g);
+    if (rc == TRA_OK) rc = check_dims(heads, head_dim, g);
+    if (rc != TRA_OK) return rc;
+    if (!q || !k || !v || !out || !ms || reps < 1) return TRA_ERR_INVALID_ARG;
+    if (plan && (rc = check_plan(g, heads, maxcnt)) != TRA_OK) return rc;
+    const PlanLayout L = plan ? plan_layout(g, heads, maxcnt) : PlanLayout{};
+    Scratch ws(stream);
+    const PackedOffsets po = reserve_packed(ws, g, heads, head_dim);
+    if ((rc = ws.allocate()) != TRA_OK) return rc;
+    return time_attn_launches(q, k, v, g, heads, head_dim, static_cast<const char *>(plan), L,
+                              packed_at(ws, po), reps, out, ms, stream);
 }
 
 int tra_sip_mask(const void *q, const void *k, const float *u, int T, int H, int W, int heads,

@@ -104,10 +104,11 @@ hipError_t launch_pair(const int32_t *cnt, int64_t maxcnt, const Grid &g, int he
                        hipStream_t s);
 
 // The same two steps for the radius mask's lists taken straight from the radii
-// (no lists): the pair table from the lists' lengths (box sizes, at most
-// maxcnt), then each item's walk, the union of its two blocks' key boxes --
-// identical to launch_pair + launch_union of tra_mask's lists when maxcnt
-// holds the largest box (tra_maxcnt), so that no list is cut short.
+// (no lists): the pair table from the radii (vertical neighbours of equal
+// radius, the others classed by radius), then each item's walk, the union of its
+// two blocks' key boxes.  Every block meets the same entries in the same order
+// as along launch_pair + launch_union of tra_mask's lists when maxcnt holds the
+// largest box (tra_maxcnt), so that no list is cut short: the same results.
 hipError_t launch_pair_radius(const int32_t *radius, int r_max, int64_t maxcnt, const Grid &g,
                               int heads, int2 *pairs, hipStream_t s);
 hipError_t launch_radius_walk(const int32_t *radius, int r_max, int64_t maxcnt, const Grid &g,

@@ -134,9 +134,6 @@ struct KeyBox {
     __device__ bool contains(int t, int y, int x) const {
         return t >= t0 && t <= t1 && y >= y0 && y <= y1 && x >= x0 && x <= x1;
     }
-    __device__ int64_t count() const {
-        return t0 > t1 ? 0 : (int64_t)(t1 - t0 + 1) * (y1 - y0 + 1) * (x1 - x0 + 1);
-    }
 };
 
 __device__ KeyBox key_box(int b, int32_t radius, int r_max, const Grid &g) {
@@ -153,8 +150,15 @@ __device__ KeyBox key_box(int b, int32_t radius, int r_max, const Grid &g) {
     return k;
 }
 
-// cnt: list lengths; or, with radius non-null, the lengths of the radius
-// mask's lists computed from the radii (its boxes, at most maxcnt).
+// cnt: list lengths; or, with radius non-null, the radius mask's lists known
+// by their radii.  Then vertical neighbours stay together when their radii are
+// equal (their key boxes then differ by at most one tile row), and the other
+// blocks are classed by radius, largest first, and paired in (frame, tile
+// column, tile row) order inside a class, so that a pair's two boxes are the
+// same box shifted by a tile or two: at the Wan 81-frame layer's probe radii
+// the walks' slot efficiency is 0.92 instead of 0.87 with the length rule, and
+// the walks take 6% fewer steps.  (Pairing does not change any result: each
+// block meets its own entries in ascending order whatever its partner.)
 __global__ __launch_bounds__(kPairThreads) void pair_kernel(const int32_t *__restrict__ cnt,
                                                            const int32_t *__restrict__ radius,
                                                            int r_max, int64_t maxcnt, Grid g,
@@ -166,8 +170,8 @@ __global__ __launch_bounds__(kPairThreads) void pair_kernel(const int32_t *__res
     const int h = blockIdx.x, tid = threadIdx.x;
     const int32_t *ch = radius ? radius + (int64_t)h * g.nb : cnt + (int64_t)h * g.nb;
     int2 *out = pairs + (int64_t)h * pph;
-    auto len = [&](int b) -> int {
-        const int64_t m = radius ? key_box(b, ch[b], r_max, g).count() : ch[b];
+    auto len = [&](int b) -> int {  // list mode
+        const int64_t m = ch[b];
         return (int)(m < 0 ? 0 : (m > maxcnt ? maxcnt : m));
     };
     // the vertical partner of block b (-1 when its tile row has none)
@@ -176,9 +180,27 @@ __global__ __launch_bounds__(kPairThreads) void pair_kernel(const int32_t *__res
         const int o = (by & 1) ? b - g.nbx : b + g.nbx;
         return ((by & 1) || by + 1 < g.nby) ? o : -1;
     };
+    auto rad = [&](int b) -> int {
+        const int32_t r = ch[b];
+        return r < 0 ? 0 : (r > r_max ? r_max : r);
+    };
+    auto well = [&](int a, int b) -> bool {
+        return radius ? rad(a) == rad(b) : lengths_pair_well(len(a), len(b));
+    };
+    auto klass = [&](int b) -> int {
+        return radius ? min(rad(b), kPairClasses - 1) : length_class(len(b));
+    };
     auto orphan = [&](int b) -> bool {
         const int o = partner(b);
-        return o >= 0 && !lengths_pair_well(len(b), len(o));
+        return o >= 0 && !well(b, o);
+    };
+    // the i-th block of the orphan order: raster, or (frame, column, row) for radii
+    const int plane = g.nby * g.nbx;
+    auto block_at = [&](int i) -> int {
+        if (!radius) return i;
+        const int t = i / plane, rem = i - t * plane;
+        const int x = rem / g.nby, y = rem - x * g.nby;
+        return (t * g.nby + y) * g.nbx + x;
     };
     // kept vertical pairs, compacted in raster order
     int64_t kept = 0;
@@ -188,7 +210,7 @@ __global__ __launch_bounds__(kPairThreads) void pair_kernel(const int32_t *__res
         bool keep = false;
         if (p < pph) {
             pair_blocks(p, g, qa, qb);
-            keep = qb < 0 || lengths_pair_well(len(qa), len(qb));
+            keep = qb < 0 || well(qa, qb);
         }
         int64_t tot;
         const int64_t at = block_exclusive_scan(keep ? 1 : 0, wave_sums, &total_sh);
@@ -201,7 +223,7 @@ __global__ __launch_bounds__(kPairThreads) void pair_kernel(const int32_t *__res
     for (int k = tid; k < kPairClasses; k += kPairThreads) start[k] = run[k] = 0;
     __syncthreads();
     for (int b = tid; b < g.nb; b += kPairThreads)
-        if (orphan(b)) atomicAdd(&start[length_class(len(b))], 1);
+        if (orphan(b)) atomicAdd(&start[klass(b)], 1);
     __syncthreads();
     int64_t norph = 0;
     if (tid == 0) {
@@ -220,9 +242,9 @@ __global__ __launch_bounds__(kPairThreads) void pair_kernel(const int32_t *__res
         for (int i = tid; i < kPairClasses * (kPairThreads / 32); i += kPairThreads)
             (&member[0][0])[i] = 0u;
         __syncthreads();
-        const int b = b0 + tid;
+        const int b = b0 + tid < g.nb ? block_at(b0 + tid) : g.nb;
         const bool orph = b < g.nb && orphan(b);
-        const int k = orph ? length_class(len(b)) : 0;
+        const int k = orph ? klass(b) : 0;
         if (orph) atomicOr(&member[k][tid >> 5], 1u << (tid & 31));
         __syncthreads();
         if (orph) {

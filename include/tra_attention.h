@@ -304,6 +304,26 @@ int tra_attn_plan(const void *q, const void *k, const void *v, int T, int H, int
                   hipStream_t stream);
 
 /*
+ * The walk plan of the radius mask's lists built straight from the radii, as
+ * tra_attention builds it (Token Radius Attention ..., "The TRA Pipeline:
+ * Fused CUDA Kernels" -- radius comparison and block pruning -- and
+ * "Cross-Step Reuse"): no lists are written; vertical neighbours of equal
+ * radius share a work item, the other blocks are classed by radius (largest
+ * first) and paired in (frame, tile column, tile row) order inside a class;
+ * each item's walk is the union of its two blocks' key boxes.  Every query
+ * block meets the same key blocks in the same order as along tra_plan of
+ * tra_mask's lists for these radii, so tra_attn_plan along either plan gives
+ * the same results.
+ *   radius    device int32 [heads][nb]; values are clamped to [0, r_max] as
+ *             tra_mask clamps them.  r_max >= 0 (TRA_RADIUS_INF allowed).
+ *   plan      device buffer of tra_plan_bytes(T,H,W,heads,block,maxcnt) bytes with
+ *             maxcnt = tra_maxcnt(T,H,W,block,r_max); pass that maxcnt to
+ *             tra_attn_plan.
+ */
+int tra_plan_radius(const int32_t *radius, int T, int H, int W, int heads, int block, int r_max,
+                    void *plan, hipStream_t stream);
+
+/*
  * Benchmark helper: the attention kernel alone.  Builds the walk plan of the
  * lists (idx, cnt and optional log-weights lw as for tra_attn_weighted; idx =
  * cnt = NULL is the dense mode) and packs k and v, then launches the attention
@@ -316,6 +336,11 @@ int tra_time_attn(const void *q, const void *k, const void *v, int T, int H, int
                   int head_dim, int block, const int32_t *idx, const int32_t *cnt,
                   const float *lw, int64_t maxcnt, int reps, void *out, float *ms,
                   hipStream_t stream);
+/* The same along a stored plan (tra_plan or tra_plan_radius, with its maxcnt);
+ * plan = NULL is the dense mode. */
+int tra_time_attn_plan(const void *q, const void *k, const void *v, int T, int H, int W,
+                       int heads, int head_dim, int block, const void *plan, int64_t maxcnt,
+                       int reps, void *out, float *ms, hipStream_t stream);
 
 /*
  * Returns the current device's pooled scratch memory that no call holds any

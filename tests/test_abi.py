@@ -35,7 +35,8 @@ def test_header_declares_the_documented_entry_points():
     names = declared_functions()
     for n in ["tra_attention", "tra_probe", "tra_mask", "tra_attn", "tra_maxcnt", "tra_grid",
               "tra_status_string", "tra_version", "tra_profile_begin", "tra_profile_end",
-              "tra_plan_bytes", "tra_plan", "tra_attn_plan"]:
+              "tra_plan_bytes", "tra_plan", "tra_attn_plan", "tra_plan_radius",
+              "tra_time_attn_plan"]:
         assert n in names
 
 
@@ -180,6 +181,20 @@ def test_plan_argument_errors(lib):
     assert lib.tra_attn_plan(FAKE, FAKE, FAKE, 4, 16, 16, 2, 128, 64, None, 5, FAKE, None) == EINVAL
     assert lib.tra_attn_plan(FAKE, FAKE, FAKE, 4, 16, 16, 2, 80, 64, FAKE, 5, FAKE, None) == EUNSUP
     assert lib.tra_attn_plan(FAKE, FAKE, FAKE, 4, 16, 16, 2, 128, 64, FAKE, 0, FAKE, None) == EINVAL
+    # tra_plan_radius: radius and plan required, r_max >= 0, block 64
+    assert lib.tra_plan_radius(None, 4, 16, 16, 2, 64, 3, FAKE, None) == EINVAL
+    assert lib.tra_plan_radius(FAKE, 4, 16, 16, 2, 64, 3, None, None) == EINVAL
+    assert lib.tra_plan_radius(FAKE, 4, 16, 16, 2, 64, -1, FAKE, None) == EINVAL
+    assert lib.tra_plan_radius(FAKE, 4, 16, 16, 2, 32, 3, FAKE, None) == EUNSUP
+    assert lib.tra_plan_radius(FAKE, 4, 16, 16, 0, 64, 3, FAKE, None) == EINVAL
+    # tra_time_attn_plan: reps >= 1, ms given, the plan's maxcnt checked when a plan is given
+    F = ctypes.c_float
+    ms = F()
+    args = (FAKE, FAKE, FAKE, 4, 16, 16, 2, 128, 64)
+    assert lib.tra_time_attn_plan(*args, FAKE, 5, 0, FAKE, ctypes.byref(ms), None) == EINVAL
+    assert lib.tra_time_attn_plan(*args, FAKE, 5, 3, FAKE, None, None) == EINVAL
+    assert lib.tra_time_attn_plan(*args, FAKE, 0, 3, FAKE, ctypes.byref(ms), None) == EINVAL
+    assert lib.tra_time_attn_plan(*args, FAKE, 5, 3, None, ctypes.byref(ms), None) == EINVAL
 
 
 def test_profile_switch_without_launches(lib):

@@ -351,6 +351,49 @@ def test_plan_reuse_across_steps():
         assert_close(out.cpu().numpy().reshape(-1, d)[rows], ref, f"plan reuse step {step}")
 
 
+@pytest.mark.parametrize("case", ["probe", "random", "routing"])
+def test_plan_from_radii(case):
+    # The walk plan built straight from radii (tra_plan_radius, the plan
+    # tra_attention builds: its own pairing, no lists) gives the same bits as
+    # tra_attn on tra_mask's lists of the same radii -- every block meets its own
+    # key blocks in ascending order whoever shares its walk.  Random radii include
+    # negative values and values above r_max (both clamped like tra_mask clamps
+    # them); "routing" is binary routing (radius 1 or TRA_RADIUS_INF).
+    T, H, W, heads, d = (5, 29, 43, 3, 128) if case != "routing" else (6, 30, 52, 2, 64)
+    shp = (heads, T, H, W, d)
+    print(f"[case] plan from radii {shp} {case}", flush=True)
+    q, k, v = ti.make_inputs(T, H, W, heads, d, seed=12, family=36)
+    qd, kd, vd = dev16(q), dev16(k), dev16(v)
+    nb = tra.tra_grid(T, H, W)[2]
+    rng = np.random.default_rng(21)
+    if case == "probe":
+        r_max = 4
+        _, radii = gpu_probe(qd, kd, shp, 1, r_max)
+    elif case == "random":
+        r_max = 3
+        radii = rng.integers(-2, 6, size=(heads, nb)).astype(np.int32)
+    else:
+        r_max = INF
+        radii = np.where(rng.random((heads, nb)) < 0.2, INF, 1).astype(np.int32)
+    idx, cnt, maxcnt = gpu_mask(radii, shp, r_max)
+    assert maxcnt == tra.tra_maxcnt(T, H, W, 64, r_max)
+    plan = torch.empty(tra.tra_plan_bytes(T, H, W, heads, 64, maxcnt), dtype=torch.uint8,
+                       device="cuda")
+    tra.tra_plan_radius(torch.from_numpy(radii).cuda(), T, H, W, heads, 64, r_max, plan)
+    out = torch.full(shp, float("nan"), dtype=torch.float32, device="cuda")
+    tra.tra_attn_plan(qd, kd, vd, T, H, W, heads, d, 64, plan, maxcnt, out)
+    ref_gpu = gpu_attn(qd, kd, vd, shp, idx, cnt, maxcnt)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_gpu), "walks from radii differ from the lists' walks"
+    if case == "probe":
+        fused = gpu_attention(qd, kd, vd, shp, 1, r_max)
+        assert torch.equal(out, fused), "tra_attention differs from its plan"
+    clamped = np.clip(radii, 0, r_max if r_max != INF else None)
+    rows = np.union1d(item_rows(shp, 1, seed=3), sample_rows(shp, 0, seed=3))
+    ref = oracle.attention_rows(q, k, v, clamped, rows)
+    assert_close(out.cpu().numpy().reshape(-1, d)[rows], ref, f"plan from radii ({case})")
+
+
 @pytest.mark.parametrize("case", ["balanced", "capped", "many"])
 def test_work_order_ranges(case):
     # The work order deals the walk items to eight XCD ranges: contiguous raster
@@ -796,5 +839,16 @@ def test_timed_attention_matches_attention():
         ms = tra.tra_time_attn(qd, kd, vd, T, H, W, heads, d, 64, idx if lists else None,
                                cnt if lists else None, None, maxcnt if lists else 0, 3, out)
         ref = gpu_attn(qd, kd, vd, shp, idx, cnt, maxcnt) if lists else gpu_attn(qd, kd, vd, shp)
+        assert ms > 0.0
+        assert torch.equal(out, ref)
+    # along a stored plan (from the radii) and in dense mode without a plan
+    plan = torch.empty(tra.tra_plan_bytes(T, H, W, heads, 64, maxcnt), dtype=torch.uint8,
+                       device="cuda")
+    tra.tra_plan_radius(torch.from_numpy(radii).cuda(), T, H, W, heads, 64, 2, plan)
+    for planned in (True, False):
+        out = torch.full(shp, float("nan"), dtype=torch.float32, device="cuda")
+        ms = tra.tra_time_attn_plan(qd, kd, vd, T, H, W, heads, d, 64, plan if planned else None,
+                                    maxcnt if planned else 0, 3, out)
+        ref = gpu_attn(qd, kd, vd, shp, idx, cnt, maxcnt) if planned else gpu_attn(qd, kd, vd, shp)
         assert ms > 0.0
         assert torch.equal(out, ref)

@@ -28,7 +28,10 @@ PEAK_TFLOPS = 2500.0        # MI355X dense bf16 / fp16 matrix-core peak
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 INF = 2147483647
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tra_attn_traffic.json")
-ATTN_SRC = os.path.join(ROOT, "content_adaptive_sparse_amd", "csrc", "tra_attn.hip")
+# the attention kernel and the walk plan it follows (pairing, walks, order):
+# the counters in TRAFFIC_FILE hold for this pair of sources
+ATTN_SRC = [os.path.join(ROOT, "content_adaptive_sparse_amd", "csrc", f)
+            for f in ("tra_attn.hip", "tra_mask.hip")]
 
 
 def log(*a):
@@ -36,8 +39,11 @@ def log(*a):
 
 
 def attn_source_hash():
-    with open(ATTN_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in ATTN_SRC:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload_key):

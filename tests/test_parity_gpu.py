@@ -380,6 +380,10 @@ def test_plan_from_radii(case):
     plan = torch.empty(tra.tra_plan_bytes(T, H, W, heads, 64, maxcnt), dtype=torch.uint8,
                        device="cuda")
     tra.tra_plan_radius(torch.from_numpy(radii).cuda(), T, H, W, heads, 64, r_max, plan)
+    torch.cuda.synchronize()
+    got = plan_pair_table(plan, T, H, W, heads, maxcnt)
+    want = radius_pair_table_model(radii, r_max, T, H, W)
+    assert np.array_equal(got, want), "pair table differs from the radius rule"
     out = torch.full(shp, float("nan"), dtype=torch.float32, device="cuda")
     tra.tra_attn_plan(qd, kd, vd, T, H, W, heads, d, 64, plan, maxcnt, out)
     ref_gpu = gpu_attn(qd, kd, vd, shp, idx, cnt, maxcnt)
@@ -504,6 +508,37 @@ def pair_table_model(cnt, T, H, W):
             if o >= 0 and not good(c[b], c[o]):
                 orph.append(b)
         orph.sort(key=lambda b: -cls(c[b]))  # stable: raster order inside a class
+        items += [(orph[i], orph[i + 1] if i + 1 < len(orph) else -1) for i in range(0, len(orph), 2)]
+        table[h, :len(items)] = items
+    return table
+
+
+def radius_pair_table_model(radii, r_max, T, H, W):
+    """The pair table of a plan built from radii: per head, the vertical pairs
+    whose radii (clamped to [0, r_max]) are equal, in raster order; then the
+    other blocks classed by radius (radii of 127 and more share the top class),
+    largest first, in (frame, tile column, tile row) order inside a class,
+    paired in that order; then (-1, -1) up to the head's slot count."""
+    heads, nb = radii.shape
+    nby, nbx = -(-H // 8), -(-W // 8)
+    npy = (nby + 1) // 2
+    pph = T * npy * nbx
+    table = np.full((heads, pph, 2), -1, dtype=np.int64)
+    for h in range(heads):
+        r = np.clip(radii[h].astype(np.int64), 0, r_max)
+        items, orph = [], []
+        for p in range(pph):
+            t, pr, bx = p // (npy * nbx), (p // nbx) % npy, p % nbx
+            qa = (t * nby + 2 * pr) * nbx + bx
+            qb = qa + nbx if 2 * pr + 1 < nby else -1
+            if qb < 0 or r[qa] == r[qb]:
+                items.append((qa, qb))
+        for b in range(nb):
+            by = (b // nbx) % nby
+            o = b - nbx if by & 1 else (b + nbx if by + 1 < nby else -1)
+            if o >= 0 and r[b] != r[o]:
+                orph.append(b)
+        orph.sort(key=lambda b: (-min(r[b], 127), b // (nby * nbx), b % nbx, (b // nbx) % nby))
         items += [(orph[i], orph[i + 1] if i + 1 < len(orph) else -1) for i in range(0, len(orph), 2)]
         table[h, :len(items)] = items
     return table

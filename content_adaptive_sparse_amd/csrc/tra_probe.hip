@@ -40,12 +40,21 @@ __global__ __launch_bounds__(256) void vmax_kernel(const uint16_t *__restrict__ 
     const int64_t lo = min(n8, gpart * chunk), hi = min(n8, lo + chunk);
     const uint4 *src = reinterpret_cast<const uint4 *>(v + (size_t)h * n);
     uint32_t mx = 0;
-    for (int64_t i = lo + threadIdx.x; i < hi; i += 256) {
-        const uint4 w = src[i];
+    auto fold = [&](const uint4 &w) {
         const uint32_t a[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) mx = max(mx, max(a[e] & 0x7fffu, (a[e] >> 16) & 0x7fffu));
+    };
+    // four loads in flight per thread, then the remainder
+    int64_t i = lo + threadIdx.x;
+    for (; i + 3 * 256 < hi; i += 4 * 256) {
+        const uint4 w0 = src[i], w1 = src[i + 256], w2 = src[i + 512], w3 = src[i + 768];
+        fold(w0);
+        fold(w1);
+        fold(w2);
+        fold(w3);
     }
+    for (; i < hi; i += 256) fold(src[i]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;

@@ -1,7 +1,8 @@
 // C ABI of the entropy-radius block-sparse attention library: argument
 // validation, tile-grid arithmetic, stream-ordered scratch memory and the
-// launch sequence probe -> mask -> attention.  Declarations and the contract
-// of every entry point are in include/tra_attention.h.
+// launch sequences (probe -> walk plan -> attention, and the staged calls).
+// Declarations and the contract of every entry point are in
+// include/tra_attention.h.
 #include "tra_attention.h"
 
 #include <hip/hip_runtime.h>
@@ -361,8 +362,10 @@ static hipError_t plan_walk(const int32_t *idx, const int32_t *cnt, const float 
     return e;
 }
 
-// The walk plan of the radius mask's lists, taken straight from the radii
-// (pair table, walks, order; the same plan plan_walk makes of the lists).
+// The walk plan of the radius mask's lists, taken straight from the radii:
+// the radius pair table, the union of each pair's two key boxes, the order.
+// Each block meets the same entries in the same order as along plan_walk of
+// the lists (the pairing differs; results do not).
 static hipError_t plan_walk_radius(const int32_t *radius, int r_max, int64_t maxcnt,
                                    const tra::Grid &g, int heads, int2 *pairs, int32_t *ulist,
                                    int32_t *ulen, int32_t *order, hipStream_t stream) {

@@ -75,7 +75,8 @@ namespace {
 // first and in raster order inside a class, and paired in that order, so that
 // a block that keeps every key block (binary routing) shares its walk with
 // another such block instead of idling half the workgroup beside a short
-// list.  One workgroup of 1024 threads per head writes the head's
+// list.  (A plan built from radii pairs by radius instead; see pair_kernel.)
+// One workgroup of 1024 threads per head writes the head's
 // pairs_per_head item slots: the kept vertical pairs in raster order, then the
 // re-paired ones, then unused slots (-1, -1).  The counting sort is stable:
 // a chunk's ranks inside each class come from a 1024-bit membership mask.
@@ -409,9 +410,9 @@ __global__ __launch_bounds__(64 * kUnionWaves) void union_kernel(
 
 // The walk of a work item straight from the two blocks' radii: the union of
 // their key boxes in ascending block order, each entry (block << 2) | sides --
-// exactly what union_kernel makes of the radius mask's lists, without the
-// lists.  One wave64 per item scans the frames either box touches, 64
-// candidate blocks at a time, and compacts with a ballot.
+// exactly what union_kernel makes of the radius mask's lists for the same two
+// blocks, without the lists.  One wave64 per item scans the frames either box
+// touches, 64 candidate blocks at a time, and compacts with a ballot.
 __global__ __launch_bounds__(64 * kUnionWaves) void radius_walk_kernel(
     const int32_t *__restrict__ radius, int r_max, Grid g, int64_t items, int pairs_per_head,
     const int2 *__restrict__ pairs, int64_t ustride, int32_t *__restrict__ ulist,

@@ -113,6 +113,12 @@ __device__ int64_t block_exclusive_scan(int64_t v, int64_t *wave_sums, int64_t *
     return r;
 }
 
+// Lanes below this one whose ballot bit is set.
+__device__ __forceinline__ int lanes_before(uint64_t bal) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+}
+
 constexpr int kPairThreads = kScanThreads;
 constexpr int kPairClasses = 128;
 
@@ -269,6 +275,141 @@ __global__ __launch_bounds__(kPairThreads) void pair_kernel(const int32_t *__res
     for (int64_t i = used + tid; i < pph; i += kPairThreads) out[i] = make_int2(-1, -1);
 }
 
+// The pair table of the radius mask's lists, from the radii, frame by frame
+// (the limits: at most kPairMaxPlane tiles per frame, kPairMaxFrames frames
+// and kPairMaxOrphans blocks; pair_kernel's radius mode otherwise).  Vertical
+// neighbours (tile rows 2 p, 2 p + 1) stay together when their radii are equal
+// (their key boxes then differ by at most one tile row); the other blocks of a
+// frame are ordered by radius, largest first, then tile column, then tile row,
+// the frames one after another, and paired in that order, so that a pair's two
+// boxes are one box shifted by a tile or two.  The items are listed frame by
+// frame -- each frame's kept pairs in raster order, then the re-paired items
+// whose first block lies in that frame -- so that the work order's contiguous
+// XCD ranges hold neighbouring frames and their key tiles share each XCD's L2.
+// One workgroup of 1024 threads per head; one wave per frame at a time.
+constexpr int kPairMaxPlane = 256;
+constexpr int kPairMaxFrames = 1024;
+constexpr int kPairMaxOrphans = 8192;
+constexpr int kNoKey = 0x7fffffff;
+
+__global__ __launch_bounds__(kPairThreads) void pair_radius_kernel(const int32_t *__restrict__ radius,
+                                                                  int r_max, Grid g, int pph,
+                                                                  int2 *__restrict__ pairs) {
+    constexpr int kWaves = kPairThreads / 64;
+    __shared__ int kcnt[kPairMaxFrames + 1];  // kept items per frame, then their prefix
+    __shared__ int ocnt[kPairMaxFrames + 1];  // re-paired blocks per frame, then their prefix
+    __shared__ int okey[kWaves][kPairMaxPlane];
+    __shared__ int oseq[kPairMaxOrphans];  // the re-paired blocks in pairing order
+    __shared__ int64_t wave_sums[kWaves];
+    __shared__ int64_t total_sh;
+    const int h = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int plane = g.nby * g.nbx, npy = (g.nby + 1) / 2, fslots = npy * g.nbx;
+    const int32_t *rh = radius + (int64_t)h * g.nb;
+    int2 *out = pairs + (int64_t)h * pph;
+    auto rad = [&](int b) -> int {
+        const int32_t r = rh[b];
+        return r < 0 ? 0 : (r > r_max ? r_max : r);
+    };
+    // block j = y nbx + x of frame f: its re-pairing key, or kNoKey when it
+    // stays with its vertical neighbour (equal radii) or has none
+    auto okey_of = [&](int f, int j) -> int {
+        const int y = j / g.nbx, x = j - y * g.nbx;
+        if ((y ^ 1) >= g.nby) return kNoKey;
+        const int r = rad(f * plane + j);
+        if (r == rad(f * plane + (y ^ 1) * g.nbx + x)) return kNoKey;
+        return (kPairClasses - 1 - min(r, kPairClasses - 1)) * plane + x * g.nby + y;
+    };
+    // pair slot p of frame f (tile-row pair p / nbx, column p % nbx)
+    auto slot_blocks = [&](int f, int p, int &qa, int &qb) {
+        const int pr = p / g.nbx, x = p - pr * g.nbx;
+        qa = (f * g.nby + 2 * pr) * g.nbx + x;
+        qb = 2 * pr + 1 < g.nby ? qa + g.nbx : -1;
+    };
+    auto kept_slot = [&](int f, int p) -> bool {
+        int qa, qb;
+        slot_blocks(f, p, qa, qb);
+        return qb < 0 || rad(qa) == rad(qb);
+    };
+    // 1. per frame: kept items and re-paired blocks
+    for (int f0 = 0; f0 < g.T; f0 += kWaves) {
+        const int f = f0 + wave;
+        if (f < g.T) {
+            int kc = 0, oc = 0;
+            for (int p0 = 0; p0 < fslots; p0 += 64)
+                kc += __popcll(__ballot(p0 + lane < fslots && kept_slot(f, p0 + lane)));
+            for (int j0 = 0; j0 < plane; j0 += 64)
+                oc += __popcll(__ballot(j0 + lane < plane && okey_of(f, j0 + lane) != kNoKey));
+            if (lane == 0) {
+                kcnt[f] = kc;
+                ocnt[f] = oc;
+            }
+        }
+    }
+    __syncthreads();
+    // 2. exclusive prefixes over the frames (one frame per thread)
+    {
+        const int64_t kv = tid < g.T ? kcnt[tid] : 0, ov = tid < g.T ? ocnt[tid] : 0;
+        const int64_t kx = block_exclusive_scan(kv, wave_sums, &total_sh);
+        const int ktot = (int)total_sh;
+        const int64_t ox = block_exclusive_scan(ov, wave_sums, &total_sh);
+        const int otot = (int)total_sh;
+        if (tid < g.T) {
+            kcnt[tid] = (int)kx;
+            ocnt[tid] = (int)ox;
+        }
+        if (tid == 0) {
+            kcnt[g.T] = ktot;
+            ocnt[g.T] = otot;
+        }
+    }
+    __syncthreads();
+    // 3. the re-paired blocks in order: frame, then key (rank among the frame's keys)
+    for (int f0 = 0; f0 < g.T; f0 += kWaves) {
+        const int f = f0 + wave;
+        if (f < g.T)
+            for (int j = lane; j < plane; j += 64) okey[wave][j] = okey_of(f, j);
+        __syncthreads();
+        if (f < g.T) {
+            for (int j = lane; j < plane; j += 64) {
+                const int my = okey[wave][j];
+                if (my == kNoKey) continue;
+                int rank = 0;
+                for (int k = 0; k < plane; ++k) rank += okey[wave][k] < my ? 1 : 0;
+                oseq[ocnt[f] + rank] = f * plane + j;
+            }
+        }
+        __syncthreads();
+    }
+    // 4. the items, frame by frame: a frame's kept pairs, then the re-paired
+    //    items whose first block lies in it
+    const int norph = ocnt[g.T];
+    const int nitems_orph = (norph + 1) / 2;
+    const int used = kcnt[g.T] + nitems_orph;
+    for (int f0 = 0; f0 < g.T; f0 += kWaves) {
+        const int f = f0 + wave;
+        if (f >= g.T) continue;
+        int base = kcnt[f] + (ocnt[f] + 1) / 2;
+        for (int p0 = 0; p0 < fslots; p0 += 64) {
+            const int p = p0 + lane;
+            const bool keep = p < fslots && kept_slot(f, p);
+            const uint64_t bal = __ballot(keep);
+            if (keep) {
+                int qa, qb;
+                slot_blocks(f, p, qa, qb);
+                out[base + lanes_before(bal)] = make_int2(qa, qb);
+            }
+            base += __popcll(bal);
+        }
+    }
+    for (int j = tid; j < nitems_orph; j += kPairThreads) {
+        const int first = oseq[2 * j];
+        const int second = 2 * j + 1 < norph ? oseq[2 * j + 1] : -1;
+        const int f = first / plane;
+        out[kcnt[f + 1] + j] = make_int2(first, second);
+    }
+    for (int64_t i = used + tid; i < pph; i += kPairThreads) out[i] = make_int2(-1, -1);
+}
+
 // Union of the two key lists of a work item (a pair of query blocks from the
 // pair table), the walk the attention kernel takes: entries
 // (block << 2) | sides, bit 0 set when the upper block keeps the block, bit 1
@@ -282,10 +423,6 @@ __global__ __launch_bounds__(kPairThreads) void pair_kernel(const int32_t *__res
 // attention exact: every query block still sees exactly its own entries.
 constexpr int kUnionWaves = 4;
 
-__device__ __forceinline__ int lanes_before(uint64_t bal) {
-    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                          __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-}
 
 __device__ int lower_bound_list(const int32_t *l, int n, int x) {
     int lo = 0, hi = n;
@@ -631,8 +768,12 @@ hipError_t launch_pair(const int32_t *cnt, int64_t maxcnt, const Grid &g, int he
 
 hipError_t launch_pair_radius(const int32_t *radius, int r_max, int64_t maxcnt, const Grid &g,
                               int heads, int2 *pairs, hipStream_t s) {
-    hipLaunchKernelGGL(pair_kernel, dim3((unsigned)heads), dim3(kPairThreads), 0, s, nullptr,
-                       radius, r_max, maxcnt, g, pairs_per_head(g), pairs);
+    if (g.nby * g.nbx <= kPairMaxPlane && g.T <= kPairMaxFrames && g.nb <= kPairMaxOrphans)
+        hipLaunchKernelGGL(pair_radius_kernel, dim3((unsigned)heads), dim3(kPairThreads), 0, s,
+                           radius, r_max, g, pairs_per_head(g), pairs);
+    else
+        hipLaunchKernelGGL(pair_kernel, dim3((unsigned)heads), dim3(kPairThreads), 0, s, nullptr,
+                           radius, r_max, maxcnt, g, pairs_per_head(g), pairs);
     return hipGetLastError();
 }
 

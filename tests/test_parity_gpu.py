@@ -351,15 +351,17 @@ def test_plan_reuse_across_steps():
         assert_close(out.cpu().numpy().reshape(-1, d)[rows], ref, f"plan reuse step {step}")
 
 
-@pytest.mark.parametrize("case", ["probe", "random", "routing"])
+@pytest.mark.parametrize("case", ["probe", "random", "routing", "wide"])
 def test_plan_from_radii(case):
     # The walk plan built straight from radii (tra_plan_radius, the plan
     # tra_attention builds: its own pairing, no lists) gives the same bits as
     # tra_attn on tra_mask's lists of the same radii -- every block meets its own
     # key blocks in ascending order whoever shares its walk.  Random radii include
     # negative values and values above r_max (both clamped like tra_mask clamps
-    # them); "routing" is binary routing (radius 1 or TRA_RADIUS_INF).
-    T, H, W, heads, d = (5, 29, 43, 3, 128) if case != "routing" else (6, 30, 52, 2, 64)
+    # them); "routing" is binary routing (radius 1 or TRA_RADIUS_INF); "wide"
+    # has more than 256 tiles per frame (the pairing without frame order).
+    T, H, W, heads, d = {"routing": (6, 30, 52, 2, 64), "wide": (3, 136, 144, 1, 64)}.get(
+        case, (5, 29, 43, 3, 128))
     shp = (heads, T, H, W, d)
     print(f"[case] plan from radii {shp} {case}", flush=True)
     q, k, v = ti.make_inputs(T, H, W, heads, d, seed=12, family=36)
@@ -369,7 +371,7 @@ def test_plan_from_radii(case):
     if case == "probe":
         r_max = 4
         _, radii = gpu_probe(qd, kd, shp, 1, r_max)
-    elif case == "random":
+    elif case in ("random", "wide"):
         r_max = 3
         radii = rng.integers(-2, 6, size=(heads, nb)).astype(np.int32)
     else:
@@ -514,32 +516,51 @@ def pair_table_model(cnt, T, H, W):
 
 
 def radius_pair_table_model(radii, r_max, T, H, W):
-    """The pair table of a plan built from radii: per head, the vertical pairs
-    whose radii (clamped to [0, r_max]) are equal, in raster order; then the
-    other blocks classed by radius (radii of 127 and more share the top class),
-    largest first, in (frame, tile column, tile row) order inside a class,
-    paired in that order; then (-1, -1) up to the head's slot count."""
+    """The pair table of a plan built from radii (radii clamped to [0, r_max];
+    radii of 127 and more rank alike).  Up to 256 tiles per frame, 1024 frames
+    and 8192 blocks: vertical pairs whose radii are equal stay together; the
+    other blocks are taken frame by frame, inside a frame by radius (largest
+    first), tile column, tile row, and paired in that order; the items are
+    listed frame by frame, each frame's kept pairs in raster order, then the
+    re-paired items whose first block lies in it; then (-1, -1) up to the head's
+    slot count.  Larger layers: the kept pairs in raster order, then the other
+    blocks by radius (largest first) in (frame, column, row) order, paired."""
     heads, nb = radii.shape
     nby, nbx = -(-H // 8), -(-W // 8)
-    npy = (nby + 1) // 2
+    plane, npy = nby * nbx, (nby + 1) // 2
     pph = T * npy * nbx
+    by_frame = plane <= 256 and T <= 1024 and nb <= 8192
     table = np.full((heads, pph, 2), -1, dtype=np.int64)
     for h in range(heads):
         r = np.clip(radii[h].astype(np.int64), 0, r_max)
-        items, orph = [], []
-        for p in range(pph):
-            t, pr, bx = p // (npy * nbx), (p // nbx) % npy, p % nbx
-            qa = (t * nby + 2 * pr) * nbx + bx
-            qb = qa + nbx if 2 * pr + 1 < nby else -1
-            if qb < 0 or r[qa] == r[qb]:
-                items.append((qa, qb))
-        for b in range(nb):
-            by = (b // nbx) % nby
-            o = b - nbx if by & 1 else (b + nbx if by + 1 < nby else -1)
-            if o >= 0 and r[b] != r[o]:
-                orph.append(b)
-        orph.sort(key=lambda b: (-min(r[b], 127), b // (nby * nbx), b % nbx, (b // nbx) % nby))
-        items += [(orph[i], orph[i + 1] if i + 1 < len(orph) else -1) for i in range(0, len(orph), 2)]
+        kept = [[] for _ in range(T)]
+        orph = []
+        for f in range(T):
+            for p in range(npy * nbx):
+                pr, x = divmod(p, nbx)
+                qa = (f * nby + 2 * pr) * nbx + x
+                qb = qa + nbx if 2 * pr + 1 < nby else -1
+                if qb < 0 or r[qa] == r[qb]:
+                    kept[f].append((qa, qb))
+            for j in range(plane):
+                y, x = divmod(j, nbx)
+                b = f * plane + j
+                if (y ^ 1) < nby and r[b] != r[f * plane + (y ^ 1) * nbx + x]:
+                    orph.append(b)
+        if by_frame:
+            orph.sort(key=lambda b: (b // plane, -min(r[b], 127), b % nbx, (b // nbx) % nby))
+        else:
+            orph.sort(key=lambda b: (-min(r[b], 127), b // plane, b % nbx, (b // nbx) % nby))
+        pitems = [(orph[i], orph[i + 1] if i + 1 < len(orph) else -1) for i in range(0, len(orph), 2)]
+        if by_frame:
+            items, j = [], 0
+            for f in range(T):
+                items += kept[f]
+                while j < len(pitems) and pitems[j][0] // plane == f:
+                    items.append(pitems[j])
+                    j += 1
+        else:
+            items = [it for f in range(T) for it in kept[f]] + pitems
         table[h, :len(items)] = items
     return table
 

@@ -400,12 +400,22 @@ def test_plan_from_radii(case):
     assert_close(out.cpu().numpy().reshape(-1, d)[rows], ref, f"plan from radii ({case})")
 
 
+def order_class(n):
+    """Length class of the work order: the length below 4, else two per octave."""
+    n = int(n)
+    if n <= 3:
+        return n
+    e = n.bit_length() - 1
+    return 2 * e + ((n >> (e - 1)) & 1)
+
+
 @pytest.mark.parametrize("case", ["balanced", "capped", "many"])
 def test_work_order_ranges(case):
     # The work order deals the walk items to eight XCD ranges: contiguous raster
     # ranges cut at equal shares of the total work (walk length + 4 per item),
-    # each of at most cap = 2 ceil(items / 8) items, taken longest first into
-    # grid slots 8 k + x, -1 past a range's end.  Every item appears once.  The
+    # each of at most cap = 2 ceil(items / 8) items, taken by length class
+    # (two per octave, longest first; item order inside a class) into grid
+    # slots 8 k + x, -1 past a range's end.  Every item appears once.  The
     # skewed case puts nearly all the work in the first items, so equal-work
     # cuts would leave the later ranges above the cap: the cap moves the cuts.
     # "many" has more than 8192 items (more than eight per thread of the order
@@ -455,7 +465,11 @@ def test_work_order_ranges(case):
         assert n <= cap, f"range {x} above the cap"
         assert np.array_equal(np.sort(col[:n]), np.arange(lo, hi)), f"range {x}"
         assert (col[n:] == -1).all(), f"range {x}: slots past the end"
-        assert (np.diff(ulen[col[:n]]) <= 0).all(), f"range {x}: not longest first"
+        # by length class (two per octave), longest class first, item order inside
+        cls = np.array([order_class(v) for v in np.clip(ulen[col[:n]], 0, min(2 * maxcnt, 8191))])
+        step = np.diff(cls)
+        assert (step <= 0).all(), f"range {x}: not longest class first"
+        assert (np.diff(col[:n])[step == 0] > 0).all(), f"range {x}: not item order in a class"
         works.append(int(cost[lo:hi].sum()))
     print(f"[order] items {items} cap {cap} range work {works} mean {total / 8:.0f} "
           f"clamped {clamped}", flush=True)

@@ -330,7 +330,7 @@ def main():
         torch.cuda.synchronize()
         cnn = cn.cpu().numpy()
         p = int(cnn.sum())
-        ta = attn_time_radii(rd, INF)
+        ta = attn_time(ix, cn, nb)
         routing = {"dense_blocks": round(float((rr == INF).mean()), 4), "local_radius": 1,
                    "density": round(p / (heads * nb * nb), 4),
                    "list_len_min_mean_max": [int(cnn.min()), round(float(cnn.mean()), 1), int(cnn.max())],

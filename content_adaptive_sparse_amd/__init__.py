@@ -26,7 +26,7 @@ __all__ = [
 ]
 
 TRA_RADIUS_INF = 2147483647
-KERNEL_KINDS = ("pack_pool", "entropy", "mask", "attn", "fill", "order", "union",
+KERNEL_KINDS = ("pack_pool", "entropy", "mask", "attn", "fill", "order", "walk",
                 "token_entropy", "token_mask", "sip", "vmax", "pair")
 
 _lib = None

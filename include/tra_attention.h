@@ -364,8 +364,8 @@ enum tra_kernel_kind {
     TRA_KERNEL_MASK = 2,      /* radius -> key-block lists */
     TRA_KERNEL_ATTN = 3,      /* block-sparse attention */
     TRA_KERNEL_FILL = 4,      /* dense-mode radius fill */
-    TRA_KERNEL_ORDER = 5,     /* work order: equal-work XCD ranges, longest first */
-    TRA_KERNEL_UNION = 6,     /* union walk of each pair of query blocks' lists */
+    TRA_KERNEL_ORDER = 5,     /* work order: equal-work XCD ranges, longest class first */
+    TRA_KERNEL_UNION = 6,     /* walk of each work item: union of its two lists, or from the radii */
     TRA_KERNEL_TOKEN_ENTROPY = 7, /* per-token entropy and base radius (warm-up) */
     TRA_KERNEL_TOKEN_MASK = 8,    /* token-disk voting lists */
     TRA_KERNEL_SIP = 9,           /* sampled lists with inverse-inclusion weights */

@@ -138,6 +138,60 @@ def test_weighted_attention_with_zero_weights_is_tra_attn():
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_weighted_walk_cases(d):
+    # Weighted walks of caller lists on a grid with edge tiles (20 rows: the
+    # last tile row holds 4 real rows; 44 columns: 4 real columns in the last
+    # tile column): empty lists (zeros), duplicates (each occurrence counts
+    # with its own weight), entries outside [0, nb) skipped, counts beyond
+    # maxcnt clamped, descending and shuffled lists, lists longer than one and
+    # two 64-entry windows, weights of both signs.  Every output row against
+    # the fp64 oracle.
+    T, H, W, heads = 3, 20, 44, 2
+    shape = (heads, T, H, W, d)
+    print(f"[case] weighted walks {shape}", flush=True)
+    q, k, v = ti.random_qkv(T, H, W, heads, d, seed=31)
+    nb = tra.tra_grid(T, H, W)[2]
+    maxcnt = 150
+    rng = np.random.default_rng(32)
+    idx = np.full((heads, nb, maxcnt), -1, dtype=np.int32)
+    cnt = np.zeros((heads, nb), dtype=np.int32)
+    lw = np.zeros((heads, nb, maxcnt), dtype=np.float32)
+    for h in range(heads):
+        for b in range(nb):
+            kind = (h * nb + b) % 7
+            if kind == 0:
+                continue  # empty list
+            if kind == 1:  # ascending, unique
+                row = np.sort(rng.choice(nb, size=rng.integers(1, nb + 1), replace=False))
+            elif kind == 2:  # descending
+                row = np.sort(rng.choice(nb, size=rng.integers(1, nb + 1), replace=False))[::-1]
+            elif kind == 3:  # duplicates, shuffled, past two windows
+                row = rng.integers(0, nb, size=rng.integers(129, maxcnt + 1))
+            elif kind == 4:  # entries outside [0, nb) among valid ones
+                row = rng.integers(-4, nb + 4, size=rng.integers(2, 80))
+                row[0] = b
+            elif kind == 5:  # count beyond maxcnt: clamped
+                row = rng.integers(0, nb, size=maxcnt)
+                cnt[h, b] = maxcnt + 17
+            else:  # own block only
+                row = np.array([b])
+            idx[h, b, :len(row)] = row
+            cnt[h, b] = max(cnt[h, b], len(row))
+            lw[h, b, :len(row)] = rng.uniform(-1.0, 3.0, size=len(row))
+    out = torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
+    tra.tra_attn_weighted(dev16(q), dev16(k), dev16(v), T, H, W, heads, d, 64,
+                          torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(),
+                          torch.from_numpy(lw).cuda(), maxcnt, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(-1, d)
+    rows = np.arange(heads * T * H * W)
+    ref = oracle.attention_lists_rows(q, k, v, idx, cnt, rows, lw=lw.astype(np.float64))
+    assert_close(got, ref, f"weighted walks d={d}")
+    empty = np.abs(ref).sum(axis=1) == 0
+    assert empty.any() and (got[empty] == 0).all()
+
+
 def test_sip_wan_layer_sampled():
     c = ti.WORKLOADS[ti.WAN13B_81F]
     shape = (c.heads, c.T, c.H, c.W, c.d)

@@ -15,6 +15,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -38,11 +39,18 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+_COMMENTS = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+
+
 def attn_source_hash():
+    """sha256[:16] of the attention kernel and walk-plan sources with comments
+    and white space removed: an edited comment keeps the counters valid, any
+    change of code voids them."""
     h = hashlib.sha256()
     for path in ATTN_SRC:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            code = _COMMENTS.sub(" ", f.read())
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

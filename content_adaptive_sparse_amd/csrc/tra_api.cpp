@@ -341,7 +341,8 @@ int tra_mask(const int32_t *radius, int T, int H, int W, int heads, int block, i
 }
 
 // The attention walk of the lists: the pair table, the union of each pair's
-// two lists, then the longest-first order of the pairs.
+// two lists, then the work order of the pairs (XCD ranges, longest length
+// class first).
 static hipError_t plan_walk(const int32_t *idx, const int32_t *cnt, const float *lw,
                             int64_t maxcnt, const tra::Grid &g, int heads, int2 *pairs,
                             int32_t *ulist, int32_t *ulen, float2 *ubias, int32_t *order,

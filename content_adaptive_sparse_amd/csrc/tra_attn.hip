@@ -74,8 +74,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     // on different XCDs; every XCD is given a contiguous range of items so its
     // L2 sees neighbouring query blocks.  With a work order (lists of unequal
     // length) the ranges hold equal shares of the total work and each is taken
-    // longest first; without one (dense mode: equal work) the ranges hold equal
-    // item counts in raster order.
+    // by walk length class, longest class first; without one (dense mode: equal
+    // work) the ranges hold equal item counts in raster order.
     const int64_t total = (int64_t)heads * pairs_per_head;
     int64_t item;
     if (order) {

@@ -124,9 +124,9 @@ hipError_t launch_sip(const float *logits, const float *u, const Grid &g, int he
 inline int64_t walk_items(const Grid &g, int heads) {
     return ((int64_t)heads * pairs_per_head(g) + 7) / 8 * 8;
 }
-// XCD-aware, longest-first order of the attention work items: eight contiguous
-// ranges of equal work, each of at most order_range_cap items (twice the
-// average count); order holds order_slots(g, heads) = 8 x cap grid slots (-1:
+// XCD-aware order of the attention work items: eight contiguous ranges of
+// equal work, each of at most order_range_cap items (twice the average count)
+// and taken by walk length class, longest class first; order holds order_slots(g, heads) = 8 x cap grid slots (-1:
 // no item), and the attention launch has one workgroup per slot (an empty
 // slot's workgroup exits at once; empty slots come last on their XCD).
 inline int64_t order_range_cap(const Grid &g, int heads) {

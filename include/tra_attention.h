@@ -307,10 +307,12 @@ int tra_attn_plan(const void *q, const void *k, const void *v, int T, int H, int
  * The walk plan of the radius mask's lists built straight from the radii, as
  * tra_attention builds it (Token Radius Attention ..., "The TRA Pipeline:
  * Fused CUDA Kernels" -- radius comparison and block pruning -- and
- * "Cross-Step Reuse"): no lists are written; vertical neighbours of equal
- * radius share a work item, the other blocks are classed by radius (largest
- * first) and paired in (frame, tile column, tile row) order inside a class;
- * each item's walk is the union of its two blocks' key boxes.  Every query
+ * "Cross-Step Reuse"): no lists are written; frame by frame, vertical
+ * neighbours of equal radius share a work item and the frame's other blocks
+ * are paired in (radius descending, tile column, tile row) order, the items
+ * listed frame after frame (grids beyond 256 tiles per frame, 1024 frames or
+ * 8192 blocks per head take the same rule over the whole head); each item's
+ * walk is the union of its two blocks' key boxes.  Every query
  * block meets the same key blocks in the same order as along tra_plan of
  * tra_mask's lists for these radii, so tra_attn_plan along either plan gives
  * the same results.

@@ -350,7 +350,8 @@ static hipError_t plan_walk(const int32_t *idx, const int32_t *cnt, const float 
     hipError_t e;
     {
         ProfScope p(TRA_KERNEL_PAIR, stream);
-        e = tra::launch_pair(cnt, maxcnt, g, heads, pairs, stream);
+        // the work order's memory holds the candidate walk lengths meanwhile
+        e = tra::launch_pair(idx, cnt, maxcnt, g, heads, pairs, order, stream);
     }
     if (e == hipSuccess) {
         ProfScope p(TRA_KERNEL_UNION, stream);

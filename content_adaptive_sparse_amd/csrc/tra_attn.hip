@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     const int2 *__restrict__ pairs, const int32_t *__restrict__ ulist,
     const int32_t *__restrict__ ulen,
     const float2 *__restrict__ ubias, int64_t ustride, const int32_t *__restrict__ order, Grid g,
-    int heads, int pairs_per_head, int per_xcd, FastDiv div_nbx, FastDiv div_nby,
+    int heads, int items_per_head, int per_xcd, FastDiv div_nbx, FastDiv div_nby,
     float *__restrict__ out, float scale_log2, EntropyOut eo) {
     static_assert(!(WEIGHTED && ENTROPY), "entropy of unweighted rows only");
     constexpr int KS = D / 16;                  // k-steps of Q.K^T
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     // length) the ranges hold equal shares of the total work and each is taken
     // by walk length class, longest class first; without one (dense mode: equal
     // work) the ranges hold equal item counts in raster order.
-    const int64_t total = (int64_t)heads * pairs_per_head;
+    const int64_t total = (int64_t)heads * items_per_head;
     int64_t item;
     if (order) {
         item = ((const const_i32_t *)order)[blockIdx.x];  // one slot per workgroup
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
         item = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     }
     if (item >= total) return;
-    const int h = (int)(item / pairs_per_head);
+    const int h = (int)(item / items_per_head);
     int blk[2];
     if (pairs) {
         const int2 pr = reinterpret_cast<const int2 *>(pairs)[item];
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
         blk[1] = __builtin_amdgcn_readfirstlane(pr.y);
         if (blk[0] < 0) return;  // an unused slot of the pair table
     } else {
-        pair_blocks((int)(item % pairs_per_head), g, blk[0], blk[1]);
+        pair_blocks((int)(item % items_per_head), g, blk[0], blk[1]);
     }
 
     const int tid = threadIdx.x;
@@ -475,7 +475,8 @@ hipError_t launch_attn(int D, const uint16_t *q, const uint16_t *kt, const uint1
                        const int32_t *ulen, const float2 *ubias, int64_t ustride,
                        const int32_t *order, const Grid &g, int heads, float *out, hipStream_t s,
                        const EntropyOut *entropy) {
-    const int pph = pairs_per_head(g);
+    // items per head: the plan's slots, or the vertical pairs of dense mode
+    const int pph = pairs ? plan_slots_per_head(g) : pairs_per_head(g);
     const int64_t total = (int64_t)heads * pph;
     const int per_xcd = (int)((total + 7) / 8);
     // one workgroup per slot of the work order, or per item in XCD ranges

@@ -86,6 +86,24 @@ __host__ __device__ inline void pair_blocks(int p, const Grid &g, int &qa, int &
     qa = (t * g.nby + 2 * pr) * g.nbx + bx;
     qb = 2 * pr + 1 < g.nby ? qa + g.nbx : -1;
 }
+// Temporal pairs: pair p of a head is the tile p % plane of frames 2 (p / plane)
+// and 2 (p / plane) + 1 (the second absent when T is odd and that frame is the
+// last).  Lists voted by query tokens (the token policy) coincide more in time
+// than across tile rows; a list plan takes them when they save steps.
+__host__ __device__ inline int temporal_pairs_per_head(const Grid &g) {
+    return (g.T + 1) / 2 * (g.nby * g.nbx);
+}
+__host__ __device__ inline void temporal_pair_blocks(int p, const Grid &g, int &qa, int &qb) {
+    const int plane = g.nby * g.nbx;
+    const int tp = p / plane;
+    qa = 2 * tp * plane + (p - tp * plane);
+    qb = 2 * tp + 1 < g.T ? qa + plane : -1;
+}
+// Item slots per head of a walk plan: room for either kind of pairs.
+__host__ __device__ inline int plan_slots_per_head(const Grid &g) {
+    const int v = pairs_per_head(g), t = temporal_pairs_per_head(g);
+    return v > t ? v : t;
+}
 
 // Union walk of each work item (see tra_mask.hip): ulist holds, at row stride
 // union_stride(maxcnt), entries (block << 2) | sides, ulen their counts; with
@@ -96,12 +114,17 @@ hipError_t launch_union(const int32_t *idx, const int32_t *cnt, const float *lw,
                         const Grid &g, int heads, const int2 *pairs, int32_t *ulist, int32_t *ulen,
                         float2 *ubias, hipStream_t s);
 
-// Pair table of a list set (see tra_mask.hip): for every head, pairs_per_head
-// item slots (qa, qb) -- vertical neighbours whose list lengths are within a
-// factor of two, the other blocks re-paired by length class -- then unused
-// slots (-1, -1); qb = -1 marks a single block.
-hipError_t launch_pair(const int32_t *cnt, int64_t maxcnt, const Grid &g, int heads, int2 *pairs,
-                       hipStream_t s);
+// Pair table of a list set (see tra_mask.hip): for every head,
+// plan_slots_per_head item slots (qa, qb) -- neighbours whose list lengths are
+// within a factor of two, the other blocks re-paired by length class -- then
+// unused slots (-1, -1); qb = -1 marks a single block.  The neighbours are
+// vertical, or temporal in a head whose temporal pairs' walks take at least 5%
+// fewer steps per list entry (judged on every fourth pair of either kind).  scratch:
+// heads (pairs_per_head + temporal_pairs_per_head) int32 of device memory for
+// those walk lengths (any memory the caller overwrites afterwards: the plan's
+// work order).
+hipError_t launch_pair(const int32_t *idx, const int32_t *cnt, int64_t maxcnt, const Grid &g,
+                       int heads, int2 *pairs, int32_t *scratch, hipStream_t s);
 
 // The same two steps for the radius mask's lists taken straight from the radii
 // (no lists): the pair table from the radii (vertical neighbours of equal
@@ -122,7 +145,7 @@ hipError_t launch_sip(const float *logits, const float *u, const Grid &g, int he
 
 // Per-item arrays of a walk plan (lengths, walks) hold walk_items(g, heads) rows.
 inline int64_t walk_items(const Grid &g, int heads) {
-    return ((int64_t)heads * pairs_per_head(g) + 7) / 8 * 8;
+    return ((int64_t)heads * plan_slots_per_head(g) + 7) / 8 * 8;
 }
 // XCD-aware order of the attention work items: eight contiguous ranges of
 // equal work, each of at most order_range_cap items (twice the average count)
@@ -130,7 +153,7 @@ inline int64_t walk_items(const Grid &g, int heads) {
 // no item), and the attention launch has one workgroup per slot (an empty
 // slot's workgroup exits at once; empty slots come last on their XCD).
 inline int64_t order_range_cap(const Grid &g, int heads) {
-    return 2 * (((int64_t)heads * pairs_per_head(g) + 7) / 8);
+    return 2 * (((int64_t)heads * plan_slots_per_head(g) + 7) / 8);
 }
 inline int64_t order_slots(const Grid &g, int heads) { return 8 * order_range_cap(g, heads); }
 hipError_t launch_order(const int32_t *ulen, const Grid &g, int heads, int64_t maxcnt,

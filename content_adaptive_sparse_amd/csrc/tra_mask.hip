@@ -67,19 +67,22 @@ namespace tra {
 namespace {
 
 // Work items: which two query blocks of a head share one attention workgroup
-// (and its copied key/value tiles).  Vertically adjacent blocks (tile rows
-// 2 p and 2 p + 1 of one frame and column: short-axis neighbours, whose lists
-// mostly coincide) stay together when their list lengths are within a factor
-// of two.  The blocks of every other vertical pair are re-paired by length
-// class: sorted by a key of four classes per octave of the length, longest
-// first and in raster order inside a class, and paired in that order, so that
-// a block that keeps every key block (binary routing) shares its walk with
-// another such block instead of idling half the workgroup beside a short
-// list.  (A plan built from radii pairs by radius instead; see pair_kernel.)
-// One workgroup of 1024 threads per head writes the head's
-// pairs_per_head item slots: the kept vertical pairs in raster order, then the
-// re-paired ones, then unused slots (-1, -1).  The counting sort is stable:
-// a chunk's ranks inside each class come from a 1024-bit membership mask.
+// (and its copied key/value tiles).  Neighbouring blocks -- vertically adjacent
+// ones (tile rows 2 p and 2 p + 1 of one frame and column: short-axis
+// neighbours, whose lists mostly coincide), or, in a head whose temporal pairs
+// (one tile in frames 2 p and 2 p + 1) make walks at least 5% shorter in
+// total, temporally adjacent ones (token-voted lists coincide more in time) --
+// stay together when their list lengths are within a factor of two.  The
+// blocks of every other neighbour pair are re-paired by length class: sorted
+// by a key of four classes per octave of the length, longest first and in
+// raster order inside a class, and paired in that order, so that a block that
+// keeps every key block (binary routing) shares its walk with another such
+// block instead of idling half the workgroup beside a short list.  (A plan
+// built from radii pairs by radius instead; see pair_kernel.)  One workgroup
+// of 1024 threads per head writes the head's plan_slots_per_head item slots:
+// the kept neighbour pairs in raster order, then the re-paired ones, then
+// unused slots (-1, -1).  The counting sort is stable: a chunk's ranks inside
+// each class come from a 1024-bit membership mask.
 constexpr int kScanThreads = 1024;
 
 // Exclusive prefix sum of one value per thread over the block (1024 threads):
@@ -121,6 +124,12 @@ __device__ __forceinline__ int lanes_before(uint64_t bal) {
 
 constexpr int kPairThreads = kScanThreads;
 constexpr int kPairClasses = 128;
+// The neighbour direction of a list plan is judged on every kCandidateStride-th
+// candidate pair of a head (pair index 0, 4, 8, ...).
+constexpr int kCandidateStride = 4;
+__host__ __device__ inline int candidates(int pairs) {
+    return (pairs + kCandidateStride - 1) / kCandidateStride;
+}
 
 __device__ __forceinline__ int length_class(int c) {
     const uint32_t x = (uint32_t)(c < 0 ? 0 : c) + 1u;
@@ -166,23 +175,63 @@ __device__ KeyBox key_box(int b, int32_t radius, int r_max, const Grid &g) {
 // the walks' slot efficiency is 0.92 instead of 0.87 with the length rule, and
 // the walks take 6% fewer steps.  (Pairing does not change any result: each
 // block meets its own entries in ascending order whatever its partner.)
+// wlen (list mode): the walk lengths of a sample of every head's vertical,
+// then temporal candidate pairs (candidate_walk_kernel), which choose the
+// neighbours: temporal ones when their sampled walks take at least 5% fewer
+// steps per list entry.
 __global__ __launch_bounds__(kPairThreads) void pair_kernel(const int32_t *__restrict__ cnt,
                                                            const int32_t *__restrict__ radius,
+                                                           const int32_t *__restrict__ wlen,
                                                            int r_max, int64_t maxcnt, Grid g,
-                                                           int pph, int2 *__restrict__ pairs) {
+                                                           int slots, int2 *__restrict__ pairs) {
     __shared__ int64_t wave_sums[kPairThreads / 64];
     __shared__ int64_t total_sh;
     __shared__ int start[kPairClasses], run[kPairClasses];
     __shared__ uint32_t member[kPairClasses][kPairThreads / 32];
     const int h = blockIdx.x, tid = threadIdx.x;
     const int32_t *ch = radius ? radius + (int64_t)h * g.nb : cnt + (int64_t)h * g.nb;
-    int2 *out = pairs + (int64_t)h * pph;
+    int2 *out = pairs + (int64_t)h * slots;
+    const int plane = g.nby * g.nbx;
     auto len = [&](int b) -> int {  // list mode
         const int64_t m = ch[b];
         return (int)(m < 0 ? 0 : (m > maxcnt ? maxcnt : m));
     };
-    // the vertical partner of block b (-1 when its tile row has none)
+    // temporal neighbours when the sampled temporal candidates' walks hold at
+    // least 5% fewer steps per list entry than the vertical ones'
+    bool temporal = false;
+    if (wlen) {
+        const int vs = candidates(pairs_per_head(g)), ts = candidates(temporal_pairs_per_head(g));
+        const int32_t *wv = wlen + (int64_t)h * vs;
+        const int32_t *wt = wlen + (int64_t)gridDim.x * vs + (int64_t)h * ts;
+        int64_t uv = 0, lv = 0, ut = 0, lt = 0;  // walk steps and list entries
+        for (int i = tid; i < vs; i += kPairThreads) {
+            int qa, qb;
+            pair_blocks(i * kCandidateStride, g, qa, qb);
+            uv += wv[i];
+            lv += len(qa) + (qb >= 0 ? len(qb) : 0);
+        }
+        for (int i = tid; i < ts; i += kPairThreads) {
+            int qa, qb;
+            temporal_pair_blocks(i * kCandidateStride, g, qa, qb);
+            ut += wt[i];
+            lt += len(qa) + (qb >= 0 ? len(qb) : 0);
+        }
+        int64_t tot[4];
+        const int64_t part[4] = {uv, lv, ut, lt};
+        for (int j = 0; j < 4; ++j) {
+            block_exclusive_scan(part[j], wave_sums, &total_sh);
+            tot[j] = total_sh;
+        }
+        // ut / lt < 0.95 uv / lv (in double: the products may pass 2^63)
+        temporal = 20.0 * (double)tot[2] * (double)tot[1] < 19.0 * (double)tot[0] * (double)tot[3];
+    }
+    // the neighbour of block b (-1 when its tile row, or frame, has none)
     auto partner = [&](int b) -> int {
+        if (temporal) {
+            const int t = b / plane;
+            const int o = (t & 1) ? b - plane : b + plane;
+            return ((t & 1) || t + 1 < g.T) ? o : -1;
+        }
         const int by = (b / g.nbx) % g.nby;
         const int o = (by & 1) ? b - g.nbx : b + g.nbx;
         return ((by & 1) || by + 1 < g.nby) ? o : -1;
@@ -202,21 +251,24 @@ __global__ __launch_bounds__(kPairThreads) void pair_kernel(const int32_t *__res
         return o >= 0 && !well(b, o);
     };
     // the i-th block of the orphan order: raster, or (frame, column, row) for radii
-    const int plane = g.nby * g.nbx;
     auto block_at = [&](int i) -> int {
         if (!radius) return i;
         const int t = i / plane, rem = i - t * plane;
         const int x = rem / g.nby, y = rem - x * g.nby;
         return (t * g.nby + y) * g.nbx + x;
     };
-    // kept vertical pairs, compacted in raster order
+    // kept neighbour pairs, compacted in raster order
+    const int npairs = temporal ? temporal_pairs_per_head(g) : pairs_per_head(g);
     int64_t kept = 0;
-    for (int p0 = 0; p0 < pph; p0 += kPairThreads) {
+    for (int p0 = 0; p0 < npairs; p0 += kPairThreads) {
         const int p = p0 + tid;
         int qa = -1, qb = -1;
         bool keep = false;
-        if (p < pph) {
-            pair_blocks(p, g, qa, qb);
+        if (p < npairs) {
+            if (temporal)
+                temporal_pair_blocks(p, g, qa, qb);
+            else
+                pair_blocks(p, g, qa, qb);
             keep = qb < 0 || well(qa, qb);
         }
         int64_t tot;
@@ -272,7 +324,7 @@ __global__ __launch_bounds__(kPairThreads) void pair_kernel(const int32_t *__res
     // an odd orphan count leaves the last item single; unused slots after it
     const int64_t used = kept + (norph + 1) / 2;
     if (tid == 0 && (norph & 1)) reinterpret_cast<int *>(out + kept + norph / 2)[1] = -1;
-    for (int64_t i = used + tid; i < pph; i += kPairThreads) out[i] = make_int2(-1, -1);
+    for (int64_t i = used + tid; i < slots; i += kPairThreads) out[i] = make_int2(-1, -1);
 }
 
 // The pair table of the radius mask's lists, from the radii, frame by frame
@@ -293,7 +345,7 @@ constexpr int kPairMaxOrphans = 8192;
 constexpr int kNoKey = 0x7fffffff;
 
 __global__ __launch_bounds__(kPairThreads) void pair_radius_kernel(const int32_t *__restrict__ radius,
-                                                                  int r_max, Grid g, int pph,
+                                                                  int r_max, Grid g, int slots,
                                                                   int2 *__restrict__ pairs) {
     constexpr int kWaves = kPairThreads / 64;
     __shared__ int kcnt[kPairMaxFrames + 1];  // kept items per frame, then their prefix
@@ -305,7 +357,7 @@ __global__ __launch_bounds__(kPairThreads) void pair_radius_kernel(const int32_t
     const int h = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int plane = g.nby * g.nbx, npy = (g.nby + 1) / 2, fslots = npy * g.nbx;
     const int32_t *rh = radius + (int64_t)h * g.nb;
-    int2 *out = pairs + (int64_t)h * pph;
+    int2 *out = pairs + (int64_t)h * slots;
     auto rad = [&](int b) -> int {
         const int32_t r = rh[b];
         return r < 0 ? 0 : (r > r_max ? r_max : r);
@@ -407,7 +459,7 @@ __global__ __launch_bounds__(kPairThreads) void pair_radius_kernel(const int32_t
         const int f = first / plane;
         out[kcnt[f + 1] + j] = make_int2(first, second);
     }
-    for (int64_t i = used + tid; i < pph; i += kPairThreads) out[i] = make_int2(-1, -1);
+    for (int64_t i = used + tid; i < slots; i += kPairThreads) out[i] = make_int2(-1, -1);
 }
 
 // Union of the two key lists of a work item (a pair of query blocks from the
@@ -454,14 +506,14 @@ __device__ bool list_ascending(const int32_t *l, int n, int nb, int lane) {
 // that does not keep the block).
 __global__ __launch_bounds__(64 * kUnionWaves) void union_kernel(
     const int32_t *__restrict__ idx, const int32_t *__restrict__ cnt,
-    const float *__restrict__ lw, int64_t maxcnt, Grid g, int64_t items, int pairs_per_head,
+    const float *__restrict__ lw, int64_t maxcnt, Grid g, int64_t items, int slots,
     const int2 *__restrict__ pairs, int64_t ustride, int32_t *__restrict__ ulist,
     int32_t *__restrict__ ulen, float2 *__restrict__ ubias) {
     constexpr float kLog2e = 1.4426950408889634f;
     const int64_t item = (int64_t)blockIdx.x * kUnionWaves + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (item >= items) return;
-    const int64_t h = item / pairs_per_head;
+    const int64_t h = item / slots;
     const int2 pr = pairs[item];
     const int qa = pr.x, qb = pr.y;
     if (qa < 0) {  // an unused item slot: an empty walk
@@ -545,19 +597,66 @@ __global__ __launch_bounds__(64 * kUnionWaves) void union_kernel(
     if (lane == 0) ulen[item] = n;
 }
 
+// Walk length of a sample of the candidate pairs of a list set -- every
+// kCandidateStride-th vertical pair of each head, then (after all heads) every
+// kCandidateStride-th temporal pair -- as union_kernel makes it: |A| + |B| -
+// |A n B| for strictly ascending lists inside [0, nb), else |A| + |B|.  One
+// wave64 per candidate; pair_kernel sums them per head to choose the
+// neighbours it keeps together.
+__global__ __launch_bounds__(64 * kUnionWaves) void candidate_walk_kernel(
+    const int32_t *__restrict__ idx, const int32_t *__restrict__ cnt, int64_t maxcnt, Grid g,
+    int heads, int32_t *__restrict__ wlen) {
+    const int vs = candidates(pairs_per_head(g)), ts = candidates(temporal_pairs_per_head(g));
+    const int64_t nv = (int64_t)heads * vs, items = nv + (int64_t)heads * ts;
+    const int64_t c = (int64_t)blockIdx.x * kUnionWaves + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (c >= items) return;
+    int64_t h;
+    int qa, qb;
+    if (c < nv) {
+        h = c / vs;
+        pair_blocks((int)(c - h * vs) * kCandidateStride, g, qa, qb);
+    } else {
+        h = (c - nv) / ts;
+        temporal_pair_blocks((int)(c - nv - h * ts) * kCandidateStride, g, qa, qb);
+    }
+    auto len = [&](int b) -> int {
+        if (b < 0) return 0;
+        const int64_t m = cnt[h * g.nb + b];
+        return (int)(m < 0 ? 0 : (m > maxcnt ? maxcnt : m));
+    };
+    const int a = len(qa), b = len(qb);
+    const int32_t *A = idx + (h * g.nb + qa) * maxcnt;
+    const int32_t *B = qb >= 0 ? idx + (h * g.nb + qb) * maxcnt : A;
+    int n = a + b;
+    if (b > 0 && list_ascending(A, a, g.nb, lane) && list_ascending(B, b, g.nb, lane)) {
+        for (int i0 = 0; i0 < a; i0 += 64) {
+            const int i = i0 + lane;
+            bool in_b = false;
+            if (i < a) {
+                const int x = A[i];
+                const int pos = lower_bound_list(B, b, x);
+                in_b = pos < b && B[pos] == x;
+            }
+            n -= __popcll(__ballot(in_b));
+        }
+    }
+    if (lane == 0) wlen[c] = n;
+}
+
 // The walk of a work item straight from the two blocks' radii: the union of
 // their key boxes in ascending block order, each entry (block << 2) | sides --
 // exactly what union_kernel makes of the radius mask's lists for the same two
 // blocks, without the lists.  One wave64 per item scans the frames either box
 // touches, 64 candidate blocks at a time, and compacts with a ballot.
 __global__ __launch_bounds__(64 * kUnionWaves) void radius_walk_kernel(
-    const int32_t *__restrict__ radius, int r_max, Grid g, int64_t items, int pairs_per_head,
+    const int32_t *__restrict__ radius, int r_max, Grid g, int64_t items, int slots,
     const int2 *__restrict__ pairs, int64_t ustride, int32_t *__restrict__ ulist,
     int32_t *__restrict__ ulen) {
     const int64_t item = (int64_t)blockIdx.x * kUnionWaves + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (item >= items) return;
-    const int64_t h = item / pairs_per_head;
+    const int64_t h = item / slots;
     const int2 pr = pairs[item];
     if (pr.x < 0) {  // an unused item slot: an empty walk
         if (lane == 0) ulen[item] = 0;
@@ -777,18 +876,23 @@ int64_t union_stride(int64_t maxcnt) { return (2 * maxcnt + 63) / 64 * 64; }
 hipError_t launch_union(const int32_t *idx, const int32_t *cnt, const float *lw, int64_t maxcnt,
                         const Grid &g, int heads, const int2 *pairs, int32_t *ulist, int32_t *ulen,
                         float2 *ubias, hipStream_t s) {
-    const int pph = pairs_per_head(g);
-    const int64_t items = (int64_t)heads * pph;
+    const int slots = plan_slots_per_head(g);
+    const int64_t items = (int64_t)heads * slots;
     hipLaunchKernelGGL(union_kernel, dim3((unsigned)((items + kUnionWaves - 1) / kUnionWaves)),
-                       dim3(64 * kUnionWaves), 0, s, idx, cnt, lw, maxcnt, g, items, pph, pairs,
+                       dim3(64 * kUnionWaves), 0, s, idx, cnt, lw, maxcnt, g, items, slots, pairs,
                        union_stride(maxcnt), ulist, ulen, ubias);
     return hipGetLastError();
 }
 
-hipError_t launch_pair(const int32_t *cnt, int64_t maxcnt, const Grid &g, int heads, int2 *pairs,
-                       hipStream_t s) {
+hipError_t launch_pair(const int32_t *idx, const int32_t *cnt, int64_t maxcnt, const Grid &g,
+                       int heads, int2 *pairs, int32_t *scratch, hipStream_t s) {
+    const int64_t cands =
+        (int64_t)heads * (candidates(pairs_per_head(g)) + candidates(temporal_pairs_per_head(g)));
+    hipLaunchKernelGGL(candidate_walk_kernel,
+                       dim3((unsigned)((cands + kUnionWaves - 1) / kUnionWaves)),
+                       dim3(64 * kUnionWaves), 0, s, idx, cnt, maxcnt, g, heads, scratch);
     hipLaunchKernelGGL(pair_kernel, dim3((unsigned)heads), dim3(kPairThreads), 0, s, cnt, nullptr,
-                       0, maxcnt, g, pairs_per_head(g), pairs);
+                       scratch, 0, maxcnt, g, plan_slots_per_head(g), pairs);
     return hipGetLastError();
 }
 
@@ -796,27 +900,27 @@ hipError_t launch_pair_radius(const int32_t *radius, int r_max, int64_t maxcnt, 
                               int heads, int2 *pairs, hipStream_t s) {
     if (g.nby * g.nbx <= kPairMaxPlane && g.T <= kPairMaxFrames && g.nb <= kPairMaxOrphans)
         hipLaunchKernelGGL(pair_radius_kernel, dim3((unsigned)heads), dim3(kPairThreads), 0, s,
-                           radius, r_max, g, pairs_per_head(g), pairs);
+                           radius, r_max, g, plan_slots_per_head(g), pairs);
     else
         hipLaunchKernelGGL(pair_kernel, dim3((unsigned)heads), dim3(kPairThreads), 0, s, nullptr,
-                           radius, r_max, maxcnt, g, pairs_per_head(g), pairs);
+                           radius, nullptr, r_max, maxcnt, g, plan_slots_per_head(g), pairs);
     return hipGetLastError();
 }
 
 hipError_t launch_radius_walk(const int32_t *radius, int r_max, int64_t maxcnt, const Grid &g,
                               int heads, const int2 *pairs, int32_t *ulist, int32_t *ulen,
                               hipStream_t s) {
-    const int pph = pairs_per_head(g);
-    const int64_t items = (int64_t)heads * pph;
+    const int slots = plan_slots_per_head(g);
+    const int64_t items = (int64_t)heads * slots;
     hipLaunchKernelGGL(radius_walk_kernel, dim3((unsigned)((items + kUnionWaves - 1) / kUnionWaves)),
-                       dim3(64 * kUnionWaves), 0, s, radius, r_max, g, items, pph, pairs,
+                       dim3(64 * kUnionWaves), 0, s, radius, r_max, g, items, slots, pairs,
                        union_stride(maxcnt), ulist, ulen);
     return hipGetLastError();
 }
 
 hipError_t launch_order(const int32_t *ulen, const Grid &g, int heads, int64_t maxcnt,
                         int32_t *order, hipStream_t s) {
-    const int64_t items = (int64_t)heads * pairs_per_head(g);
+    const int64_t items = (int64_t)heads * plan_slots_per_head(g);
     // lengths above kOrderMaxBin count as kOrderMaxBin (work and class)
     const int maxlen = (int)(2 * maxcnt < kOrderMaxBin ? 2 * maxcnt : kOrderMaxBin);
     hipLaunchKernelGGL(order_kernel, dim3(kXcds), dim3(kOrderThreads), 0, s, ulen, items,

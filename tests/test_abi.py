@@ -161,7 +161,8 @@ def test_plan_bytes_closed_form(lib):
 
     for (T, H, W, heads, maxcnt) in [(21, 30, 52, 12, 476), (8, 8, 8, 1, 7), (3, 20, 28, 2, 1)]:
         nby, nbx = -(-H // 8), -(-W // 8)
-        items = heads * T * ((nby + 1) // 2) * nbx
+        # item slots per head: vertical pairs or temporal pairs, whichever are more
+        items = heads * max(T * ((nby + 1) // 2) * nbx, (T + 1) // 2 * nby * nbx)
         slots = -(-items // 8) * 8
         order = 8 * 2 * -(-items // 8)  # eight ranges of at most twice the mean count
         stride = -(-(2 * maxcnt) // 64) * 64

@@ -440,8 +440,7 @@ def test_work_order_ranges(case):
     tra.tra_plan(idx, cnt, maxcnt, T, H, W, heads, 64, plan)
     torch.cuda.synchronize()
     raw = plan.cpu().numpy().view(np.int32)
-    nby, nbx = -(-H // 8), -(-W // 8)
-    items = heads * T * ((nby + 1) // 2) * nbx
+    items = heads * plan_slots(T, H, W)
     cap = 2 * -(-items // 8)
     order = raw[: 8 * cap]
     o_ulen = -(-(4 * 8 * cap) // 256) * 256 // 4  # the walk lengths follow, 256-byte aligned
@@ -488,16 +487,55 @@ def test_work_order_ranges(case):
         assert_close(out.reshape(-1, 128)[rows], ref, "attention along the capped order")
 
 
-def pair_table_model(cnt, T, H, W):
-    """The pair table the plan must hold, from the list lengths alone: per head,
-    the vertical pairs (tile rows 2p, 2p + 1) whose lengths are within a factor
-    of two, in raster order; then the other blocks sorted by length class (four
-    per octave of length + 1), longest class first, raster order inside a class,
-    paired in that order; then (-1, -1) up to the head's slot count."""
-    heads, nb = cnt.shape
+def plan_slots(T, H, W):
+    """Item slots per head of a walk plan: vertical pairs (T ceil(nby / 2) nbx)
+    or temporal pairs (ceil(T / 2) nby nbx), whichever are more."""
     nby, nbx = -(-H // 8), -(-W // 8)
-    npy = (nby + 1) // 2
-    pph = T * npy * nbx
+    return max(T * ((nby + 1) // 2) * nbx, (T + 1) // 2 * nby * nbx)
+
+
+def candidate_walk(idx_h, cnt_h, maxcnt, nb, a, b):
+    """Walk length of the pair (a, b) as the union walk makes it: |A| + |B| -
+    |A n B| for strictly ascending lists inside [0, nb), else |A| + |B|."""
+    def lst(x):
+        return [] if x < 0 else list(idx_h[x, :min(max(int(cnt_h[x]), 0), maxcnt)])
+
+    A, B = lst(a), lst(b)
+
+    def ascending(l):
+        return all(0 <= v < nb for v in l) and all(u < v for u, v in zip(l, l[1:]))
+
+    if B and ascending(A) and ascending(B):
+        return len(A) + len(B) - len(set(A) & set(B))
+    return len(A) + len(B)
+
+
+def pair_table_model(idx, cnt, T, H, W):
+    """The pair table the plan must hold: per head, the neighbour pairs -- the
+    vertical ones (tile rows 2p, 2p + 1), or the temporal ones (one tile in
+    frames 2p, 2p + 1) when their walks (candidate_walk, every fourth pair of
+    either kind) take at least 5% fewer steps per list entry -- whose list lengths are within a factor of two, in raster
+    order; then the other blocks sorted by length class (four per octave of
+    length + 1), longest class first, raster order inside a class, paired in
+    that order; then (-1, -1) up to the head's slot count.  Returns the table and
+    the per-head choice (True: temporal)."""
+    heads, nb = cnt.shape
+    maxcnt = idx.shape[-1]
+    nby, nbx = -(-H // 8), -(-W // 8)
+    npy, plane = (nby + 1) // 2, nby * nbx
+    slots = plan_slots(T, H, W)
+
+    def vertical_pairs():
+        for p in range(T * npy * nbx):
+            t, pr, bx = p // (npy * nbx), (p // nbx) % npy, p % nbx
+            qa = (t * nby + 2 * pr) * nbx + bx
+            yield qa, (qa + nbx if 2 * pr + 1 < nby else -1)
+
+    def temporal_pairs():
+        for p in range((T + 1) // 2 * plane):
+            tp, j = divmod(p, plane)
+            qa = 2 * tp * plane + j
+            yield qa, (qa + plane if 2 * tp + 1 < T else -1)
 
     def cls(c):
         x = max(int(c), 0) + 1
@@ -508,25 +546,33 @@ def pair_table_model(cnt, T, H, W):
     def good(a, b):
         return 2 * min(a, b) >= max(a, b)
 
-    table = np.full((heads, pph, 2), -1, dtype=np.int64)
+    table = np.full((heads, slots, 2), -1, dtype=np.int64)
+    temporal = []
     for h in range(heads):
-        c = cnt[h]
-        items, orph = [], []
-        for p in range(pph):
-            t, pr, bx = p // (npy * nbx), (p // nbx) % npy, p % nbx
-            qa = (t * nby + 2 * pr) * nbx + bx
-            qb = qa + nbx if 2 * pr + 1 < nby else -1
+        c = np.clip(cnt[h].astype(np.int64), 0, maxcnt)
+        # judged on every fourth pair of either kind: walk steps per list entry
+        def steps_entries(pairs):
+            u = e = 0
+            for a, b in list(pairs)[::4]:
+                u += candidate_walk(idx[h], cnt[h], maxcnt, nb, a, b)
+                e += int(c[a]) + (int(c[b]) if b >= 0 else 0)
+            return u, e
+
+        uv, lv = steps_entries(vertical_pairs())
+        ut, lt = steps_entries(temporal_pairs())
+        temp = 20 * ut * lv < 19 * uv * lt
+        temporal.append(temp)
+        items, partner = [], {}
+        for qa, qb in (temporal_pairs() if temp else vertical_pairs()):
+            if qb >= 0:
+                partner[qa], partner[qb] = qb, qa
             if qb < 0 or good(c[qa], c[qb]):
                 items.append((qa, qb))
-        for b in range(nb):
-            by = (b // nbx) % nby
-            o = b - nbx if by & 1 else (b + nbx if by + 1 < nby else -1)
-            if o >= 0 and not good(c[b], c[o]):
-                orph.append(b)
+        orph = [b for b in range(nb) if b in partner and not good(c[b], c[partner[b]])]
         orph.sort(key=lambda b: -cls(c[b]))  # stable: raster order inside a class
         items += [(orph[i], orph[i + 1] if i + 1 < len(orph) else -1) for i in range(0, len(orph), 2)]
         table[h, :len(items)] = items
-    return table
+    return table, temporal
 
 
 def radius_pair_table_model(radii, r_max, T, H, W):
@@ -542,9 +588,8 @@ def radius_pair_table_model(radii, r_max, T, H, W):
     heads, nb = radii.shape
     nby, nbx = -(-H // 8), -(-W // 8)
     plane, npy = nby * nbx, (nby + 1) // 2
-    pph = T * npy * nbx
     by_frame = plane <= 256 and T <= 1024 and nb <= 8192
-    table = np.full((heads, pph, 2), -1, dtype=np.int64)
+    table = np.full((heads, plan_slots(T, H, W), 2), -1, dtype=np.int64)
     for h in range(heads):
         r = np.clip(radii[h].astype(np.int64), 0, r_max)
         kept = [[] for _ in range(T)]
@@ -580,8 +625,7 @@ def radius_pair_table_model(radii, r_max, T, H, W):
 
 
 def plan_pair_table(plan, T, H, W, heads, maxcnt):
-    nby, nbx = -(-H // 8), -(-W // 8)
-    items = heads * T * ((nby + 1) // 2) * nbx
+    items = heads * plan_slots(T, H, W)
     rows = -(-items // 8) * 8
     cap = 2 * -(-items // 8)
     stride = -(-(2 * maxcnt) // 64) * 64
@@ -591,28 +635,65 @@ def plan_pair_table(plan, T, H, W, heads, maxcnt):
     return raw.reshape(heads, -1, 2).astype(np.int64)
 
 
-@pytest.mark.parametrize("kind", ["routing", "radii"])
+def temporal_lists(T, H, W, heads, seed):
+    """Caller lists whose temporal neighbours (one tile in frames 2p, 2p + 1)
+    nearly coincide while vertical neighbours are independent: random ascending
+    lists of nb / 8 to nb / 3 blocks, the second frame of each pair keeping its
+    partner's list with one block added or dropped (the last frame of an odd T
+    stands alone)."""
+    nby, nbx = -(-H // 8), -(-W // 8)
+    plane = nby * nbx
+    nb = T * plane
+    rng = np.random.default_rng(seed)
+    maxcnt = nb // 3 + 1
+    idx = np.full((heads, nb, maxcnt), -1, dtype=np.int32)
+    cnt = np.zeros((heads, nb), dtype=np.int32)
+    for h in range(heads):
+        for tp in range(0, T, 2):
+            for j in range(plane):
+                a = tp * plane + j
+                la = np.sort(rng.choice(nb, size=rng.integers(nb // 8, nb // 3), replace=False))
+                idx[h, a, :len(la)], cnt[h, a] = la, len(la)
+                if tp + 1 < T:
+                    lb = set(la.tolist())
+                    x = int(rng.integers(nb))
+                    lb.symmetric_difference_update({x})
+                    lb = np.array(sorted(lb), dtype=np.int32)
+                    idx[h, a + plane, :len(lb)], cnt[h, a + plane] = lb, len(lb)
+    return idx, cnt, maxcnt
+
+
+@pytest.mark.parametrize("kind", ["routing", "radii", "temporal"])
 def test_pair_table(kind):
-    # The plan's pair table equals the rule applied to the list lengths, every
+    # The plan's pair table equals the rule applied to the lists (neighbour
+    # direction per head from the candidate walks, then the list lengths), every
     # query block appears in exactly one item, and attention along it is exact.
     T, H, W, heads, d = 5, 40, 56, 2, 128
     shp = (heads, T, H, W, d)
     print(f"[case] pair table {kind} {shp}", flush=True)
     nb = tra.tra_grid(T, H, W)[2]
     rng = np.random.default_rng(29)
-    if kind == "routing":
-        radii = np.where(rng.random((heads, nb)) < 0.2, INF, 1).astype(np.int32)
-        r_max = INF
+    radii = None
+    if kind == "temporal":
+        li, lc, maxcnt = temporal_lists(T, H, W, heads, seed=30)
+        idx, cnt = torch.from_numpy(li).cuda(), torch.from_numpy(lc).cuda()
     else:
-        radii = rng.integers(0, 5, size=(heads, nb)).astype(np.int32)
-        r_max = 4
-    idx, cnt, maxcnt = gpu_mask(radii, shp, r_max)
+        if kind == "routing":
+            radii = np.where(rng.random((heads, nb)) < 0.2, INF, 1).astype(np.int32)
+            r_max = INF
+        else:
+            radii = rng.integers(0, 5, size=(heads, nb)).astype(np.int32)
+            r_max = 4
+        idx, cnt, maxcnt = gpu_mask(radii, shp, r_max)
     plan = torch.zeros(tra.tra_plan_bytes(T, H, W, heads, 64, maxcnt), dtype=torch.uint8,
                        device="cuda")
     tra.tra_plan(idx, cnt, maxcnt, T, H, W, heads, 64, plan)
     torch.cuda.synchronize()
     got = plan_pair_table(plan, T, H, W, heads, maxcnt)
-    want = pair_table_model(cnt.cpu().numpy(), T, H, W)
+    want, temporal = pair_table_model(idx.cpu().numpy(), cnt.cpu().numpy(), T, H, W)
+    print(f"[pairs] {kind}: temporal neighbours per head {temporal}", flush=True)
+    if kind == "temporal":  # lists that coincide in time take temporal neighbours
+        assert all(temporal)
     assert np.array_equal(got, want), "pair table differs from the rule"
     for h in range(heads):
         blocks = got[h].ravel()
@@ -623,7 +704,11 @@ def test_pair_table(kind):
     out = torch.full(shp, float("nan"), dtype=torch.float32, device="cuda")
     tra.tra_attn_plan(dev16(q), dev16(k), dev16(v), T, H, W, heads, d, 64, plan, maxcnt, out)
     torch.cuda.synchronize()
-    ref = oracle.attention(q, k, v, radii)
+    if radii is not None:
+        ref = oracle.attention(q, k, v, radii)
+    else:
+        ref = oracle.attention_lists_rows(q, k, v, idx.cpu().numpy(), cnt.cpu().numpy(),
+                                          np.arange(heads * T * H * W)).reshape(out.shape)
     assert_close(out.cpu().numpy(), ref, f"attention along the pair table ({kind})")
 
 

@@ -279,8 +279,10 @@ int tra_attn_weighted(const void *q, const void *k, const void *v, int T, int H,
  * Plan / execute split with cross-step reuse (Token Radius Attention ...,
  * "The TRA Pipeline: Cross-Step Reuse": the sparsity decided in a warm-up step
  * is reused by the later denoising steps).  tra_plan turns key-block lists into
- * the attention walk -- the pairing of query blocks into work items (vertical
- * neighbours whose list lengths are within a factor of two; the other blocks
+ * the attention walk -- the pairing of query blocks into work items
+ * (neighbours whose list lengths are within a factor of two: vertical ones, or,
+ * in a head where a sample of the candidate pairs shows temporal walks at least
+ * 5% shorter per list entry, one tile in frames 2p and 2p + 1; the other blocks
  * re-paired by length class, so that long lists share a walk with long ones),
  * the union of each item's two lists, then the work order -- and stores it in a
  * caller-owned device buffer of tra_plan_bytes bytes; tra_attn_plan then runs the attention of new

@@ -181,12 +181,13 @@ class ProfScope {
 // Packed K/V of one call: K and V^T tiles, the partial maxima of |v| and the
 // per-head V exponents (see launch_vmax).
 struct PackedOffsets {
-    size_t kt, vt, vpart, vexp;
+    size_t kt, vt, vpart, vexp, sched;
 };
 struct Packed {
     uint16_t *kt, *vt;
     uint32_t *vpart;
     int32_t *vexp;
+    int32_t *sched;  // the attention launch's work-claiming counters
 };
 
 PackedOffsets reserve_packed(Scratch &ws, const tra::Grid &g, int heads, int head_dim) {
@@ -196,12 +197,13 @@ PackedOffsets reserve_packed(Scratch &ws, const tra::Grid &g, int heads, int hea
     o.vt = ws.reserve(tiles);
     o.vpart = ws.reserve((size_t)heads * tra::kVmaxParts * sizeof(uint32_t));
     o.vexp = ws.reserve((size_t)heads * sizeof(int32_t));
+    o.sched = ws.reserve(tra::kSchedBytes);
     return o;
 }
 
 Packed packed_at(const Scratch &ws, const PackedOffsets &o) {
     return Packed{ws.at<uint16_t>(o.kt), ws.at<uint16_t>(o.vt), ws.at<uint32_t>(o.vpart),
-                  ws.at<int32_t>(o.vexp)};
+                  ws.at<int32_t>(o.vexp), ws.at<int32_t>(o.sched)};
 }
 
 // The head's largest |v|, then the tile packing of k and v (and, with q given,
@@ -432,8 +434,8 @@ static hipError_t attn_launch(const void *q, const Packed &pk, const tra::Grid &
     const float2 *ubias = plan && L.weighted ? (const float2 *)(plan + L.o_ubias) : nullptr;
     const int2 *pairs = plan ? (const int2 *)(plan + L.o_pairs) : nullptr;
     return tra::launch_attn(head_dim, (const uint16_t *)q, pk.kt, pk.vt, pk.vexp, pairs, ulist,
-                            ulen, ubias, plan ? L.ustride : 0, order, g, heads, (float *)out,
-                            stream, eo);
+                            ulen, ubias, plan ? L.ustride : 0, order, pk.sched, g, heads,
+                            (float *)out, stream, eo);
 }
 
 // Pack k and v, then attention along a walk plan (nullptr: dense mode).

@@ -38,6 +38,12 @@ constexpr int kAttnThreads = 256;
 // bits anywhere in its normal range.
 constexpr float kRescaleLog2 = 8.0f;
 
+// Counters of a launch along a work order: sched[y kSchedStride] counts the
+// claims on XCD range y (each counter on a 256-byte line of its own).
+__global__ void sched_clear_kernel(int32_t *sched) {
+    if (threadIdx.x < kXcdRanges) sched[threadIdx.x * kSchedStride] = 0;
+}
+
 // WEIGHTED: every walk entry carries, per side, a log2 weight added to the
 // logits of its keys (inverse inclusion probabilities of sampled blocks).
 // ENTROPY: each query also keeps, against the same lazy reference m, the fp32
@@ -50,7 +56,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     const uint16_t *__restrict__ vt, const int32_t *__restrict__ vexp,
     const int2 *__restrict__ pairs, const int32_t *__restrict__ ulist,
     const int32_t *__restrict__ ulen,
-    const float2 *__restrict__ ubias, int64_t ustride, const int32_t *__restrict__ order, Grid g,
+    const float2 *__restrict__ ubias, int64_t ustride, const int32_t *__restrict__ order,
+    int32_t *__restrict__ sched, Grid g,
     int heads, int items_per_head, int per_xcd, FastDiv div_nbx, FastDiv div_nby,
     float *__restrict__ out, float scale_log2, EntropyOut eo) {
     static_assert(!(WEIGHTED && ENTROPY), "entropy of unweighted rows only");
@@ -75,11 +82,28 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     // L2 sees neighbouring query blocks.  With a work order (lists of unequal
     // length) the ranges hold equal shares of the total work and each is taken
     // by walk length class, longest class first; without one (dense mode: equal
-    // work) the ranges hold equal item counts in raster order.
+    // work) the ranges hold equal item counts in raster order.  Along a work
+    // order each workgroup claims the next item of its XCD's range, and once
+    // that range is spent the next item of another range: the XCDs do not run
+    // at one speed (equal ranges of dense work finish up to 6% apart), so the
+    // fast ones take over the slow ones' last items.
     const int64_t total = (int64_t)heads * items_per_head;
     int64_t item;
     if (order) {
-        item = ((const const_i32_t *)order)[blockIdx.x];  // one slot per workgroup
+        __shared__ int32_t claimed;
+        if (threadIdx.x == 0) {
+            const int cap = (int)(gridDim.x / kXcdRanges);  // slots per range
+            const int x = (int)(blockIdx.x % kXcdRanges);
+            int it = -1;
+            for (int j = 0; j < kXcdRanges && it < 0; ++j) {
+                const int y = (x + j) % kXcdRanges;
+                const int k = atomicAdd(sched + y * kSchedStride, 1);
+                if (k < cap) it = ((const const_i32_t *)order)[(int64_t)kXcdRanges * k + y];
+            }
+            claimed = it;  // -1: every range is spent
+        }
+        __syncthreads();
+        item = claimed;
         if (item < 0) return;
     } else {
         item = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
@@ -473,8 +497,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
 hipError_t launch_attn(int D, const uint16_t *q, const uint16_t *kt, const uint16_t *vt,
                        const int32_t *vexp, const int2 *pairs, const int32_t *ulist,
                        const int32_t *ulen, const float2 *ubias, int64_t ustride,
-                       const int32_t *order, const Grid &g, int heads, float *out, hipStream_t s,
-                       const EntropyOut *entropy) {
+                       const int32_t *order, int32_t *sched, const Grid &g, int heads, float *out,
+                       hipStream_t s, const EntropyOut *entropy) {
+    if (order && !sched) return hipErrorInvalidValue;
     // items per head: the plan's slots, or the vertical pairs of dense mode
     const int pph = pairs ? plan_slots_per_head(g) : pairs_per_head(g);
     const int64_t total = (int64_t)heads * pph;
@@ -487,10 +512,11 @@ hipError_t launch_attn(int D, const uint16_t *q, const uint16_t *kt, const uint1
     const EntropyOut eo = entropy ? *entropy : EntropyOut{nullptr, nullptr, 0.f, 0.f};
 #define TRA_LAUNCH(DD, WW, EE)                                                                \
     hipLaunchKernelGGL((attn_kernel<DD, WW, EE>), grid, block, 0, s, q, kt, vt, vexp, pairs,     \
-                       ulist, ulen, ubias, ustride, order, g, heads, pph, per_xcd, div_nbx,        \
+                       ulist, ulen, ubias, ustride, order, sched, g, heads, pph, per_xcd, div_nbx, \
                        div_nby, out, scale_log2, eo)
     const bool weighted = ubias != nullptr && ulist != nullptr;
     if (weighted && entropy) return hipErrorInvalidValue;
+    if (order) hipLaunchKernelGGL(sched_clear_kernel, dim3(1), dim3(64), 0, s, sched);
     if (D == 128 && weighted)
         TRA_LAUNCH(128, true, false);
     else if (D == 128 && entropy)

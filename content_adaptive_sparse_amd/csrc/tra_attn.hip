@@ -82,33 +82,37 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     // L2 sees neighbouring query blocks.  With a work order (lists of unequal
     // length) the ranges hold equal shares of the total work and each is taken
     // by walk length class, longest class first; without one (dense mode: equal
-    // work) the ranges hold equal item counts in raster order.  Along a work
-    // order each workgroup claims the next item of its XCD's range, and once
-    // that range is spent the next item of another range: the XCDs do not run
-    // at one speed (equal ranges of dense work finish up to 6% apart), so the
-    // fast ones take over the slow ones' last items.
+    // work) the ranges hold equal item counts in raster order.  Each workgroup
+    // claims the next item of its XCD's range, and once that range is spent the
+    // next item of another range: the XCDs do not run at one speed (equal
+    // ranges of dense work finish up to 6% apart), so the fast ones take over
+    // the slow ones' last items.
     const int64_t total = (int64_t)heads * items_per_head;
     int64_t item;
-    if (order) {
+    {
         __shared__ int32_t claimed;
         if (threadIdx.x == 0) {
-            const int cap = (int)(gridDim.x / kXcdRanges);  // slots per range
+            // slots per range: the order's rows, or the dense ranges' length
+            const int cap = order ? (int)(gridDim.x / kXcdRanges) : per_xcd;
             const int x = (int)(blockIdx.x % kXcdRanges);
             int it = -1;
             for (int j = 0; j < kXcdRanges && it < 0; ++j) {
                 const int y = (x + j) % kXcdRanges;
                 const int k = atomicAdd(sched + y * kSchedStride, 1);
-                if (k < cap) it = ((const const_i32_t *)order)[(int64_t)kXcdRanges * k + y];
+                if (k >= cap) continue;
+                if (order) {
+                    it = ((const const_i32_t *)order)[(int64_t)kXcdRanges * k + y];
+                } else {
+                    const int64_t r = (int64_t)y * per_xcd + k;
+                    it = r < total ? (int)r : -1;
+                }
             }
             claimed = it;  // -1: every range is spent
         }
         __syncthreads();
         item = claimed;
-        if (item < 0) return;
-    } else {
-        item = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     }
-    if (item >= total) return;
+    if (item < 0 || item >= total) return;
     const int h = (int)(item / items_per_head);
     int blk[2];
     if (pairs) {
@@ -499,7 +503,7 @@ hipError_t launch_attn(int D, const uint16_t *q, const uint16_t *kt, const uint1
                        const int32_t *ulen, const float2 *ubias, int64_t ustride,
                        const int32_t *order, int32_t *sched, const Grid &g, int heads, float *out,
                        hipStream_t s, const EntropyOut *entropy) {
-    if (order && !sched) return hipErrorInvalidValue;
+    if (!sched) return hipErrorInvalidValue;
     // items per head: the plan's slots, or the vertical pairs of dense mode
     const int pph = pairs ? plan_slots_per_head(g) : pairs_per_head(g);
     const int64_t total = (int64_t)heads * pph;
@@ -516,7 +520,7 @@ hipError_t launch_attn(int D, const uint16_t *q, const uint16_t *kt, const uint1
                        div_nby, out, scale_log2, eo)
     const bool weighted = ubias != nullptr && ulist != nullptr;
     if (weighted && entropy) return hipErrorInvalidValue;
-    if (order) hipLaunchKernelGGL(sched_clear_kernel, dim3(1), dim3(64), 0, s, sched);
+    hipLaunchKernelGGL(sched_clear_kernel, dim3(1), dim3(64), 0, s, sched);
     if (D == 128 && weighted)
         TRA_LAUNCH(128, true, false);
     else if (D == 128 && entropy)

@@ -170,9 +170,9 @@ struct EntropyOut {
     float two_gamma_log2e;
 };
 
-// Items along a work order are claimed at run time: one int32 counter per XCD
-// range, kSchedStride int32 apart, in kSchedBytes of device memory per launch
-// (cleared by the launch itself; calls that overlap must not share it).
+// Attention items are claimed at run time: one int32 counter per XCD range,
+// kSchedStride int32 apart, in kSchedBytes of device memory per launch (cleared
+// by the launch itself; calls that overlap must not share it).
 constexpr int kXcdRanges = 8;
 constexpr int kSchedStride = 64;
 constexpr size_t kSchedBytes = (size_t)kXcdRanges * kSchedStride * sizeof(int32_t);
@@ -180,7 +180,7 @@ constexpr size_t kSchedBytes = (size_t)kXcdRanges * kSchedStride * sizeof(int32_
 // ulist == nullptr: the dense mode (every block, both sides; order and pairs
 // null, vertical pairs in XCD-contiguous raster order).  vexp: the per-head V
 // exponents.  pairs: the plan's pair table.  sched: kSchedBytes of scratch for
-// a launch along a work order (order non-null), else unused.
+// the launch's work-claiming counters.
 hipError_t launch_attn(int D, const uint16_t *q, const uint16_t *kt, const uint16_t *vt,
                        const int32_t *vexp, const int2 *pairs, const int32_t *ulist,
                        const int32_t *ulen, const float2 *ubias, int64_t ustride,

@@ -136,7 +136,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? TRA_OK : TRA_ERR_HIP; }
 
 // Work items of the attention kernel: pairs of neighbouring query blocks.
 size_t walk_rows(const tra::Grid &g, int heads) { return (size_t)tra::walk_items(g, heads); }
-size_t order_len(const tra::Grid &g, int heads) { return (size_t)tra::order_slots(g, heads); }
+size_t order_len(const tra::Grid &g, int heads) { return (size_t)tra::order_ints(g, heads); }
 
 // ---- optional per-kernel event timing ----
 struct ProfRecord {
@@ -213,7 +213,7 @@ hipError_t pack_kv(int head_dim, const void *q, const void *k, const void *v, co
     hipError_t e;
     {
         ProfScope ps(TRA_KERNEL_VMAX, stream);
-        e = tra::launch_vmax(head_dim, (const uint16_t *)v, g, heads, p.vpart, stream);
+        e = tra::launch_vmax(head_dim, (const uint16_t *)v, g, heads, p.vpart, p.sched, stream);
     }
     if (e != hipSuccess) return e;
     ProfScope ps(TRA_KERNEL_PACK_POOL, stream);
@@ -558,13 +558,20 @@ int tra_attn_weighted(const void *q, const void *k, const void *v, int T, int H,
     return attn_lists(q, k, v, g, heads, head_dim, idx, cnt, lw, maxcnt, out, stream);
 }
 
+// Launches timed back to back get a zeroed set of work-claiming counters each.
+constexpr int kMaxTimedReps = 4096;
+
 // Packs k and v into pk, then times `reps` back-to-back attention launches
-// along the plan (nullptr: dense mode) between one pair of events on `stream`.
+// along the plan (nullptr: dense mode) between one pair of events on `stream`;
+// sched_sets: reps sets of work-claiming counters (kSchedBytes each), zeroed
+// before the timed launches.
 static int time_attn_launches(const void *q, const void *k, const void *v, const tra::Grid &g,
                               int heads, int head_dim, const char *plan, const PlanLayout &L,
-                              const Packed &pk, int reps, void *out, float *ms,
-                              hipStream_t stream) {
+                              const Packed &pk, int32_t *sched_sets, int reps, void *out,
+                              float *ms, hipStream_t stream) {
+    const int64_t set_ints = (int64_t)(tra::kSchedBytes / sizeof(int32_t));
     hipError_t e = pack_kv(head_dim, nullptr, k, v, g, heads, nullptr, nullptr, pk, stream);
+    if (e == hipSuccess) e = tra::launch_zero(sched_sets, set_ints * reps, stream);
     if (e != hipSuccess) return hip_status(e);
     hipEvent_t ev[2];
     if (hipEventCreate(&ev[0]) != hipSuccess) return TRA_ERR_HIP;
@@ -573,8 +580,11 @@ static int time_attn_launches(const void *q, const void *k, const void *v, const
         return TRA_ERR_HIP;
     }
     e = hipEventRecord(ev[0], stream);
-    for (int i = 0; i < reps && e == hipSuccess; ++i)
-        e = attn_launch(q, pk, g, heads, head_dim, plan, L, out, stream);
+    for (int i = 0; i < reps && e == hipSuccess; ++i) {
+        Packed pi = pk;
+        pi.sched = sched_sets + set_ints * i;
+        e = attn_launch(q, pi, g, heads, head_dim, plan, L, out, stream);
+    }
     if (e == hipSuccess) e = hipEventRecord(ev[1], stream);
     if (e == hipSuccess) e = hipEventSynchronize(ev[1]);
     float t = 0.f;
@@ -594,20 +604,23 @@ int tra_time_attn(const void *q, const void *k, const void *v, int T, int H, int
     int rc = make_grid(T, H, W, block, &g);
     if (rc == TRA_OK) rc = check_dims(heads, head_dim, g);
     if (rc != TRA_OK) return rc;
-    if (!q || !k || !v || !out || !ms || reps < 1) return TRA_ERR_INVALID_ARG;
+    if (!q || !k || !v || !out || !ms || reps < 1 || reps > kMaxTimedReps)
+        return TRA_ERR_INVALID_ARG;
     if ((idx == nullptr) != (cnt == nullptr) || (lw && !idx)) return TRA_ERR_INVALID_ARG;
     if (idx && (rc = check_plan(g, heads, maxcnt)) != TRA_OK) return rc;
     const PlanLayout L = idx ? plan_layout(g, heads, maxcnt, lw != nullptr) : PlanLayout{};
     Scratch ws(stream);
     const PackedOffsets po = reserve_packed(ws, g, heads, head_dim);
     const size_t o_plan = idx ? ws.reserve(L.bytes) : 0;
+    const size_t o_sets = ws.reserve(tra::kSchedBytes * (size_t)reps);
     if ((rc = ws.allocate()) != TRA_OK) return rc;
     const Packed pk = packed_at(ws, po);
     char *plan = idx ? ws.at<char>(o_plan) : nullptr;
     hipError_t e = hipSuccess;
     if (idx) e = plan_walk_into(idx, cnt, lw, maxcnt, g, heads, plan, L, stream);
     if (e != hipSuccess) return hip_status(e);
-    return time_attn_launches(q, k, v, g, heads, head_dim, plan, L, pk, reps, out, ms, stream);
+    return time_attn_launches(q, k, v, g, heads, head_dim, plan, L, pk, ws.at<int32_t>(o_sets),
+                              reps, out, ms, stream);
 }
 
 int tra_time_attn_plan(const void *q, const void *k, const void *v, int T, int H, int W,
@@ -617,14 +630,16 @@ int tra_time_attn_plan(const void *q, const void *k, const void *v, int T, int H
     int rc = make_grid(T, H, W, block, &g);
     if (rc == TRA_OK) rc = check_dims(heads, head_dim, g);
     if (rc != TRA_OK) return rc;
-    if (!q || !k || !v || !out || !ms || reps < 1) return TRA_ERR_INVALID_ARG;
+    if (!q || !k || !v || !out || !ms || reps < 1 || reps > kMaxTimedReps)
+        return TRA_ERR_INVALID_ARG;
     if (plan && (rc = check_plan(g, heads, maxcnt)) != TRA_OK) return rc;
     const PlanLayout L = plan ? plan_layout(g, heads, maxcnt) : PlanLayout{};
     Scratch ws(stream);
     const PackedOffsets po = reserve_packed(ws, g, heads, head_dim);
+    const size_t o_sets = ws.reserve(tra::kSchedBytes * (size_t)reps);
     if ((rc = ws.allocate()) != TRA_OK) return rc;
     return time_attn_launches(q, k, v, g, heads, head_dim, static_cast<const char *>(plan), L,
-                              packed_at(ws, po), reps, out, ms, stream);
+                              packed_at(ws, po), ws.at<int32_t>(o_sets), reps, out, ms, stream);
 }
 
 int tra_sip_mask(const void *q, const void *k, const float *u, int T, int H, int W, int heads,

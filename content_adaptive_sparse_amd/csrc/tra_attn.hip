@@ -37,12 +37,9 @@ constexpr int kAttnThreads = 256;
 // reference, so the result does not depend on it; fp16 keeps 11 significant
 // bits anywhere in its normal range.
 constexpr float kRescaleLog2 = 8.0f;
-
-// Counters of a launch along a work order: sched[y kSchedStride] counts the
-// claims on XCD range y (each counter on a 256-byte line of its own).
-__global__ void sched_clear_kernel(int32_t *sched) {
-    if (threadIdx.x < kXcdRanges) sched[threadIdx.x * kSchedStride] = 0;
-}
+// Slots past the end of an XCD range that look for other ranges' last items
+// (later slots of that XCD exit at once).
+constexpr int kThieves = 32;
 
 // WEIGHTED: every walk entry carries, per side, a log2 weight added to the
 // logits of its keys (inverse inclusion probabilities of sampled blocks).
@@ -82,35 +79,64 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     // L2 sees neighbouring query blocks.  With a work order (lists of unequal
     // length) the ranges hold equal shares of the total work and each is taken
     // by walk length class, longest class first; without one (dense mode: equal
-    // work) the ranges hold equal item counts in raster order.  Each workgroup
-    // claims the next item of its XCD's range, and once that range is spent the
-    // next item of another range: the XCDs do not run at one speed (equal
-    // ranges of dense work finish up to 6% apart), so the fast ones take over
-    // the slow ones' last items.
+    // work) the ranges hold equal item counts in raster order.  Along a work
+    // order the first three quarters of each range are taken in place; the last
+    // quarter (its shortest items) is claimed at run time, by the range's own
+    // workgroups and, once their range is spent, by other XCDs': the XCDs do
+    // not run at one speed (equal ranges of dense work finish up to 6% apart),
+    // so the fast ones take over the slow ones' last items, and only those
+    // items pay for the claim's atomic.
     const int64_t total = (int64_t)heads * items_per_head;
     int64_t item;
-    {
-        __shared__ int32_t claimed;
-        if (threadIdx.x == 0) {
-            // slots per range: the order's rows, or the dense ranges' length
-            const int cap = order ? (int)(gridDim.x / kXcdRanges) : per_xcd;
-            const int x = (int)(blockIdx.x % kXcdRanges);
-            int it = -1;
-            for (int j = 0; j < kXcdRanges && it < 0; ++j) {
-                const int y = (x + j) % kXcdRanges;
-                const int k = atomicAdd(sched + y * kSchedStride, 1);
-                if (k >= cap) continue;
-                if (order) {
-                    it = ((const const_i32_t *)order)[(int64_t)kXcdRanges * k + y];
-                } else {
-                    const int64_t r = (int64_t)y * per_xcd + k;
-                    it = r < total ? (int)r : -1;
+    if (!ENTROPY && order) {  // the entropy warm-up is dense: no work order
+        const const_i32_t *ord = (const const_i32_t *)order;
+        const int64_t cap = gridDim.x / kXcdRanges;  // slots per range
+        const int x = (int)(blockIdx.x % kXcdRanges);
+        const int64_t k = blockIdx.x / kXcdRanges;
+        const int nx = ord[kXcdRanges * cap + x];  // the range's length
+        const int mine = ord[blockIdx.x];          // loaded beside it
+        if (k < nx - nx / 4) {
+            item = mine;
+        } else if (k >= nx + kThieves) {
+            item = -1;  // enough slots past the range's end look for other ranges' items
+        } else {
+            // the own range's last quarter first (slots inside the range); once
+            // that is spent, one look at every other range's counter (a lane
+            // each), then a claim on the first range with items left, looked at
+            // again if that claim comes late
+            __shared__ int32_t claimed;
+            if (threadIdx.x < 64) {
+                const int lane = threadIdx.x;
+                int it = -1;
+                if (lane == 0 && k < nx) {
+                    const int c = atomicAdd(sched + x * kSchedStride, 1);
+                    if (c < nx / 4) it = ord[kXcdRanges * (int64_t)(nx - nx / 4 + c) + x];
                 }
+                it = __shfl(it, 0);
+                for (int round = 0; round < kXcdRanges && it < 0; ++round) {
+                    const int y = (x + 1 + lane) % kXcdRanges;
+                    bool left = false;
+                    int ny = 0;
+                    if (lane < kXcdRanges - 1) {
+                        ny = ord[kXcdRanges * cap + y];
+                        left = atomicAdd(sched + y * kSchedStride, 0) < ny / 4;
+                    }
+                    const uint64_t cand = __ballot(left);
+                    if (!cand) break;  // every range's last quarter is spent
+                    const int j = __builtin_ctzll(cand);
+                    if (lane == j) {
+                        const int c = atomicAdd(sched + y * kSchedStride, 1);
+                        if (c < ny / 4) it = ord[kXcdRanges * (int64_t)(ny - ny / 4 + c) + y];
+                    }
+                    it = __shfl(it, j);
+                }
+                if (lane == 0) claimed = it;
             }
-            claimed = it;  // -1: every range is spent
+            __syncthreads();
+            item = claimed;
         }
-        __syncthreads();
-        item = claimed;
+    } else {
+        item = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     }
     if (item < 0 || item >= total) return;
     const int h = (int)(item / items_per_head);
@@ -496,14 +522,27 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     }
 }
 
+__global__ void zero_kernel(int32_t *p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
 }  // namespace
+
+hipError_t launch_zero(int32_t *p, int64_t n, hipStream_t s) {
+    if (n > 0)
+        hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024)),
+                           dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
 
 hipError_t launch_attn(int D, const uint16_t *q, const uint16_t *kt, const uint16_t *vt,
                        const int32_t *vexp, const int2 *pairs, const int32_t *ulist,
                        const int32_t *ulen, const float2 *ubias, int64_t ustride,
                        const int32_t *order, int32_t *sched, const Grid &g, int heads, float *out,
                        hipStream_t s, const EntropyOut *entropy) {
-    if (!sched) return hipErrorInvalidValue;
+    if (order && !sched) return hipErrorInvalidValue;
     // items per head: the plan's slots, or the vertical pairs of dense mode
     const int pph = pairs ? plan_slots_per_head(g) : pairs_per_head(g);
     const int64_t total = (int64_t)heads * pph;
@@ -520,7 +559,7 @@ hipError_t launch_attn(int D, const uint16_t *q, const uint16_t *kt, const uint1
                        div_nby, out, scale_log2, eo)
     const bool weighted = ubias != nullptr && ulist != nullptr;
     if (weighted && entropy) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(sched_clear_kernel, dim3(1), dim3(64), 0, s, sched);
+    if (entropy && order) return hipErrorInvalidValue;  // the entropy warm-up walks every block
     if (D == 128 && weighted)
         TRA_LAUNCH(128, true, false);
     else if (D == 128 && entropy)

@@ -38,8 +38,10 @@ size_t packed_tile_elems(int D);
 // kernel reduces them, scales V and writes e_h to vexp [heads].
 constexpr int kVmaxParts = 256;  // at most the packing kernel's 256 threads
 int vmax_parts(const Grid &g, int D);
+// sched (or null): the next attention launch's work-claiming counters (kSchedBytes),
+// zeroed here -- every launch along a work order follows the packing of its K and V.
 hipError_t launch_vmax(int D, const uint16_t *v, const Grid &g, int heads, uint32_t *vpart,
-                       hipStream_t s);
+                       int32_t *sched, hipStream_t s);
 
 hipError_t launch_pack_pool(int D, bool pool, bool pack, const uint16_t *q, const uint16_t *k,
                             const uint16_t *v, const Grid &g, int heads, float *qp, float *kp,
@@ -149,13 +151,16 @@ inline int64_t walk_items(const Grid &g, int heads) {
 }
 // XCD-aware order of the attention work items: eight contiguous ranges of
 // equal work, each of at most order_range_cap items (twice the average count)
-// and taken by walk length class, longest class first; order holds order_slots(g, heads) = 8 x cap grid slots (-1:
-// no item), and the attention launch has one workgroup per slot (an empty
-// slot's workgroup exits at once; empty slots come last on their XCD).
+// and taken by walk length class, longest class first.  order holds
+// order_slots(g, heads) = 8 x cap grid slots (-1: no item), then the eight range
+// lengths (order_ints ints in all); the attention launch has one workgroup per
+// slot (an empty slot's workgroup exits at once; empty slots come last on their
+// XCD).
 inline int64_t order_range_cap(const Grid &g, int heads) {
     return 2 * (((int64_t)heads * plan_slots_per_head(g) + 7) / 8);
 }
 inline int64_t order_slots(const Grid &g, int heads) { return 8 * order_range_cap(g, heads); }
+inline int64_t order_ints(const Grid &g, int heads) { return order_slots(g, heads) + 8; }
 hipError_t launch_order(const int32_t *ulen, const Grid &g, int heads, int64_t maxcnt,
                         int32_t *order, hipStream_t s);
 
@@ -170,17 +175,20 @@ struct EntropyOut {
     float two_gamma_log2e;
 };
 
-// Attention items are claimed at run time: one int32 counter per XCD range,
-// kSchedStride int32 apart, in kSchedBytes of device memory per launch (cleared
-// by the launch itself; calls that overlap must not share it).
+// Along a work order the last quarter of each XCD range is claimed at run
+// time: one int32 counter per range, kSchedStride int32 apart, in kSchedBytes
+// of device memory that must be zero when the launch starts (launch_vmax zeroes
+// it; launches in a row need a zeroed set each) and is used by that launch alone.
 constexpr int kXcdRanges = 8;
 constexpr int kSchedStride = 64;
 constexpr size_t kSchedBytes = (size_t)kXcdRanges * kSchedStride * sizeof(int32_t);
+// Zeroes n int32 at p (a fill kernel: nothing that a captured graph could not replay).
+hipError_t launch_zero(int32_t *p, int64_t n, hipStream_t s);
 
 // ulist == nullptr: the dense mode (every block, both sides; order and pairs
 // null, vertical pairs in XCD-contiguous raster order).  vexp: the per-head V
 // exponents.  pairs: the plan's pair table.  sched: kSchedBytes of scratch for
-// the launch's work-claiming counters.
+// the work-claiming counters of a launch along a work order.
 hipError_t launch_attn(int D, const uint16_t *q, const uint16_t *kt, const uint16_t *vt,
                        const int32_t *vexp, const int2 *pairs, const int32_t *ulist,
                        const int32_t *ulen, const float2 *ubias, int64_t ustride,

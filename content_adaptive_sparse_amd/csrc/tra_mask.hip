@@ -700,7 +700,8 @@ __global__ __launch_bounds__(64 * kUnionWaves) void radius_walk_kernel(
 // leave a tail, and the items that run together on an XCD still come from
 // neighbouring frames (exact longest-first scattered them over the range and
 // measured 4-5% slower on the larger layers).  The k-th item of range x in
-// that order goes to grid slot 8 k + x, and slots past a range's end hold -1.
+// that order goes to grid slot 8 k + x, and slots past a range's end hold -1;
+// the eight range lengths follow the slots.
 // One workgroup per XCD, each finding all eight cuts the same way: per-thread
 // chunk sums, a block scan, the item whose work spans each share; then the
 // class counts of its range, a descending prefix and a stable scatter.
@@ -816,6 +817,7 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *__r
         __syncthreads();
     }
     for (int64_t k = (hi - lo) + tid; k < cap; k += kOrderThreads) order[kXcds * k + x] = -1;
+    if (tid == 0) order[kXcds * cap + x] = (int32_t)(hi - lo);  // the range's length
 }
 
 // Sampling with inclusion-probability weights (AB-Attention speeds up video

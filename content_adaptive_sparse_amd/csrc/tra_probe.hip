@@ -30,9 +30,13 @@ __device__ __forceinline__ int swap_bits23(int p) {
 // Largest |v| of a head, as the bit pattern of a non-negative bfloat16 (for
 // finite non-negative values the bit patterns order like the values).  Grid
 // (parts, heads): workgroup g scans the g-th of `parts` equal chunks of the
-// head's T H W d elements, eight at a time, and writes its maximum.
+// head's T H W d elements, eight at a time, and writes its maximum.  The first
+// workgroup also zeroes the attention launch's work-claiming counters.
 __global__ __launch_bounds__(256) void vmax_kernel(const uint16_t *__restrict__ v, int64_t n,
-                                                   int parts, uint32_t *__restrict__ vpart) {
+                                                   int parts, uint32_t *__restrict__ vpart,
+                                                   int32_t *__restrict__ sched) {
+    if (sched && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < kXcdRanges)
+        sched[threadIdx.x * kSchedStride] = 0;
     __shared__ uint32_t red[4];
     const int h = blockIdx.y, gpart = blockIdx.x;
     const int64_t n8 = n / 8;  // n = T H W d is a multiple of 8 (d in {64, 128})
@@ -413,11 +417,11 @@ int vmax_parts(const Grid &g, int D) {
 }
 
 hipError_t launch_vmax(int D, const uint16_t *v, const Grid &g, int heads, uint32_t *vpart,
-                       hipStream_t s) {
+                       int32_t *sched, hipStream_t s) {
     const int parts = vmax_parts(g, D);
     const int64_t n = (int64_t)g.T * g.H * g.W * D;
     hipLaunchKernelGGL(vmax_kernel, dim3((unsigned)parts, (unsigned)heads), dim3(256), 0, s, v, n,
-                       parts, vpart);
+                       parts, vpart, sched);
     return hipGetLastError();
 }
 

@@ -333,7 +333,9 @@ int tra_plan_radius(const int32_t *radius, int T, int H, int W, int heads, int b
  * cnt = NULL is the dense mode) and packs k and v, then launches the attention
  * kernel `reps` times back to back on `stream` between one pair of HIP events,
  * waits for the second event and writes the mean milliseconds per launch to
- * *ms.  out holds the attention output (as tra_attn_weighted).  reps >= 1.
+ * *ms.  out holds the attention output (as tra_attn_weighted).  reps in
+ * [1, 4096] (each launch gets its own 2 KB of work-claiming counters, zeroed
+ * before the timed launches); other values return TRA_ERR_INVALID_ARG.
  * Unlike the other entry points this one synchronises (on its own event).
  */
 int tra_time_attn(const void *q, const void *k, const void *v, int T, int H, int W, int heads,

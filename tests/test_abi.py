@@ -137,8 +137,9 @@ def test_warmup_and_timing_argument_errors(lib):
     assert lib.tra_token_warmup(*args, F(1.0), F(-1.0), FAKE, None, FAKE, None) == EINVAL
     assert lib.tra_token_warmup(FAKE, FAKE, FAKE, 4, 16, 16, 2, 96, 64, F(1.0), F(0.5), FAKE,
                                 None, FAKE, None) == EUNSUP
-    # tra_time_attn: reps >= 1, ms given, idx/cnt together, weights only with lists
+    # tra_time_attn: reps in [1, 4096], ms given, idx/cnt together, weights only with lists
     assert lib.tra_time_attn(*args, None, None, None, 0, 0, FAKE, ctypes.byref(ms), None) == EINVAL
+    assert lib.tra_time_attn(*args, None, None, None, 0, 4097, FAKE, ctypes.byref(ms), None) == EINVAL
     assert lib.tra_time_attn(*args, None, None, None, 0, 3, FAKE, None, None) == EINVAL
     assert lib.tra_time_attn(*args, FAKE, None, None, 5, 3, FAKE, ctypes.byref(ms), None) == EINVAL
     assert lib.tra_time_attn(*args, None, None, FAKE, 0, 3, FAKE, ctypes.byref(ms), None) == EINVAL
@@ -164,7 +165,7 @@ def test_plan_bytes_closed_form(lib):
         # item slots per head: vertical pairs or temporal pairs, whichever are more
         items = heads * max(T * ((nby + 1) // 2) * nbx, (T + 1) // 2 * nby * nbx)
         slots = -(-items // 8) * 8
-        order = 8 * 2 * -(-items // 8)  # eight ranges of at most twice the mean count
+        order = 8 * 2 * -(-items // 8) + 8  # eight ranges of at most twice the mean count, their lengths
         stride = -(-(2 * maxcnt) // 64) * 64
         # work order, walk lengths, walks, pair table (two int32 per item slot)
         want = up(4 * order) + up(4 * slots) + up(4 * slots * stride) + up(8 * slots)
@@ -188,11 +189,12 @@ def test_plan_argument_errors(lib):
     assert lib.tra_plan_radius(FAKE, 4, 16, 16, 2, 64, -1, FAKE, None) == EINVAL
     assert lib.tra_plan_radius(FAKE, 4, 16, 16, 2, 32, 3, FAKE, None) == EUNSUP
     assert lib.tra_plan_radius(FAKE, 4, 16, 16, 0, 64, 3, FAKE, None) == EINVAL
-    # tra_time_attn_plan: reps >= 1, ms given, the plan's maxcnt checked when a plan is given
+    # tra_time_attn_plan: reps in [1, 4096], ms given, the plan's maxcnt checked when a plan is given
     F = ctypes.c_float
     ms = F()
     args = (FAKE, FAKE, FAKE, 4, 16, 16, 2, 128, 64)
     assert lib.tra_time_attn_plan(*args, FAKE, 5, 0, FAKE, ctypes.byref(ms), None) == EINVAL
+    assert lib.tra_time_attn_plan(*args, FAKE, 5, 4097, FAKE, ctypes.byref(ms), None) == EINVAL
     assert lib.tra_time_attn_plan(*args, FAKE, 5, 3, FAKE, None, None) == EINVAL
     assert lib.tra_time_attn_plan(*args, FAKE, 0, 3, FAKE, ctypes.byref(ms), None) == EINVAL
     assert lib.tra_time_attn_plan(*args, FAKE, 5, 3, None, ctypes.byref(ms), None) == EINVAL

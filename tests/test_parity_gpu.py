@@ -443,7 +443,8 @@ def test_work_order_ranges(case):
     items = heads * plan_slots(T, H, W)
     cap = 2 * -(-items // 8)
     order = raw[: 8 * cap]
-    o_ulen = -(-(4 * 8 * cap) // 256) * 256 // 4  # the walk lengths follow, 256-byte aligned
+    lengths = raw[8 * cap: 8 * cap + 8]  # the eight range lengths follow the slots
+    o_ulen = -(-(4 * (8 * cap + 8)) // 256) * 256 // 4  # then the walk lengths, 256-byte aligned
     ulen = raw[o_ulen: o_ulen + items]
     assert np.array_equal(np.sort(order[order >= 0]), np.arange(items)), "not a permutation"
     cost = np.clip(ulen, 0, min(2 * maxcnt, 8191)).astype(np.int64) + 4
@@ -464,6 +465,7 @@ def test_work_order_ranges(case):
         assert n <= cap, f"range {x} above the cap"
         assert np.array_equal(np.sort(col[:n]), np.arange(lo, hi)), f"range {x}"
         assert (col[n:] == -1).all(), f"range {x}: slots past the end"
+        assert lengths[x] == n, f"range {x}: recorded length"
         # by length class (two per octave), longest class first, item order inside
         cls = np.array([order_class(v) for v in np.clip(ulen[col[:n]], 0, min(2 * maxcnt, 8191))])
         step = np.diff(cls)
@@ -630,7 +632,7 @@ def plan_pair_table(plan, T, H, W, heads, maxcnt):
     cap = 2 * -(-items // 8)
     stride = -(-(2 * maxcnt) // 64) * 64
     up = lambda x: -(-x // 256) * 256
-    o = up(4 * 8 * cap) + up(4 * rows) + up(4 * rows * stride)
+    o = up(4 * (8 * cap + 8)) + up(4 * rows) + up(4 * rows * stride)
     raw = plan.cpu().numpy()[o: o + 8 * items].view(np.int32)
     return raw.reshape(heads, -1, 2).astype(np.int64)
 

@@ -236,21 +236,34 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     // 16 l.  One global address and one LDS base (M0, wave-uniform) serve the
     // wave's pieces: a piece's 1 KB step is the instruction's immediate
     // offset, which applies to both the global and the LDS address.
+    // The copies are written as inline assembly so that the compiler does not
+    // track them: it cannot tell the ring slots apart and would otherwise wait
+    // for every copy in flight before the next LDS operand read, although the
+    // slot being filled is never read before the next barrier.  Every wave
+    // waits for its own copies (vmcnt 0) before each barrier, and nothing
+    // reads a slot between the copy into it and that barrier.  The copies
+    // write LDS only (no register results), so no register is left in flight.
     static_assert(PPW == 2 || PPW == 4, "pieces per wave");
     const size_t head_tiles = (size_t)h * g.nb;
     const int wave_lds_bytes = __builtin_amdgcn_readfirstlane(wave * PPW * 1024);
     const uint32_t lane_bytes = (uint32_t)(wave * PPW * 1024 + lane * 16);
-#define TRA_ISSUE(src, dst, blk)                                                              \
-    do {                                                                                      \
-        const global_void_t *g_ = (const global_void_t *)(                                    \
-            reinterpret_cast<const char *>(src + (head_tiles + (blk)) * 64 * D) + lane_bytes); \
-        lds_void_t *l_ = (lds_void_t *)(reinterpret_cast<char *>(dst) + wave_lds_bytes);      \
-        __builtin_amdgcn_global_load_lds(g_, l_, 16, 0, 0);                                   \
-        __builtin_amdgcn_global_load_lds(g_, l_, 16, 1024, 0);                                \
-        if constexpr (PPW == 4) {                                                             \
-            __builtin_amdgcn_global_load_lds(g_, l_, 16, 2048, 0);                            \
-            __builtin_amdgcn_global_load_lds(g_, l_, 16, 3072, 0);                            \
-        }                                                                                     \
+#define TRA_ISSUE(src, dst, blk)                                                                \
+    do {                                                                                        \
+        const char *g_ =                                                                        \
+            reinterpret_cast<const char *>(src + (head_tiles + (blk)) * 64 * D) + lane_bytes;   \
+        const uint32_t m_ = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)( \
+            reinterpret_cast<char *>(dst) + wave_lds_bytes));                                   \
+        if constexpr (PPW == 4)                                                                 \
+            asm volatile("global_load_lds_dwordx4 %1, off\n\t"                                   \
+                         "global_load_lds_dwordx4 %1, off offset:1024\n\t"                       \
+                         "global_load_lds_dwordx4 %1, off offset:2048\n\t"                       \
+                         "global_load_lds_dwordx4 %1, off offset:3072" ::"{m0}"(m_),              \
+                         "v"(g_)                                                                \
+                         : "memory");                                                           \
+        else                                                                                    \
+            asm volatile("global_load_lds_dwordx4 %1, off\n\t"                                   \
+                         "global_load_lds_dwordx4 %1, off offset:1024" ::"{m0}"(m_), "v"(g_)      \
+                         : "memory");                                                           \
     } while (0)
 
     // Every matrix-core operand of a packed tile is a 1 KB piece in which this
@@ -278,14 +291,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     int e1 = entry(1);  // entries u and u + 1
     float w1 = weight(1);
     TRA_ISSUE(kt, kring[0], e0 >> 2);
-    if (e1 >= 0) {
-        TRA_ISSUE(kt, kring[1], e1 >> 2);
-        TRA_ISSUE(vt, vring[0], e0 >> 2);
-        __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * PPW));  // K of entry 0 landed
-    } else {
-        TRA_ISSUE(vt, vring[0], e0 >> 2);
-        __builtin_amdgcn_s_waitcnt(wait_vmcnt(PPW));
-    }
+    if (e1 >= 0) TRA_ISSUE(kt, kring[1], e1 >> 2);
+    TRA_ISSUE(vt, vring[0], e0 >> 2);
+    // every load so far (Q rows, walk windows, the first copies) has landed:
+    // the compiler, which does not see the copies, then keeps no wait for the
+    // Q rows inside the loop
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
 
     // Row sums of fp16 probabilities (two independent chains).
@@ -401,6 +412,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
                     sb[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], sb[hf], 0, 0, 0);
                 }
             }
+            // the K operand reads run six ahead of the products that use them
+            __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // 6 LDS reads
+#pragma unroll
+            for (int i = 0; i < 2 * KS - 6; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 product
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);  // the last 6 products
             const uint32_t kb = (uint32_t)(e0 >> 2);
             const uint32_t row = fdiv(kb, div_nbx);
             const int kbx = (int)(kb - row * div_nbx.d);
@@ -472,6 +491,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     int u = 0;
     auto step = [&](auto slot_tag) -> bool {
         const bool mine = live && e0 >= 0 && ((e0 >> side) & 1);
+        // a wave computing a step issues ahead of one at the barrier or
+        // issuing copies (two waves of different workgroups share a SIMD)
+        __builtin_amdgcn_s_setprio(1);
         if (mine) {
             if (prev_mine) work(slot_tag, T1{}, T1{});
             else work(slot_tag, T1{}, T0{});
@@ -479,6 +501,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
             work(slot_tag, T0{}, T1{});
         }
         prev_mine = mine;
+        __builtin_amdgcn_s_setprio(0);
         if (e0 < 0) return false;
         // K of entry u + 1 and V^T of entry u were the copies in flight
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);

@@ -115,7 +115,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the chip raises its clock over the first ~25 ms of work after an idle gap
+    # (attention launches 3.3 ms at first, 2.55-2.6 ms once warm): 20 layers
+    # (about 55 ms) reach the steady state
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="wan13b_81f",
                     help="workload slug (tra_inputs.WORKLOADS): tiny, wan13b_81f, wan13b_241f, "
                          "wan14b_81f, hunyuan_129f")
@@ -237,12 +240,13 @@ def main():
         tra.tra_plan_radius(rd, T, H, W, heads, 64, rmax, pl)
         return pl, mc
 
-    # one untimed launch before each timed run (the first launch after host
-    # work runs at a lower clock and with cold caches)
+    # ten untimed launches before each timed run: after the host work between
+    # the benchmark's phases the chip's clock ramps up again over the first
+    # 25-30 ms of work
     plan, _ = radius_plan(radius, c.r_max)
-    tra.tra_time_attn_plan(qd, kd, vd, T, H, W, heads, d, 64, plan, maxcnt, 1, out)
+    tra.tra_time_attn_plan(qd, kd, vd, T, H, W, heads, d, 64, plan, maxcnt, 10, out)
     t_attn = tra.tra_time_attn_plan(qd, kd, vd, T, H, W, heads, d, 64, plan, maxcnt, reps, out)
-    tra.tra_time_attn_plan(qd, kd, vd, T, H, W, heads, d, 64, None, 0, 1, out)
+    tra.tra_time_attn_plan(qd, kd, vd, T, H, W, heads, d, 64, None, 0, 4, out)
     t_dense_attn = tra.tra_time_attn_plan(qd, kd, vd, T, H, W, heads, d, 64, None, 0, reps, out)
     del plan
     idx = torch.empty(heads, nb, maxcnt, dtype=torch.int32, device="cuda")
@@ -485,7 +489,7 @@ def main():
             "radius_histogram": rhist,
             "attn_ms": round(t_attn, 4),
             "attn_timing": (f"mean of {reps} back-to-back attention launches between one HIP event "
-                            "pair on the launch stream, after one untimed launch, along the walk plan the "
+                            "pair on the launch stream, after ten untimed launches, along the walk plan the "
                             "layer builds from the radii (tra_plan_radius, tra_time_attn_plan)"),
             "mfma_executed_tflops_attn": round(mfma_flops / (t_attn * 1e-3) / 1e12, 1),
             "real_token_tflops_attn": round(real_flops / (t_attn * 1e-3) / 1e12, 1),

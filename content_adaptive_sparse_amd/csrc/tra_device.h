@@ -53,7 +53,6 @@ constexpr int wait_vmcnt(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 
 constexpr int kWaitVmcnt0 = wait_vmcnt(0);
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void global_void_t;
 // Arrays never written while a kernel runs (work orders, walk lengths) read
 // through the constant address space give scalar loads.
 typedef __attribute__((address_space(4))) const int32_t const_i32_t;

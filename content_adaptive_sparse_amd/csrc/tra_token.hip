@@ -78,30 +78,35 @@ __global__ __launch_bounds__(kEntThreads, 2) void token_entropy_kernel(
     // Copy of key tile kb into a slot: each wave moves PPW 1 KB pieces with one
     // global address and one wave-uniform LDS base, the pieces' 1 KB step in the
     // instruction's immediate offset (it moves the global and the LDS address).
+    // Inline assembly, so that the compiler does not wait for the copy in flight
+    // (into the other slot) before this tile's operand reads; each wave waits
+    // for its own copies before the barrier that precedes the tile's use.
     static_assert(PPW == 2 || PPW == 4, "pieces per wave");
     const size_t head_tiles = (size_t)h * g.nb;
     const int wave_lds_bytes = __builtin_amdgcn_readfirstlane(wave * PPW * 1024);
     const uint32_t lane_bytes = (uint32_t)(wave * PPW * 1024 + lane * 16);
     const int lane8 = lane * 8;
     auto issue = [&](int kb, int slot) {
-        const global_void_t *g_ = (const global_void_t *)(
-            reinterpret_cast<const char *>(kt + (head_tiles + kb) * 64 * D) + lane_bytes);
-        lds_void_t *l_ = (lds_void_t *)(reinterpret_cast<char *>(kring[slot]) + wave_lds_bytes);
-        __builtin_amdgcn_global_load_lds(g_, l_, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(g_, l_, 16, 1024, 0);
-        if constexpr (PPW == 4) {
-            __builtin_amdgcn_global_load_lds(g_, l_, 16, 2048, 0);
-            __builtin_amdgcn_global_load_lds(g_, l_, 16, 3072, 0);
-        }
+        const char *g_ = reinterpret_cast<const char *>(kt + (head_tiles + kb) * 64 * D) + lane_bytes;
+        const uint32_t m_ = __builtin_amdgcn_readfirstlane(
+            (uint32_t)(uintptr_t)(lds_void_t *)(reinterpret_cast<char *>(kring[slot]) + wave_lds_bytes));
+        if constexpr (PPW == 4)
+            asm volatile("global_load_lds_dwordx4 %1, off\n\t"
+                         "global_load_lds_dwordx4 %1, off offset:1024\n\t"
+                         "global_load_lds_dwordx4 %1, off offset:2048\n\t"
+                         "global_load_lds_dwordx4 %1, off offset:3072" ::"{m0}"(m_), "v"(g_)
+                         : "memory");
+        else
+            asm volatile("global_load_lds_dwordx4 %1, off\n\t"
+                         "global_load_lds_dwordx4 %1, off offset:1024" ::"{m0}"(m_), "v"(g_)
+                         : "memory");
     };
 
     issue(0, 0);
-    if (g.nb > 1) {
-        issue(1, 1);
-        __builtin_amdgcn_s_waitcnt(wait_vmcnt(PPW));
-    } else {
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    }
+    if (g.nb > 1) issue(1, 1);
+    // every load so far (Q rows, the first copies) has landed; the compiler, which
+    // does not see the copies, then keeps no wait for the Q rows inside the loop
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
 
     float m_ref = -1e30f, Z = 0.f, A = 0.f;
